@@ -1,0 +1,268 @@
+"""Seeded synthetic inputs for paged decode attention.
+
+This module only makes inputs: query vectors, K/V page pools, block tables
+and context lengths.  It holds none of the attention arithmetic, and it is
+the one module that both the HIP path's callers and the float64 oracle's
+callers use, so that both see the same bits.
+
+Values.  Every bf16 value is drawn by a counter-based generator, so any
+element can be regenerated on its own on any device:
+
+    a = mix32((i mod 2^32) xor k1),  b = mix32(a xor (i div 2^32) xor k2)
+    value_i = NORMAL_TABLE[b >> 16]
+
+``mix32`` is the "lowbias32" integer finaliser published by Chris Wellons
+(hash-prospector): x ^= x>>16; x *= 0x7feb352d; x ^= x>>15; x *= 0x846ca68b;
+x ^= x>>16, all modulo 2^32.  ``NORMAL_TABLE[j]`` is the bf16 rounding
+(round-to-nearest-even) of the standard normal quantile at (j + 0.5) / 65536,
+so each element is an N(0, 1) draw quantised to 65536 levels (tails cut at
+about 4.3 sigma).  (k1, k2) come from the seed and the tensor's name.  The
+arithmetic is integer-only, so CPU and GPU produce identical bits.
+
+Parity runs poison what must never be read: pool pages no block table points
+to, and the slots of a sequence's last page at or beyond its length, hold the
+bf16 quiet-NaN pattern 0x7FC0.  Block-table entries past a sequence's last
+page are -1.
+
+Workload shapes are those of the decode-attention traces on the PersistentKV
+page ("PersistentKV: Page-Aware Decode Scheduling ...", Evaluation Protocol:
+single long context, mixed lengths, many short rows) and of the
+many-session resident loop on the Wave Persistent Kernel note.  The pages do
+not give their trace generators; these recipes stand in for them.
+Measurement seed 20260623, calibration seed 20260622 (the PersistentKV page's
+held-out and calibration seeds, Results section).
+"""
+
+from __future__ import annotations
+
+import math
+import zlib
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+MEASURE_SEED = 20260623
+CALIBRATION_SEED = 20260622
+BF16_NAN = 0x7FC0
+_M32 = 0xFFFFFFFF
+
+
+def _mix32_int(x: int) -> int:
+    x &= _M32
+    x ^= x >> 16
+    x = (x * 0x7FEB352D) & _M32
+    x ^= x >> 15
+    x = (x * 0x846CA68B) & _M32
+    x ^= x >> 16
+    return x
+
+
+def _mix32(x: torch.Tensor) -> torch.Tensor:
+    """lowbias32 on int64 tensors holding values in [0, 2^32)."""
+    x = x ^ (x >> 16)
+    x = (x * 0x7FEB352D) & _M32
+    x = x ^ (x >> 15)
+    x = (x * 0x846CA68B) & _M32          # may wrap in int64; low 32 bits exact
+    x = x ^ (x >> 16)
+    return x
+
+
+_TABLE_CACHE: dict = {}
+
+
+def normal_table(device) -> torch.Tensor:
+    """int64 tensor [65536] of bf16 bit patterns of N(0,1) quantiles."""
+    key = str(device)
+    if key not in _TABLE_CACHE:
+        from scipy.special import ndtri
+        p = (np.arange(65536, dtype=np.float64) + 0.5) / 65536.0
+        f32 = ndtri(p).astype(np.float32)
+        u = f32.view(np.uint32).astype(np.uint64)
+        rne = (u + 0x7FFF + ((u >> 16) & 1)) >> 16          # float32 -> bf16 RNE
+        _TABLE_CACHE[key] = torch.from_numpy(rne.astype(np.int64)).to(device)
+    return _TABLE_CACHE[key]
+
+
+def stream_keys(seed: int, name: str):
+    """Two 32-bit keys for tensor ``name`` under ``seed``."""
+    n = zlib.crc32(name.encode())
+    k1 = _mix32_int(_mix32_int(seed & _M32) ^ n)
+    k2 = _mix32_int(k1 ^ 0x9E3779B9)
+    return k1, k2
+
+
+def normal_bf16_bits(seed: int, name: str, index: torch.Tensor) -> torch.Tensor:
+    """bf16 bit patterns (int64 tensor, values 0..65535) for element ``index``."""
+    k1, k2 = stream_keys(seed, name)
+    a = _mix32((index & _M32) ^ k1)
+    b = _mix32(a ^ (index >> 32) ^ k2)
+    return normal_table(index.device)[b >> 16]
+
+
+def _to_bf16(bits: torch.Tensor) -> torch.Tensor:
+    """int64 tensor of 16-bit patterns -> torch.bfloat16 with those bits."""
+    return (bits - ((bits >> 15) & 1) * 65536).to(torch.int16).view(torch.bfloat16)
+
+
+def fill_normal_bf16(out: torch.Tensor, seed: int, name: str, offset: int = 0,
+                     chunk: int = 1 << 24) -> torch.Tensor:
+    """Fill a contiguous bf16 tensor with the stream ``name`` starting at
+    element ``offset`` (chunked to bound the int64 temporaries)."""
+    flat = out.view(-1)
+    n = flat.numel()
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        idx = torch.arange(offset + s, offset + e, dtype=torch.int64, device=out.device)
+        flat[s:e] = _to_bf16(normal_bf16_bits(seed, name, idx))
+    return out
+
+
+def bits_u16(t: torch.Tensor) -> np.ndarray:
+    """Host numpy uint16 view of a bf16 tensor's bits (copies to CPU)."""
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+@dataclass
+class Workload:
+    """One decode-attention call's shapes plus the recipe of its inputs."""
+    name: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    ctx_lens: np.ndarray              # int32 [B]
+    block_table: np.ndarray           # int32 [B][max_pages_per_seq], -1 = unused
+    num_pages: int
+    seed: int
+    scale: float = 0.0
+    extra: dict = field(default_factory=dict)
+
+    def __post_init__(self):
+        if self.scale == 0.0:
+            self.scale = 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def batch(self) -> int:
+        return int(self.ctx_lens.shape[0])
+
+    @property
+    def max_pages_per_seq(self) -> int:
+        return int(self.block_table.shape[1])
+
+    @property
+    def kv_bytes(self) -> int:
+        """Bytes of K and V of valid tokens: the algorithmic read volume."""
+        return int(self.ctx_lens.astype(np.int64).sum()) * self.num_kv_heads \
+            * self.head_dim * 2 * 2
+
+    def q(self, device="cpu") -> torch.Tensor:
+        t = torch.empty(self.batch, self.num_q_heads, self.head_dim,
+                        dtype=torch.bfloat16, device=device)
+        return fill_normal_bf16(t, self.seed, self.name + "/q")
+
+    def pool(self, which: str, device="cpu", poison: bool = True) -> torch.Tensor:
+        """K ('k') or V ('v') pool [num_pages][Hkv][P][D] bf16."""
+        t = torch.empty(self.num_pages, self.num_kv_heads, self.page_size,
+                        self.head_dim, dtype=torch.bfloat16, device=device)
+        fill_normal_bf16(t, self.seed, self.name + "/" + which)
+        if poison:
+            self.poison(t)
+        return t
+
+    def pool_pages(self, which: str, pages: np.ndarray) -> torch.Tensor:
+        """Regenerate only the given pool pages on the CPU (unpoisoned values),
+        shaped [len(pages)][Hkv][P][D]: the same bits ``pool`` holds there."""
+        per_page = self.num_kv_heads * self.page_size * self.head_dim
+        pages = torch.as_tensor(np.asarray(pages, dtype=np.int64))
+        idx = pages[:, None] * per_page + torch.arange(per_page, dtype=torch.int64)[None, :]
+        bits = normal_bf16_bits(self.seed, self.name + "/" + which, idx.reshape(-1))
+        return _to_bf16(bits).view(len(pages), self.num_kv_heads, self.page_size,
+                                   self.head_dim)
+
+    def poison(self, pool: torch.Tensor) -> None:
+        """Write NaN into unreferenced pages and past-the-end slots."""
+        used = np.zeros(self.num_pages, dtype=bool)
+        P = self.page_size
+        nan = torch.tensor(BF16_NAN, dtype=torch.int16).view(torch.bfloat16)
+        for b in range(self.batch):
+            L = int(self.ctx_lens[b])
+            npg = -(-L // P)
+            used[self.block_table[b, :npg]] = True
+            if L % P:
+                last = int(self.block_table[b, npg - 1])
+                pool[last, :, L % P:, :] = nan.to(pool.device)
+        unused = np.nonzero(~used)[0]
+        if unused.size:
+            pool[torch.as_tensor(unused, device=pool.device)] = nan.to(pool.device)
+
+    def block_table_t(self, device="cpu") -> torch.Tensor:
+        return torch.as_tensor(self.block_table, dtype=torch.int32).to(device)
+
+    def ctx_lens_t(self, device="cpu") -> torch.Tensor:
+        return torch.as_tensor(self.ctx_lens, dtype=torch.int32).to(device)
+
+
+def _tables(rng: np.random.Generator, lens, page_size: int, num_pages: int,
+            max_pages: int | None = None):
+    """Block tables that scatter every sequence over a random permutation of
+    the pool (each physical page is used at most once)."""
+    need = [-(-int(L) // page_size) for L in lens]
+    if max_pages is None:
+        max_pages = max(need) if need else 0
+    perm = rng.permutation(num_pages).astype(np.int32)
+    bt = np.full((len(lens), max(max_pages, 1)), -1, dtype=np.int32)
+    pos = 0
+    for b, n in enumerate(need):
+        bt[b, :n] = perm[pos:pos + n]
+        pos += n
+    return bt
+
+
+def tiny(seed: int = MEASURE_SEED) -> Workload:
+    """Batch 1, 4 query heads / 1 KV head, head_dim 64, 256 tokens in 16 pages
+    scattered over a 64-page pool."""
+    rng = np.random.default_rng([seed, 1])
+    lens = np.array([256], dtype=np.int32)
+    return Workload("tiny", 4, 1, 64, 16, lens, _tables(rng, lens, 16, 64), 64, seed)
+
+
+def long_context(seed: int = MEASURE_SEED, ctx: int = 131072) -> Workload:
+    """Batch 1, 32/8 heads, head_dim 128, 131072 tokens over a permuted pool."""
+    rng = np.random.default_rng([seed, 2])
+    lens = np.array([ctx], dtype=np.int32)
+    npg = -(-ctx // 16)
+    return Workload("long", 32, 8, 128, 16, lens, _tables(rng, lens, 16, npg), npg, seed)
+
+
+def mixed(seed: int = MEASURE_SEED, batch: int = 8, lo: int = 1024, hi: int = 65536) -> Workload:
+    """8 sequences, lengths log-uniform in [1024, 65536] (rounded), 32/8 heads."""
+    rng = np.random.default_rng([seed, 3])
+    lens = np.rint(np.exp(rng.uniform(math.log(lo), math.log(hi), size=batch)))
+    lens = np.clip(lens, lo, hi).astype(np.int32)
+    npg = int(sum(-(-int(L) // 16) for L in lens))
+    return Workload("mixed", 32, 8, 128, 16, lens, _tables(rng, lens, 16, npg), npg, seed)
+
+
+def many_short(seed: int = MEASURE_SEED, batch: int = 64, ctx: int = 4096) -> Workload:
+    """64 sequences of 4096 tokens, 32/8 heads."""
+    rng = np.random.default_rng([seed, 4])
+    lens = np.full(batch, ctx, dtype=np.int32)
+    npg = batch * (-(-ctx // 16))
+    return Workload("short", 32, 8, 128, 16, lens, _tables(rng, lens, 16, npg), npg, seed)
+
+
+def custom(name: str, lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
+           seed: int = MEASURE_SEED, spare_pages: int = 0, page_size: int = 16,
+           max_pages: int | None = None) -> Workload:
+    """Any shape: lengths given, pool = the pages needed plus ``spare_pages``
+    (spare pages are poisoned)."""
+    rng = np.random.default_rng([seed, zlib.crc32(name.encode())])
+    lens = np.asarray(lens, dtype=np.int32)
+    npg = int(sum(-(-int(L) // page_size) for L in lens)) + spare_pages
+    npg = max(npg, 1)
+    return Workload(name, num_q_heads, num_kv_heads, head_dim, page_size, lens,
+                    _tables(rng, lens, page_size, npg, max_pages), npg, seed)
+
+
+CONFIGS = {"tiny": tiny, "long": long_context, "mixed": mixed, "short": many_short}
