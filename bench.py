@@ -1,0 +1,236 @@
+"""Benchmark: paged decode attention KV-read throughput on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload long|mixed|short|tiny]
+
+One step = one pkv_decode call (persistent decode kernel + LSE merge when
+rows are split) over the whole batch, inputs resident in HBM.  The headline
+workload is the single long context (batch 1, 32/8 heads, head_dim 128,
+131072 tokens, bf16, 32 splits of 4096 tokens).  Before timing, a parity gate
+checks sampled (sequence, KV head) units against the float64 oracle.  The K/V
+pools are kept in two copies that steps alternate between, so each step
+streams from HBM rather than from the 256 MB last-level cache.
+
+Prints one JSON line.  `value` is KV-read GB/s over the whole step (decode
++ merge, HIP events on the launch stream); `roofline` prices the decode
+kernel alone (its own HIP events) against the 8 TB/s HBM peak;
+`cpu_baseline` is the oracle timed on a bounded sample on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode-attn KV-read GB/s (% of HBM peak); p99 step latency, 56 sessions"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="long", choices=["long", "mixed", "short", "tiny"])
+    ap.add_argument("--others", default="mixed,short",
+                    help="extra workloads measured in the same run ('' for none)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="bounded oracle sample for cpu_baseline (0 disables)")
+    ap.add_argument("--order", default="canonical", choices=["canonical", "lpt"])
+    ap.add_argument("--wg-per-cu", type=int, default=0)
+    ap.add_argument("--copies", type=int, default=2)
+    ap.add_argument("--no-gate", action="store_true")
+    return ap.parse_args()
+
+
+def measure(torch, pkv, workloads, name, steps, warmup, order, wg_per_cu, copies, gate, say):
+    wl = workloads.CONFIGS[name]()
+    dev = "cuda"
+    q = wl.q(dev)
+    pools = []
+    for c in range(copies):
+        pools.append((wl.pool("k", dev, poison=(c == 0)), wl.pool("v", dev, poison=(c == 0))))
+    bt = wl.block_table_t(dev)
+    lens = wl.ctx_lens_t(dev)
+    out = torch.empty(wl.batch, wl.num_q_heads, wl.head_dim, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(wl.batch, wl.num_q_heads, dtype=torch.float32, device=dev)
+    cfg = pkv.make_config(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages, wl.batch,
+                          wl.max_pages_per_seq, scale=wl.scale,
+                          order=pkv.PKV_ORDER_LPT if order == "lpt" else pkv.PKV_ORDER_CANONICAL,
+                          wg_per_cu=wg_per_cu)
+    stream = torch.cuda.current_stream()
+    dec = pkv.PagedDecoder(cfg, stream=stream)
+    info = dec.build_queue(wl.ctx_lens)
+    tens = [pkv.make_tensors(q, k, v, bt, lens, out, lse) for k, v in pools]
+
+    if gate:   # correctness gate before any timing (oracle on sampled units)
+        from oracle import paged_attention as pa
+        pkv.pkv_decode(dec.handle, tens[0], stream)
+        torch.cuda.synchronize()
+        dec.query()
+        o = out.float().cpu().numpy()
+        l = lse.cpu().numpy()
+        qb = workloads.bits_u16(q)
+        G = wl.num_q_heads // wl.num_kv_heads
+        for b, hk in [(0, 0), (wl.batch - 1, wl.num_kv_heads - 1)]:
+            L = int(wl.ctx_lens[b])
+            npg = -(-L // 16)
+            pg = wl.block_table[b, :npg]
+            ks = workloads.bits_u16(wl.pool_slabs("k", pg, hk))[:, None]
+            vs = workloads.bits_u16(wl.pool_slabs("v", pg, hk))[:, None]
+            ro, rl = pa.range_state(qb[b:b + 1, hk * G:(hk + 1) * G], ks, vs,
+                                    np.arange(npg)[None], 0, 0, 0, L, wl.scale, 16)
+            err = np.abs(o[b, hk * G:(hk + 1) * G] - ro)
+            lerr = np.abs(l[b, hk * G:(hk + 1) * G] - rl)
+            if not (err.max() <= 2e-2 and err.mean() <= 2e-3 and lerr.max() <= 2e-2):
+                raise SystemExit(f"parity gate failed on {name} unit {(b, hk)}: "
+                                 f"max {err.max():.3e} mean {err.mean():.3e} lse {lerr.max():.3e}")
+        say(f"parity gate passed ({name})")
+
+    for i in range(warmup):
+        pkv.pkv_decode(dec.handle, tens[i % copies], stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:                       # torch creates the HIP events on first record
+        a.record(stream)
+        b.record(stream)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        pkv.pkv_set_decode_events(dec.handle, ev[i][0], ev[i][1])
+        pkv.pkv_decode(dec.handle, tens[i % copies], stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pkv.pkv_set_decode_events(dec.handle, None, None)
+    st = dec.query()
+    total_ms = start.elapsed_time(stop)
+    kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms_step = total_ms / steps
+    res = {
+        "workload": name, "kv_bytes": info.kv_bytes, "items": info.n_items,
+        "split": bool(info.split), "launches_per_step": info.launches_per_step,
+        "partial_bytes": info.partial_bytes, "ms_per_step": ms_step,
+        "gbs": info.kv_bytes / (ms_step * 1e-3) / 1e9,
+        "decode_ms_mean": float(kern_ms.mean()), "decode_ms_median": float(np.median(kern_ms)),
+        "decode_ms_p99": float(np.percentile(kern_ms, 99)),
+        "decode_gbs": info.kv_bytes / (kern_ms.mean() * 1e-3) / 1e9,
+        "host_wall_ms_per_step": wall * 1e3 / steps, "grid": st["grid"], "num_cus": st["num_cus"],
+        "batch": wl.batch, "ctx_lens_sum": int(wl.ctx_lens.sum()),
+    }
+    dec.close()
+    del pools, tens
+    torch.cuda.empty_cache()
+    return res, wl
+
+
+def cpu_baseline(workloads, wl, seconds, say):
+    """The oracle as it stands, on whole (sequence, KV head) units of the same
+    workload, for about `seconds` of CPU time."""
+    from oracle import paged_attention as pa
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    qb = workloads.bits_u16(wl.q("cpu"))
+    G = wl.num_q_heads // wl.num_kv_heads
+    units = [(b, h) for b in range(wl.batch) for h in range(wl.num_kv_heads)]
+    done_bytes, spent, n = 0, 0.0, 0
+    for b, hk in units:
+        L = int(wl.ctx_lens[b])
+        npg = -(-L // 16)
+        pg = wl.block_table[b, :npg]
+        ks = workloads.bits_u16(wl.pool_slabs("k", pg, hk))[:, None]
+        vs = workloads.bits_u16(wl.pool_slabs("v", pg, hk))[:, None]
+        t0 = time.perf_counter()
+        pa.range_state(qb[b:b + 1, hk * G:(hk + 1) * G], ks, vs, np.arange(npg)[None], 0, 0, 0, L,
+                       wl.scale, 16)
+        spent += time.perf_counter() - t0
+        done_bytes += L * wl.head_dim * 2 * 2
+        n += 1
+        if spent >= seconds:
+            break
+    say(f"cpu baseline: {n} units, {spent:.1f} s")
+    return {"value": done_bytes / spent / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n} of {len(units)} (sequence, KV head) units of the '{wl.name}' workload "
+                      f"({done_bytes / 1e6:.1f} MB of K+V), float64 NumPy oracle, inputs regenerated "
+                      f"on the host and excluded from the time"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
+              "(this path runs on a single MI355X; no multi-GPU run exists)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from paged_kv_attention_persistent_amd import pkv, workloads
+
+    def say(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    pkv.lib()
+    main_res, wl = measure(torch, pkv, workloads, args.workload, args.steps, args.warmup,
+                           args.order, args.wg_per_cu, args.copies, not args.no_gate, say)
+    say(f"{args.workload}: {main_res['gbs']:.1f} GB/s per step, decode kernel "
+        f"{main_res['decode_gbs']:.1f} GB/s ({main_res['decode_ms_mean'] * 1e3:.1f} us)")
+    others = {}
+    for name in [x for x in args.others.split(",") if x and x != args.workload]:
+        r, _ = measure(torch, pkv, workloads, name, max(args.steps // 2, 10), args.warmup,
+                       args.order, args.wg_per_cu, args.copies, not args.no_gate, say)
+        others[name] = {k: r[k] for k in ("gbs", "decode_gbs", "ms_per_step", "decode_ms_mean",
+                                          "items", "split", "kv_bytes", "launches_per_step")}
+        others[name]["pct_of_hbm_peak"] = 100.0 * r["gbs"] / HBM_PEAK_GBS
+        say(f"{name}: {r['gbs']:.1f} GB/s per step, decode {r['decode_gbs']:.1f} GB/s")
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(workloads, wl, args.cpu_seconds, say)
+    achieved = main_res["decode_gbs"]
+    line = {
+        "metric": METRIC,
+        "value": round(main_res["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded counter-based N(0,1) bf16; permuted page pool)",
+        "pct_of_hbm_peak": round(100.0 * main_res["gbs"] / HBM_PEAK_GBS, 2),
+        "config": {"workload": "single long context", "batch": 1, "context_tokens": 131072,
+                   "q_heads": 32, "kv_heads": 8, "head_dim": 128, "page_size": 16,
+                   "kv_chunk_tokens": 4096, "items": main_res["items"],
+                   "launches_per_step": main_res["launches_per_step"],
+                   "kv_bytes_per_step": main_res["kv_bytes"], "grid": main_res["grid"],
+                   "order": args.order} if args.workload == "long" else
+                  {"workload": args.workload, "items": main_res["items"],
+                   "kv_bytes_per_step": main_res["kv_bytes"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_kernel<128,4>",
+                     "decode_us_mean": round(main_res["decode_ms_mean"] * 1e3, 3)},
+        "cpu_baseline": cpu,
+        "other_workloads": others,
+        "host_wall_ms_per_step": round(main_res["host_wall_ms_per_step"], 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,234 @@
+/*
+ * pkv.h - C ABI of libpkv: decode attention over a block-table paged KV
+ * cache, executed by a persistent kernel that drains a device work queue.
+ * Target: AMD Instinct MI355X (gfx950, CDNA4), HIP runtime.
+ *
+ * What is computed (PersistentKV page, "PersistentKV: Page-Aware Decode
+ * Scheduling for Long-Context LLM Serving on Commodity GPUs", Technical
+ * Summary, Methodology 1 "Native Block-Table Decode Engine"): for every
+ * sequence b and query head h, with G = Hq / Hkv and KV head floor(h / G),
+ *     s_t   = scale * q[b][h] . K_t          t = 0 .. L_b - 1
+ *     out   = sum_t softmax(s)_t V_t          (bf16, rounded to nearest even)
+ *     lse   = ln sum_t exp(s_t)               (fp32, natural log)
+ * where token t is read in place from page block_table[b][t / P], row
+ * t % P (no repacking, "Layout"), only tokens below L_b are read ("Row-Local
+ * Bounds"), and a row with L_b = 0 gets out = 0, lse = -inf (the neutral
+ * state).  Long rows may be cut into disjoint ranges whose partial states a
+ * separate merge kernel combines exactly ("Sequence Splitting"); the work
+ * queue holds only non-empty (row, KV head, range) items ("Compact
+ * Workqueue"); the split decision is the adaptive policy of Methodology 2
+ * "Calibrated Adaptive Policy".  Workgroups pop items with one atomic each,
+ * as the persistent executor on the GPUOS page pops tasks ("GPUOS: A GPU
+ * Operating System Primitive for Transparent Operation Fusion", section 4.1).
+ *
+ * Data layout (all row-major, contiguous, 16-byte aligned device memory):
+ *   q          bf16  [B][Hq][D]
+ *   k_pool     bf16  [num_pages][Hkv][P][D]      (one (page, head) slab of
+ *   v_pool     bf16  [num_pages][Hkv][P][D]       P*D values is contiguous)
+ *   block_table int32 [B][block_table_stride]    entries past ceil(L_b/P)
+ *                                                are ignored (may be -1)
+ *   ctx_lens   int32 [B]
+ *   out        bf16  [B][Hq][D]
+ *   lse        fp32  [B][Hq]
+ * Supported: page_size 16; head_dim 64 with G in {1, 2, 4, 8}; head_dim 128
+ * with G in {1, 2, 4}.
+ *
+ * Ownership: the caller owns every device buffer, including the workspace
+ * (size from pkv_workspace_size) and streams; the library never frees caller
+ * memory.  The library itself allocates only host memory: the handle and a
+ * small pinned staging area for queue uploads.  A handle is not thread-safe.
+ *
+ * Errors: every call returns a pkv_status; PKV_OK is 0 and every error is
+ * negative.  A call that fails validation enqueues nothing.  A fault detected
+ * on the device (a block-table entry outside [0, num_pages), a malformed
+ * item) sets an error word in the workspace; the kernel then reads page 0
+ * instead (so no access leaves the pool), and the next pkv_decode or
+ * pkv_query returns PKV_ERR_DEVICE_FAULT with the word in
+ * pkv_runtime_info.  pkv_last_error gives the text of the last failure.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_API __attribute__((visibility("default")))
+
+typedef int32_t pkv_status;
+enum {
+    PKV_OK = 0,
+    PKV_ERR_INVALID_ARG = -1,   /* null pointer, bad size, misaligned buffer */
+    PKV_ERR_UNSUPPORTED = -2,   /* head_dim / page_size / group size not built */
+    PKV_ERR_CAPACITY = -3,      /* batch, items or pages exceed the config */
+    PKV_ERR_HIP = -4,           /* HIP runtime error (text in pkv_last_error) */
+    PKV_ERR_STATE = -5,         /* wrong call order (e.g. decode before build) */
+    PKV_ERR_DEVICE_FAULT = -6,  /* device error word set (see pkv_runtime_info) */
+    PKV_ERR_TIMEOUT = -7
+};
+
+/* Split policy (PersistentKV page, Methodology 2).  AUTO: cut rows into
+ * kv_chunk_tokens-token ranges iff B * Hkv < num_cus and some L_b exceeds
+ * kv_chunk_tokens; otherwise one item per (row, KV head). */
+enum { PKV_POLICY_AUTO = 0, PKV_POLICY_NO_SPLIT = 1, PKV_POLICY_SPLIT = 2 };
+
+/* Queue order: CANONICAL = (seq, kv_head, chunk) ascending; LPT = stable sort
+ * of the canonical list by item length, longest first. */
+enum { PKV_ORDER_CANONICAL = 0, PKV_ORDER_LPT = 1 };
+
+/* Device error words (pkv_runtime_info.error_code). */
+enum {
+    PKV_DEVERR_NONE = 0,
+    PKV_DEVERR_PAGE_OOB = 1,    /* block-table entry outside the pool; detail = entry */
+    PKV_DEVERR_BAD_ITEM = 2     /* item fields out of range; detail = item index */
+};
+
+typedef struct pkv_config {
+    uint32_t struct_size;       /* sizeof(pkv_config): ABI version check */
+    int32_t num_q_heads;        /* Hq */
+    int32_t num_kv_heads;       /* Hkv; Hq % Hkv == 0 */
+    int32_t head_dim;           /* D: 64 or 128 */
+    int32_t page_size;          /* P: 16 */
+    int32_t num_pages;          /* pages in each of k_pool / v_pool */
+    int32_t max_batch;          /* largest B passed to pkv_build_queue */
+    int32_t max_pages_per_seq;  /* longest row in pages (bounds L_b and items) */
+    float scale;                /* 0 -> 1 / sqrt(D) */
+    int32_t policy;             /* PKV_POLICY_* */
+    int32_t order;              /* PKV_ORDER_* */
+    int32_t kv_chunk_tokens;    /* split range length; 0 -> 4096; multiple of P */
+    int32_t num_cus;            /* policy input; 0 -> the device's CU count */
+    int32_t max_items;          /* queue capacity; 0 -> bound from the shape */
+    int32_t wg_per_cu;          /* persistent grid = CUs * wg_per_cu; 0 -> 1 */
+    int32_t reserved[9];        /* must be zero */
+} pkv_config;
+
+typedef struct pkv_tensors {
+    const void* q;              /* bf16 [B][Hq][D] */
+    const void* k_pool;         /* bf16 [num_pages][Hkv][P][D] */
+    const void* v_pool;         /* bf16 [num_pages][Hkv][P][D] */
+    const int32_t* block_table; /* int32 [B][block_table_stride] */
+    const int32_t* ctx_lens;    /* int32 [B] (device copy; used by the device
+                                   queue builder) */
+    void* out;                  /* bf16 [B][Hq][D] */
+    float* lse;                 /* fp32 [B][Hq] */
+    int32_t batch;              /* B: must equal the batch of the built queue */
+    int32_t block_table_stride; /* elements per block-table row; 0 -> max_pages_per_seq */
+} pkv_tensors;
+
+typedef struct pkv_queue_info {
+    int32_t n_items;            /* items in the compact queue */
+    int32_t split;              /* policy decision: 1 = ranges of kv_chunk_tokens */
+    int32_t chunk_tokens;       /* range length used */
+    int32_t n_split_rows;       /* rows with more than one range */
+    int32_t n_merge_rows;       /* rows finished by the merge kernel (split or empty) */
+    int32_t n_partial_slots;    /* partial states written by the decode kernel */
+    int32_t launches_per_step;  /* kernels pkv_decode enqueues: 1 or 2 */
+    int32_t reserved;
+    uint64_t kv_bytes;          /* K+V bytes of valid tokens (algorithmic read volume) */
+    uint64_t partial_bytes;     /* bytes of partial states written and re-read */
+} pkv_queue_info;
+
+typedef struct pkv_runtime_info {
+    uint32_t error_code;        /* PKV_DEVERR_* */
+    uint32_t error_detail;
+    uint32_t queue_head;        /* next item index the kernel would pop (0 when idle) */
+    uint32_t n_items;           /* items of the current queue */
+    uint32_t items_done;        /* items finished since create (wraps) */
+    uint32_t decode_calls;      /* pkv_decode calls since create */
+    int32_t grid;               /* persistent workgroups per decode launch */
+    int32_t num_cus;            /* CUs of the device */
+} pkv_runtime_info;
+
+/* Workspace regions (byte offsets into the caller's workspace), so that a
+ * caller or test can inspect the queue and the partial states in place. */
+typedef struct pkv_layout {
+    uint64_t ctrl_off;          /* control words (queue head, error word, counters) */
+    uint64_t queue_off;         /* queue header: int32 n_items, n_merge_rows, split,
+                                   chunk_tokens, batch */
+    uint64_t n_chunks_off;      /* int32 [max_batch] */
+    uint64_t part_off_off;      /* int32 [max_batch + 1] */
+    uint64_t merge_rows_off;    /* int32 [max_batch] */
+    uint64_t items_off;         /* 16-byte items [max_items]: u32 seq, u16 kv_head,
+                                   u16 chunk, u32 tok_begin, u32 tok_end */
+    uint64_t partial_o_off;     /* fp32 [max_items][G][D], normalised partial outputs */
+    uint64_t partial_lse_off;   /* fp32 [max_items][G], natural-log partial LSE */
+    uint64_t total_bytes;
+    int32_t max_items;
+    int32_t reserved;
+} pkv_layout;
+
+typedef struct pkv_handle pkv_handle;
+
+/* Bytes of device workspace a handle with this config needs. */
+PKV_API pkv_status pkv_workspace_size(const pkv_config* cfg, size_t* bytes);
+
+/* Workspace layout of a config (pure host computation). */
+PKV_API pkv_status pkv_workspace_layout(const pkv_config* cfg, pkv_layout* layout);
+
+/* Create a handle on the current HIP device.  workspace: device memory of at
+ * least pkv_workspace_size bytes, 256-byte aligned, owned by the caller and
+ * kept alive until pkv_destroy.  stream: hipStream_t used for queue uploads
+ * (0 = the null stream).  Initialises the workspace's control words
+ * (asynchronously on stream). */
+PKV_API pkv_status pkv_create(const pkv_config* cfg, void* workspace, size_t workspace_bytes,
+                              void* stream, pkv_handle** out);
+
+/* Build the compact work queue on the host from host context lengths
+ * (int32 [batch]) and enqueue its upload on the handle's stream.  Returns
+ * after the upload is enqueued; info (nullable) receives the counters. */
+PKV_API pkv_status pkv_build_queue(pkv_handle* h, const int32_t* ctx_lens_host, int32_t batch,
+                                   pkv_queue_info* info);
+
+/* Same queue, built on the device from device context lengths (int32
+ * [batch]) by one workgroup on stream; bit-identical to pkv_build_queue.
+ * Supports PKV_ORDER_CANONICAL only.  The split decision is taken on the
+ * device, so the host learns no counters. */
+PKV_API pkv_status pkv_build_queue_device(pkv_handle* h, const int32_t* ctx_lens_device,
+                                          int32_t batch, void* stream);
+
+/* Enqueue the decode for the built queue on stream (async): the persistent
+ * decode kernel, then, if any row is split or empty, the merge kernel.
+ * Returns PKV_ERR_DEVICE_FAULT (and enqueues nothing) if an earlier call left
+ * a device error word set. */
+PKV_API pkv_status pkv_decode(pkv_handle* h, const pkv_tensors* t, void* stream);
+
+/* Optional timing: hipEvent_t handles recorded on the decode stream right
+ * before and right after the persistent decode kernel (not the merge).  Pass
+ * nulls to stop recording. */
+PKV_API pkv_status pkv_set_decode_events(pkv_handle* h, void* before, void* after);
+
+/* Read the control words (synchronises the device).  Returns
+ * PKV_ERR_DEVICE_FAULT when the device error word is set. */
+PKV_API pkv_status pkv_query(pkv_handle* h, pkv_runtime_info* info);
+
+/* Clear the device error word (synchronises the device). */
+PKV_API pkv_status pkv_clear_error(pkv_handle* h);
+
+/* Destroy the handle (does not free the caller's workspace). */
+PKV_API pkv_status pkv_destroy(pkv_handle* h);
+
+PKV_API const char* pkv_status_string(pkv_status s);
+PKV_API const char* pkv_last_error(const pkv_handle* h);
+
+/* Host-only planning, no handle and no GPU: the queue pkv_build_queue would
+ * upload, written into caller host arrays: items (16-byte entries, capacity
+ * items_cap), n_chunks [batch], part_off [batch + 1], merge_rows [batch].
+ * num_cus must be set in cfg (no device is queried). */
+PKV_API pkv_status pkv_plan_queue(const pkv_config* cfg, const int32_t* ctx_lens, int32_t batch,
+                                  void* items, int32_t items_cap, int32_t* n_chunks,
+                                  int32_t* part_off, int32_t* merge_rows, pkv_queue_info* info);
+
+/* Test hook: write the bf16 K and V rows that the decode kernel's own gather
+ * reads for queue item item_index, in token order, to device buffers k_out and
+ * v_out (bf16 [Hkv-local: 1][tok_end - tok_begin][D]).  Enqueued on stream. */
+PKV_API pkv_status pkv_debug_gather(pkv_handle* h, const pkv_tensors* t, int32_t item_index,
+                                    void* k_out, void* v_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,385 @@
+// C-ABI entry points of libpkv (declared in include/pkv.h).
+//
+// Ownership follows the GPUOS page's rule that the runtime only receives
+// pointers to memory the framework already allocated ("GPUOS: A GPU Operating
+// System Primitive for Transparent Operation Fusion", section 4.3 "Memory
+// Management and Safety"): every device buffer, the workspace included, is
+// the caller's.  Device faults are reported back to the host as an error
+// code, in the spirit of that page's kill switches (section 5, "returning an
+// error code to the host").
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <string>
+
+#include "pkv_internal.h"
+
+using namespace pkv;
+
+struct pkv_handle {
+    Resolved r;
+    pkv_layout lay;
+    int device = 0;
+    int device_cus = 0;
+    int grid = 0;
+    unsigned char* ws = nullptr;
+    hipStream_t stream = nullptr;
+    // pinned staging for queue uploads, double-buffered
+    unsigned char* staging[2] = {nullptr, nullptr};
+    hipEvent_t staging_evt[2] = {nullptr, nullptr};
+    bool staging_pending[2] = {false, false};
+    int staging_next = 0;
+    size_t staging_bytes = 0;
+    hipEvent_t upload_evt = nullptr;
+    // mapped host word mirrored by the kernels on a device fault
+    uint32_t* host_err = nullptr;
+    uint32_t* host_err_dev = nullptr;
+    bool built = false;
+    bool built_on_device = false;
+    int batch = 0;
+    pkv_queue_info qinfo{};
+    hipEvent_t ev_before = nullptr;
+    hipEvent_t ev_after = nullptr;
+    std::string last_error;
+};
+
+namespace {
+
+pkv_status fail(pkv_handle* h, pkv_status s, const std::string& why) {
+    if (h) h->last_error = why;
+    return s;
+}
+
+pkv_status hip_fail(pkv_handle* h, hipError_t e, const char* what) {
+    return fail(h, PKV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+DecodeParams make_params(const pkv_handle* h, const pkv_tensors* t) {
+    DecodeParams p;
+    memset(&p, 0, sizeof(p));
+    p.q = static_cast<const uint16_t*>(t ? t->q : nullptr);
+    p.k_pool = static_cast<const uint16_t*>(t ? t->k_pool : nullptr);
+    p.v_pool = static_cast<const uint16_t*>(t ? t->v_pool : nullptr);
+    p.block_table = t ? t->block_table : nullptr;
+    p.out = static_cast<uint16_t*>(t ? t->out : nullptr);
+    p.lse = t ? t->lse : nullptr;
+    p.ctrl = reinterpret_cast<Ctrl*>(h->ws + h->lay.ctrl_off);
+    p.qhdr = reinterpret_cast<const QHdr*>(h->ws + h->lay.queue_off);
+    p.n_chunks = reinterpret_cast<const int32_t*>(h->ws + h->lay.n_chunks_off);
+    p.part_off = reinterpret_cast<const int32_t*>(h->ws + h->lay.part_off_off);
+    p.merge_rows = reinterpret_cast<const int32_t*>(h->ws + h->lay.merge_rows_off);
+    p.items = reinterpret_cast<const Item*>(h->ws + h->lay.items_off);
+    p.partial_o = reinterpret_cast<float*>(h->ws + h->lay.partial_o_off);
+    p.partial_lse = reinterpret_cast<float*>(h->ws + h->lay.partial_lse_off);
+    p.host_error = h->host_err_dev;
+    p.batch = t ? t->batch : 0;
+    p.bt_stride = (t && t->block_table_stride) ? t->block_table_stride : h->r.max_pages_per_seq;
+    p.num_pages = h->r.num_pages;
+    p.hq = h->r.hq;
+    p.hkv = h->r.hkv;
+    p.max_tokens = h->r.max_pages_per_seq * h->r.page;
+    p.max_items = h->r.max_items;
+    p.scale_log2 = h->r.scale * 1.44269504088896340736f;
+    return p;
+}
+
+pkv_status check_tensors(pkv_handle* h, const pkv_tensors* t) {
+    if (!t) return fail(h, PKV_ERR_INVALID_ARG, "null tensors");
+    if (!t->q || !t->k_pool || !t->v_pool || !t->block_table || !t->out || !t->lse)
+        return fail(h, PKV_ERR_INVALID_ARG, "null tensor pointer");
+    if (!aligned(t->q, 16) || !aligned(t->k_pool, 16) || !aligned(t->v_pool, 16) || !aligned(t->out, 16))
+        return fail(h, PKV_ERR_INVALID_ARG, "q, k_pool, v_pool and out must be 16-byte aligned");
+    if (!aligned(t->block_table, 4) || !aligned(t->lse, 4) || (t->ctx_lens && !aligned(t->ctx_lens, 4)))
+        return fail(h, PKV_ERR_INVALID_ARG, "block_table, ctx_lens and lse must be 4-byte aligned");
+    if (t->batch < 0 || t->batch > h->r.max_batch) return fail(h, PKV_ERR_CAPACITY, "batch outside [0, max_batch]");
+    if (t->block_table_stride < 0 ||
+        (t->block_table_stride > 0 && t->block_table_stride < h->r.max_pages_per_seq))
+        return fail(h, PKV_ERR_INVALID_ARG, "block_table_stride smaller than max_pages_per_seq");
+    return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+PKV_API const char* pkv_status_string(pkv_status s) {
+    switch (s) {
+        case PKV_OK: return "ok";
+        case PKV_ERR_INVALID_ARG: return "invalid argument";
+        case PKV_ERR_UNSUPPORTED: return "unsupported shape";
+        case PKV_ERR_CAPACITY: return "capacity exceeded";
+        case PKV_ERR_HIP: return "HIP runtime error";
+        case PKV_ERR_STATE: return "wrong call order";
+        case PKV_ERR_DEVICE_FAULT: return "device fault";
+        case PKV_ERR_TIMEOUT: return "timeout";
+        default: return "unknown status";
+    }
+}
+
+PKV_API const char* pkv_last_error(const pkv_handle* h) { return h ? h->last_error.c_str() : ""; }
+
+PKV_API pkv_status pkv_workspace_layout(const pkv_config* cfg, pkv_layout* layout) {
+    if (!layout) return PKV_ERR_INVALID_ARG;
+    Resolved r;
+    const char* why;
+    // The layout does not depend on the CU count; use 1 when the config leaves it unset.
+    pkv_status s = resolve_config(cfg, 1, &r, &why);
+    if (s != PKV_OK) return s;
+    compute_layout(r, layout);
+    return PKV_OK;
+}
+
+PKV_API pkv_status pkv_workspace_size(const pkv_config* cfg, size_t* bytes) {
+    if (!bytes) return PKV_ERR_INVALID_ARG;
+    pkv_layout lay;
+    pkv_status s = pkv_workspace_layout(cfg, &lay);
+    if (s != PKV_OK) return s;
+    *bytes = (size_t)lay.total_bytes;
+    return PKV_OK;
+}
+
+PKV_API pkv_status pkv_plan_queue(const pkv_config* cfg, const int32_t* ctx_lens, int32_t batch,
+                                  void* items, int32_t items_cap, int32_t* n_chunks,
+                                  int32_t* part_off, int32_t* merge_rows, pkv_queue_info* info) {
+    Resolved r;
+    const char* why;
+    pkv_status s = resolve_config(cfg, 0, &r, &why);
+    if (s != PKV_OK) return s;
+    if (!items || !n_chunks || !part_off || !merge_rows || items_cap < 0) return PKV_ERR_INVALID_ARG;
+    QHdr qh;
+    return plan_queue(r, ctx_lens, batch, &qh, n_chunks, part_off, merge_rows,
+                      static_cast<Item*>(items), items_cap, info, &why);
+}
+
+PKV_API pkv_status pkv_create(const pkv_config* cfg, void* workspace, size_t workspace_bytes,
+                              void* stream, pkv_handle** out) {
+    if (!out) return PKV_ERR_INVALID_ARG;
+    *out = nullptr;
+    pkv_handle* h = new (std::nothrow) pkv_handle();
+    if (!h) return PKV_ERR_CAPACITY;
+    hipError_t e = hipGetDevice(&h->device);
+    if (e != hipSuccess) { delete h; return PKV_ERR_HIP; }
+    e = hipDeviceGetAttribute(&h->device_cus, hipDeviceAttributeMultiprocessorCount, h->device);
+    if (e != hipSuccess) { delete h; return PKV_ERR_HIP; }
+    const char* why;
+    pkv_status s = resolve_config(cfg, h->device_cus, &h->r, &why);
+    if (s != PKV_OK) { delete h; return s; }
+    compute_layout(h->r, &h->lay);
+    if (!workspace || workspace_bytes < h->lay.total_bytes || !aligned(workspace, 256)) {
+        delete h;
+        return PKV_ERR_INVALID_ARG;
+    }
+    h->ws = static_cast<unsigned char*>(workspace);
+    h->stream = static_cast<hipStream_t>(stream);
+    h->grid = h->device_cus * h->r.wg_per_cu;
+    h->staging_bytes = h->lay.items_off - h->lay.queue_off + 16ull * h->r.max_items;
+    for (int i = 0; i < 2; ++i) {
+        if ((e = hipHostMalloc((void**)&h->staging[i], h->staging_bytes, hipHostMallocDefault)) != hipSuccess ||
+            (e = hipEventCreateWithFlags(&h->staging_evt[i], hipEventDisableTiming)) != hipSuccess) {
+            pkv_destroy(h);
+            return PKV_ERR_HIP;
+        }
+        memset(h->staging[i], 0, h->staging_bytes);
+    }
+    if ((e = hipEventCreateWithFlags(&h->upload_evt, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipHostMalloc((void**)&h->host_err, 64, hipHostMallocMapped | hipHostMallocCoherent)) != hipSuccess ||
+        (e = hipHostGetDevicePointer((void**)&h->host_err_dev, h->host_err, 0)) != hipSuccess) {
+        pkv_destroy(h);
+        return PKV_ERR_HIP;
+    }
+    memset(h->host_err, 0, 64);
+    int rc = launch_init_ctrl(reinterpret_cast<Ctrl*>(h->ws + h->lay.ctrl_off), h->stream);
+    if (rc != 0) { pkv_destroy(h); return PKV_ERR_HIP; }
+    // an empty queue until the first build
+    QHdr* qh = reinterpret_cast<QHdr*>(h->staging[0]);
+    memset(qh, 0, sizeof(QHdr));
+    e = hipMemcpyAsync(h->ws + h->lay.queue_off, qh, sizeof(QHdr), hipMemcpyHostToDevice, h->stream);
+    if (e == hipSuccess) e = hipEventRecord(h->staging_evt[0], h->stream);
+    if (e == hipSuccess) e = hipEventRecord(h->upload_evt, h->stream);
+    if (e != hipSuccess) { pkv_destroy(h); return PKV_ERR_HIP; }
+    h->staging_pending[0] = true;
+    h->staging_next = 1;
+    *out = h;
+    return PKV_OK;
+}
+
+PKV_API pkv_status pkv_build_queue(pkv_handle* h, const int32_t* ctx_lens_host, int32_t batch,
+                                   pkv_queue_info* info) {
+    if (!h) return PKV_ERR_INVALID_ARG;
+    if (batch < 0 || batch > h->r.max_batch) return fail(h, PKV_ERR_CAPACITY, "batch outside [0, max_batch]");
+    if (batch > 0 && !ctx_lens_host) return fail(h, PKV_ERR_INVALID_ARG, "null ctx_lens");
+    const int i = h->staging_next;
+    hipError_t e;
+    if (h->staging_pending[i]) {          // the previous upload from this buffer must have left
+        if ((e = hipEventSynchronize(h->staging_evt[i])) != hipSuccess) return hip_fail(h, e, "staging wait");
+        h->staging_pending[i] = false;
+    }
+    unsigned char* st = h->staging[i];
+    const uint64_t q0 = h->lay.queue_off;
+    QHdr* qh = reinterpret_cast<QHdr*>(st);
+    int32_t* n_chunks = reinterpret_cast<int32_t*>(st + (h->lay.n_chunks_off - q0));
+    int32_t* part_off = reinterpret_cast<int32_t*>(st + (h->lay.part_off_off - q0));
+    int32_t* merge_rows = reinterpret_cast<int32_t*>(st + (h->lay.merge_rows_off - q0));
+    Item* items = reinterpret_cast<Item*>(st + (h->lay.items_off - q0));
+    pkv_queue_info qi;
+    const char* why;
+    pkv_status s = plan_queue(h->r, ctx_lens_host, batch, qh, n_chunks, part_off, merge_rows, items,
+                              h->r.max_items, &qi, &why);
+    if (s != PKV_OK) return fail(h, s, why);
+    const size_t bytes = (h->lay.items_off - q0) + 16ull * qi.n_items;
+    if ((e = hipMemcpyAsync(h->ws + q0, st, bytes, hipMemcpyHostToDevice, h->stream)) != hipSuccess)
+        return hip_fail(h, e, "queue upload");
+    if ((e = hipEventRecord(h->staging_evt[i], h->stream)) != hipSuccess) return hip_fail(h, e, "event record");
+    if ((e = hipEventRecord(h->upload_evt, h->stream)) != hipSuccess) return hip_fail(h, e, "event record");
+    h->staging_pending[i] = true;
+    h->staging_next = 1 - i;
+    h->built = true;
+    h->built_on_device = false;
+    h->batch = batch;
+    h->qinfo = qi;
+    if (info) *info = qi;
+    return PKV_OK;
+}
+
+PKV_API pkv_status pkv_build_queue_device(pkv_handle* h, const int32_t* ctx_lens_device, int32_t batch,
+                                          void* stream) {
+    if (!h) return PKV_ERR_INVALID_ARG;
+    if (batch < 0 || batch > h->r.max_batch) return fail(h, PKV_ERR_CAPACITY, "batch outside [0, max_batch]");
+    if (batch > 4096) return fail(h, PKV_ERR_UNSUPPORTED, "device builder supports batch <= 4096");
+    if (batch > 0 && (!ctx_lens_device || !aligned(ctx_lens_device, 4)))
+        return fail(h, PKV_ERR_INVALID_ARG, "null or misaligned ctx_lens");
+    if (h->r.order != PKV_ORDER_CANONICAL) return fail(h, PKV_ERR_UNSUPPORTED, "device builder: canonical order only");
+    BuildParams p;
+    memset(&p, 0, sizeof(p));
+    p.ctx_lens = ctx_lens_device;
+    p.qhdr = reinterpret_cast<QHdr*>(h->ws + h->lay.queue_off);
+    p.n_chunks = reinterpret_cast<int32_t*>(h->ws + h->lay.n_chunks_off);
+    p.part_off = reinterpret_cast<int32_t*>(h->ws + h->lay.part_off_off);
+    p.merge_rows = reinterpret_cast<int32_t*>(h->ws + h->lay.merge_rows_off);
+    p.items = reinterpret_cast<Item*>(h->ws + h->lay.items_off);
+    p.ctrl = reinterpret_cast<Ctrl*>(h->ws + h->lay.ctrl_off);
+    p.host_error = h->host_err_dev;
+    p.batch = batch;
+    p.hkv = h->r.hkv;
+    p.num_cus = h->r.num_cus;
+    p.chunk = h->r.chunk;
+    p.policy = h->r.policy;
+    p.max_items = h->r.max_items;
+    p.max_tokens = h->r.max_pages_per_seq * h->r.page;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (s != h->stream && (e = hipStreamWaitEvent(s, h->upload_evt, 0)) != hipSuccess)
+        return hip_fail(h, e, "stream wait");
+    int rc = launch_build_queue(p, s);
+    if (rc != 0) return hip_fail(h, (hipError_t)rc, "build_queue launch");
+    if ((e = hipEventRecord(h->upload_evt, s)) != hipSuccess) return hip_fail(h, e, "event record");
+    h->built = true;
+    h->built_on_device = true;
+    h->batch = batch;
+    memset(&h->qinfo, 0, sizeof(h->qinfo));
+    return PKV_OK;
+}
+
+PKV_API pkv_status pkv_decode(pkv_handle* h, const pkv_tensors* t, void* stream) {
+    if (!h) return PKV_ERR_INVALID_ARG;
+    if (!h->built) return fail(h, PKV_ERR_STATE, "pkv_decode before pkv_build_queue");
+    pkv_status s = check_tensors(h, t);
+    if (s != PKV_OK) return s;
+    if (t->batch != h->batch) return fail(h, PKV_ERR_INVALID_ARG, "batch differs from the built queue");
+    if (__atomic_load_n(h->host_err, __ATOMIC_ACQUIRE) != 0)
+        return fail(h, PKV_ERR_DEVICE_FAULT, "device error word set (see pkv_query)");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (st != h->stream && (e = hipStreamWaitEvent(st, h->upload_evt, 0)) != hipSuccess)
+        return hip_fail(h, e, "stream wait");
+    const DecodeParams p = make_params(h, t);
+    if (h->ev_before && (e = hipEventRecord(h->ev_before, st)) != hipSuccess) return hip_fail(h, e, "event record");
+    int rc = launch_decode(p, h->r.d, h->r.g, h->grid, st);
+    if (rc != 0) return hip_fail(h, (hipError_t)rc, "decode launch");
+    if (h->ev_after && (e = hipEventRecord(h->ev_after, st)) != hipSuccess) return hip_fail(h, e, "event record");
+    const int merge_rows = h->built_on_device ? h->batch : h->qinfo.n_merge_rows;
+    if (merge_rows > 0) {
+        rc = launch_merge(p, h->r.d, h->r.g, merge_rows, st);
+        if (rc != 0) return hip_fail(h, (hipError_t)rc, "merge launch");
+    }
+    return PKV_OK;
+}
+
+PKV_API pkv_status pkv_set_decode_events(pkv_handle* h, void* before, void* after) {
+    if (!h) return PKV_ERR_INVALID_ARG;
+    if ((before == nullptr) != (after == nullptr)) return fail(h, PKV_ERR_INVALID_ARG, "set both events or neither");
+    h->ev_before = static_cast<hipEvent_t>(before);
+    h->ev_after = static_cast<hipEvent_t>(after);
+    return PKV_OK;
+}
+
+PKV_API pkv_status pkv_query(pkv_handle* h, pkv_runtime_info* info) {
+    if (!h || !info) return PKV_ERR_INVALID_ARG;
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(h, e, "device sync");
+    Ctrl c;
+    QHdr q;
+    if ((e = hipMemcpy(&c, h->ws + h->lay.ctrl_off, sizeof(c), hipMemcpyDeviceToHost)) != hipSuccess)
+        return hip_fail(h, e, "ctrl read");
+    if ((e = hipMemcpy(&q, h->ws + h->lay.queue_off, sizeof(q), hipMemcpyDeviceToHost)) != hipSuccess)
+        return hip_fail(h, e, "queue header read");
+    memset(info, 0, sizeof(*info));
+    info->error_code = c.error_code;
+    info->error_detail = c.error_detail;
+    info->queue_head = c.head;
+    info->n_items = (uint32_t)q.n_items;
+    info->items_done = c.items_done;
+    info->decode_calls = c.decode_calls;
+    info->grid = h->grid;
+    info->num_cus = h->device_cus;
+    if (c.error_code != 0) return fail(h, PKV_ERR_DEVICE_FAULT, "device error word set");
+    return PKV_OK;
+}
+
+PKV_API pkv_status pkv_clear_error(pkv_handle* h) {
+    if (!h) return PKV_ERR_INVALID_ARG;
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(h, e, "device sync");
+    const uint32_t z[2] = {0u, 0u};
+    e = hipMemcpy(h->ws + h->lay.ctrl_off + offsetof(Ctrl, error_code), z, sizeof(z), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(h, e, "clear error");
+    __atomic_store_n(h->host_err, 0u, __ATOMIC_RELEASE);
+    return PKV_OK;
+}
+
+PKV_API pkv_status pkv_debug_gather(pkv_handle* h, const pkv_tensors* t, int32_t item_index,
+                                    void* k_out, void* v_out, void* stream) {
+    if (!h) return PKV_ERR_INVALID_ARG;
+    if (!h->built) return fail(h, PKV_ERR_STATE, "pkv_debug_gather before pkv_build_queue");
+    pkv_status s = check_tensors(h, t);
+    if (s != PKV_OK) return s;
+    if (!k_out || !v_out || !aligned(k_out, 16) || !aligned(v_out, 16))
+        return fail(h, PKV_ERR_INVALID_ARG, "k_out and v_out must be 16-byte aligned");
+    if (item_index < 0) return fail(h, PKV_ERR_INVALID_ARG, "negative item index");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (st != h->stream && (e = hipStreamWaitEvent(st, h->upload_evt, 0)) != hipSuccess)
+        return hip_fail(h, e, "stream wait");
+    const DecodeParams p = make_params(h, t);
+    int rc = launch_debug_gather(p, h->r.d, item_index, static_cast<uint16_t*>(k_out),
+                                 static_cast<uint16_t*>(v_out), st);
+    if (rc != 0) return hip_fail(h, (hipError_t)rc, "gather launch");
+    return PKV_OK;
+}
+
+PKV_API pkv_status pkv_destroy(pkv_handle* h) {
+    if (!h) return PKV_ERR_INVALID_ARG;
+    if (h->stream || h->staging[0]) (void)hipStreamSynchronize(h->stream);
+    for (int i = 0; i < 2; ++i) {
+        if (h->staging_evt[i]) (void)hipEventDestroy(h->staging_evt[i]);
+        if (h->staging[i]) (void)hipHostFree(h->staging[i]);
+    }
+    if (h->upload_evt) (void)hipEventDestroy(h->upload_evt);
+    if (h->host_err) (void)hipHostFree(h->host_err);
+    delete h;
+    return PKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,173 @@
+// Host side of the work queue: configuration defaults, workspace layout, and
+// the adaptive split policy plus compact queue builder.
+//
+// Policy and queue follow the PersistentKV page ("PersistentKV: Page-Aware
+// Decode Scheduling for Long-Context LLM Serving on Commodity GPUs",
+// Technical Summary): Methodology 1 "Row-Local Bounds" (ranges follow each
+// row's true length), "Compact Workqueue" (tasks only for non-empty
+// row / KV-head / split intervals) and Methodology 2 "Calibrated Adaptive
+// Policy" (split when too few rows exist to fill the GPU, otherwise one task
+// per row and head).  The page's third-party route does not exist here and
+// becomes the no-split route; the threshold is the occupancy rule
+// B * Hkv < CUs with some row longer than one range.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+
+pkv_status resolve_config(const pkv_config* cfg, int device_cus, Resolved* r, const char** why) {
+    *why = "";
+    if (!cfg || !r) { *why = "null config"; return PKV_ERR_INVALID_ARG; }
+    if (cfg->struct_size != sizeof(pkv_config)) { *why = "pkv_config.struct_size mismatch"; return PKV_ERR_INVALID_ARG; }
+    for (int i = 0; i < 9; ++i)
+        if (cfg->reserved[i]) { *why = "reserved config fields must be zero"; return PKV_ERR_INVALID_ARG; }
+    if (cfg->num_q_heads <= 0 || cfg->num_kv_heads <= 0 || cfg->num_q_heads % cfg->num_kv_heads) {
+        *why = "num_q_heads must be a positive multiple of num_kv_heads"; return PKV_ERR_INVALID_ARG;
+    }
+    if (cfg->num_kv_heads > 65535) { *why = "num_kv_heads exceeds 65535"; return PKV_ERR_UNSUPPORTED; }
+    r->hq = cfg->num_q_heads;
+    r->hkv = cfg->num_kv_heads;
+    r->g = r->hq / r->hkv;
+    if (!(r->g == 1 || r->g == 2 || r->g == 4 || r->g == 8)) { *why = "group size must be 1, 2, 4 or 8"; return PKV_ERR_UNSUPPORTED; }
+    if (!(cfg->head_dim == 64 || cfg->head_dim == 128)) { *why = "head_dim must be 64 or 128"; return PKV_ERR_UNSUPPORTED; }
+    r->d = cfg->head_dim;
+    if (r->d == 128 && r->g == 8) { *why = "group size 8 is built for head_dim 64 only"; return PKV_ERR_UNSUPPORTED; }
+    if (cfg->page_size != kPageSize) { *why = "page_size must be 16"; return PKV_ERR_UNSUPPORTED; }
+    r->page = kPageSize;
+    if (cfg->num_pages <= 0 || cfg->max_batch <= 0 || cfg->max_pages_per_seq <= 0) {
+        *why = "num_pages, max_batch and max_pages_per_seq must be positive"; return PKV_ERR_INVALID_ARG;
+    }
+    if ((int64_t)cfg->max_pages_per_seq * kPageSize > INT32_MAX) { *why = "max_pages_per_seq too large"; return PKV_ERR_CAPACITY; }
+    r->num_pages = cfg->num_pages;
+    r->max_batch = cfg->max_batch;
+    r->max_pages_per_seq = cfg->max_pages_per_seq;
+    if (!isfinite(cfg->scale)) { *why = "scale must be finite"; return PKV_ERR_INVALID_ARG; }
+    r->scale = cfg->scale == 0.0f ? 1.0f / sqrtf((float)r->d) : cfg->scale;
+    if (cfg->policy < PKV_POLICY_AUTO || cfg->policy > PKV_POLICY_SPLIT) { *why = "unknown policy"; return PKV_ERR_INVALID_ARG; }
+    r->policy = cfg->policy;
+    if (cfg->order != PKV_ORDER_CANONICAL && cfg->order != PKV_ORDER_LPT) { *why = "unknown order"; return PKV_ERR_INVALID_ARG; }
+    r->order = cfg->order;
+    r->chunk = cfg->kv_chunk_tokens == 0 ? kDefaultChunk : cfg->kv_chunk_tokens;
+    if (r->chunk <= 0 || r->chunk % kPageSize) { *why = "kv_chunk_tokens must be a positive multiple of 16"; return PKV_ERR_INVALID_ARG; }
+    const int64_t max_tokens = (int64_t)r->max_pages_per_seq * kPageSize;
+    const int64_t max_chunks = (max_tokens + r->chunk - 1) / r->chunk;
+    if (max_chunks > 65535) { *why = "more than 65535 ranges per row"; return PKV_ERR_CAPACITY; }
+    r->num_cus = cfg->num_cus > 0 ? cfg->num_cus : device_cus;
+    if (r->num_cus <= 0) { *why = "num_cus unknown (set it in the config)"; return PKV_ERR_INVALID_ARG; }
+    if (cfg->max_items < 0) { *why = "max_items must be >= 0"; return PKV_ERR_INVALID_ARG; }
+    if (cfg->max_items > 0) {
+        r->max_items = cfg->max_items;
+    } else {
+        const int64_t bound = (int64_t)r->hkv * r->max_batch * max_chunks;
+        if (bound > (int64_t)1 << 28) { *why = "derived max_items too large; set max_items"; return PKV_ERR_CAPACITY; }
+        r->max_items = (int)bound;
+    }
+    r->wg_per_cu = cfg->wg_per_cu == 0 ? 1 : cfg->wg_per_cu;
+    if (r->wg_per_cu < 1 || r->wg_per_cu > 8) { *why = "wg_per_cu must be 1..8"; return PKV_ERR_INVALID_ARG; }
+    return PKV_OK;
+}
+
+void compute_layout(const Resolved& r, pkv_layout* lay) {
+    memset(lay, 0, sizeof(*lay));
+    uint64_t off = 0;
+    lay->ctrl_off = off;
+    off = align256(off + sizeof(Ctrl));
+    lay->queue_off = off;
+    off = align256(off + sizeof(QHdr));
+    lay->n_chunks_off = off;
+    off = align256(off + 4ull * r.max_batch);
+    lay->part_off_off = off;
+    off = align256(off + 4ull * (r.max_batch + 1));
+    lay->merge_rows_off = off;
+    off = align256(off + 4ull * r.max_batch);
+    lay->items_off = off;
+    off = align256(off + 16ull * r.max_items);
+    lay->partial_o_off = off;
+    off = align256(off + 4ull * r.max_items * r.g * r.d);
+    lay->partial_lse_off = off;
+    off = align256(off + 4ull * r.max_items * r.g);
+    lay->total_bytes = off;
+    lay->max_items = r.max_items;
+}
+
+pkv_status plan_queue(const Resolved& r, const int32_t* ctx_lens, int32_t batch, QHdr* qh,
+                      int32_t* n_chunks, int32_t* part_off, int32_t* merge_rows, Item* items,
+                      int32_t items_cap, pkv_queue_info* info, const char** why) {
+    *why = "";
+    if (batch < 0 || batch > r.max_batch) { *why = "batch outside [0, max_batch]"; return PKV_ERR_CAPACITY; }
+    if (batch > 0 && !ctx_lens) { *why = "null ctx_lens"; return PKV_ERR_INVALID_ARG; }
+    const int64_t max_tokens = (int64_t)r.max_pages_per_seq * r.page;
+    int64_t max_len = 0, sum_len = 0;
+    for (int b = 0; b < batch; ++b) {
+        const int64_t L = ctx_lens[b];
+        if (L < 0) { *why = "negative context length"; return PKV_ERR_INVALID_ARG; }
+        if (L > max_tokens) { *why = "context length exceeds max_pages_per_seq * page_size"; return PKV_ERR_CAPACITY; }
+        max_len = std::max(max_len, L);
+        sum_len += L;
+    }
+    bool split;
+    if (r.policy == PKV_POLICY_NO_SPLIT) split = false;
+    else if (r.policy == PKV_POLICY_SPLIT) split = true;
+    else split = batch > 0 && (int64_t)batch * r.hkv < r.num_cus && max_len > r.chunk;
+
+    int64_t n_items = 0;
+    int n_split_rows = 0, n_merge = 0;
+    part_off[0] = 0;
+    for (int b = 0; b < batch; ++b) {
+        const int64_t L = ctx_lens[b];
+        const int32_t nc = L == 0 ? 0 : (split ? (int32_t)((L + r.chunk - 1) / r.chunk) : 1);
+        n_chunks[b] = nc;
+        part_off[b + 1] = part_off[b] + (nc > 1 ? nc : 0);
+        n_items += (int64_t)nc * r.hkv;
+        if (nc > 1) ++n_split_rows;
+        if (nc != 1) merge_rows[n_merge++] = b;
+    }
+    if (n_items > items_cap) { *why = "queue exceeds max_items"; return PKV_ERR_CAPACITY; }
+
+    int64_t k = 0;
+    for (int b = 0; b < batch; ++b) {
+        const int64_t L = ctx_lens[b];
+        for (int h = 0; h < r.hkv; ++h) {
+            for (int c = 0; c < n_chunks[b]; ++c) {
+                Item it;
+                it.seq = (uint32_t)b;
+                it.kv_head = (uint16_t)h;
+                it.chunk = (uint16_t)c;
+                it.tok_begin = split ? (uint32_t)((int64_t)c * r.chunk) : 0u;
+                it.tok_end = split ? (uint32_t)std::min<int64_t>(L, (int64_t)(c + 1) * r.chunk) : (uint32_t)L;
+                items[k++] = it;
+            }
+        }
+    }
+    if (r.order == PKV_ORDER_LPT) {
+        std::stable_sort(items, items + n_items, [](const Item& a, const Item& b) {
+            return (a.tok_end - a.tok_begin) > (b.tok_end - b.tok_begin);
+        });
+    }
+    memset(qh, 0, sizeof(*qh));
+    qh->n_items = (int32_t)n_items;
+    qh->n_merge_rows = n_merge;
+    qh->split = split ? 1 : 0;
+    qh->chunk_tokens = r.chunk;
+    qh->batch = batch;
+    if (info) {
+        memset(info, 0, sizeof(*info));
+        info->n_items = (int32_t)n_items;
+        info->split = split ? 1 : 0;
+        info->chunk_tokens = r.chunk;
+        info->n_split_rows = n_split_rows;
+        info->n_merge_rows = n_merge;
+        info->n_partial_slots = part_off[batch] * r.hkv;
+        info->launches_per_step = 1 + (n_merge > 0 ? 1 : 0);
+        info->kv_bytes = (uint64_t)sum_len * r.hkv * r.d * 2ull * 2ull;
+        info->partial_bytes = (uint64_t)info->n_partial_slots * r.g * (r.d + 1) * 4ull * 2ull;
+    }
+    return PKV_OK;
+}
+
+}  // namespace pkv

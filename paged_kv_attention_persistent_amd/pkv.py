@@ -1,0 +1,317 @@
+"""ctypes binding of libpkv (include/pkv.h), same entry-point names.
+
+Argument marshalling only: every step of decode attention runs in the HIP
+kernels of libpkv.so.  Torch tensors are passed as device pointers
+(``data_ptr()``) and torch streams / events as their raw HIP handles.  If the
+library is missing, ``lib()`` raises; there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpkv.so")
+
+PKV_OK = 0
+PKV_ERR_INVALID_ARG = -1
+PKV_ERR_UNSUPPORTED = -2
+PKV_ERR_CAPACITY = -3
+PKV_ERR_HIP = -4
+PKV_ERR_STATE = -5
+PKV_ERR_DEVICE_FAULT = -6
+PKV_ERR_TIMEOUT = -7
+
+PKV_POLICY_AUTO, PKV_POLICY_NO_SPLIT, PKV_POLICY_SPLIT = 0, 1, 2
+PKV_ORDER_CANONICAL, PKV_ORDER_LPT = 0, 1
+PKV_DEVERR_NONE, PKV_DEVERR_PAGE_OOB, PKV_DEVERR_BAD_ITEM = 0, 1, 2
+
+ITEM_DTYPE = np.dtype([("seq", "<u4"), ("kv_head", "<u2"), ("chunk", "<u2"),
+                       ("tok_begin", "<u4"), ("tok_end", "<u4")])
+
+
+class pkv_config(C.Structure):
+    _fields_ = [("struct_size", C.c_uint32), ("num_q_heads", C.c_int32),
+                ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("page_size", C.c_int32), ("num_pages", C.c_int32),
+                ("max_batch", C.c_int32), ("max_pages_per_seq", C.c_int32),
+                ("scale", C.c_float), ("policy", C.c_int32), ("order", C.c_int32),
+                ("kv_chunk_tokens", C.c_int32), ("num_cus", C.c_int32),
+                ("max_items", C.c_int32), ("wg_per_cu", C.c_int32),
+                ("reserved", C.c_int32 * 9)]
+
+
+class pkv_tensors(C.Structure):
+    _fields_ = [("q", C.c_void_p), ("k_pool", C.c_void_p), ("v_pool", C.c_void_p),
+                ("block_table", C.c_void_p), ("ctx_lens", C.c_void_p),
+                ("out", C.c_void_p), ("lse", C.c_void_p), ("batch", C.c_int32),
+                ("block_table_stride", C.c_int32)]
+
+
+class pkv_queue_info(C.Structure):
+    _fields_ = [("n_items", C.c_int32), ("split", C.c_int32), ("chunk_tokens", C.c_int32),
+                ("n_split_rows", C.c_int32), ("n_merge_rows", C.c_int32),
+                ("n_partial_slots", C.c_int32), ("launches_per_step", C.c_int32),
+                ("reserved", C.c_int32), ("kv_bytes", C.c_uint64),
+                ("partial_bytes", C.c_uint64)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+
+
+class pkv_runtime_info(C.Structure):
+    _fields_ = [("error_code", C.c_uint32), ("error_detail", C.c_uint32),
+                ("queue_head", C.c_uint32), ("n_items", C.c_uint32),
+                ("items_done", C.c_uint32), ("decode_calls", C.c_uint32),
+                ("grid", C.c_int32), ("num_cus", C.c_int32)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class pkv_layout(C.Structure):
+    _fields_ = [("ctrl_off", C.c_uint64), ("queue_off", C.c_uint64),
+                ("n_chunks_off", C.c_uint64), ("part_off_off", C.c_uint64),
+                ("merge_rows_off", C.c_uint64), ("items_off", C.c_uint64),
+                ("partial_o_off", C.c_uint64), ("partial_lse_off", C.c_uint64),
+                ("total_bytes", C.c_uint64), ("max_items", C.c_int32),
+                ("reserved", C.c_int32)]
+
+
+# name -> (restype, argtypes); the exported C ABI, one entry per declaration in pkv.h
+SIGNATURES = {
+    "pkv_workspace_size": (C.c_int32, [C.POINTER(pkv_config), C.POINTER(C.c_size_t)]),
+    "pkv_workspace_layout": (C.c_int32, [C.POINTER(pkv_config), C.POINTER(pkv_layout)]),
+    "pkv_create": (C.c_int32, [C.POINTER(pkv_config), C.c_void_p, C.c_size_t, C.c_void_p,
+                               C.POINTER(C.c_void_p)]),
+    "pkv_build_queue": (C.c_int32, [C.c_void_p, C.POINTER(C.c_int32), C.c_int32,
+                                    C.POINTER(pkv_queue_info)]),
+    "pkv_build_queue_device": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p]),
+    "pkv_decode": (C.c_int32, [C.c_void_p, C.POINTER(pkv_tensors), C.c_void_p]),
+    "pkv_set_decode_events": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p]),
+    "pkv_query": (C.c_int32, [C.c_void_p, C.POINTER(pkv_runtime_info)]),
+    "pkv_clear_error": (C.c_int32, [C.c_void_p]),
+    "pkv_destroy": (C.c_int32, [C.c_void_p]),
+    "pkv_status_string": (C.c_char_p, [C.c_int32]),
+    "pkv_last_error": (C.c_char_p, [C.c_void_p]),
+    "pkv_plan_queue": (C.c_int32, [C.POINTER(pkv_config), C.POINTER(C.c_int32), C.c_int32,
+                                   C.c_void_p, C.c_int32, C.POINTER(C.c_int32),
+                                   C.POINTER(C.c_int32), C.POINTER(C.c_int32),
+                                   C.POINTER(pkv_queue_info)]),
+    "pkv_debug_gather": (C.c_int32, [C.c_void_p, C.POINTER(pkv_tensors), C.c_int32,
+                                     C.c_void_p, C.c_void_p, C.c_void_p]),
+}
+
+_LIB = None
+
+
+def lib() -> C.CDLL:
+    """Load libpkv.so (built in-tree by ``build.py``); raise if it is missing."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m paged_kv_attention_persistent_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str = ""):
+        self.status = status
+        msg = lib().pkv_status_string(status).decode()
+        super().__init__(f"{where}: {msg} ({status}){': ' + detail if detail else ''}")
+
+
+def _check(status: int, where: str, handle=None) -> None:
+    if status != PKV_OK:
+        detail = lib().pkv_last_error(handle).decode() if handle else ""
+        raise PkvError(status, where, detail)
+
+
+def make_config(num_q_heads, num_kv_heads, head_dim, num_pages, max_batch, max_pages_per_seq,
+                page_size=16, scale=0.0, policy=PKV_POLICY_AUTO, order=PKV_ORDER_CANONICAL,
+                kv_chunk_tokens=0, num_cus=0, max_items=0, wg_per_cu=0) -> pkv_config:
+    cfg = pkv_config()
+    cfg.struct_size = C.sizeof(pkv_config)
+    cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim = num_q_heads, num_kv_heads, head_dim
+    cfg.page_size, cfg.num_pages = page_size, num_pages
+    cfg.max_batch, cfg.max_pages_per_seq = max_batch, max_pages_per_seq
+    cfg.scale, cfg.policy, cfg.order = scale, policy, order
+    cfg.kv_chunk_tokens, cfg.num_cus, cfg.max_items, cfg.wg_per_cu = \
+        kv_chunk_tokens, num_cus, max_items, wg_per_cu
+    return cfg
+
+
+def pkv_workspace_size(cfg: pkv_config) -> int:
+    n = C.c_size_t(0)
+    _check(lib().pkv_workspace_size(C.byref(cfg), C.byref(n)), "pkv_workspace_size")
+    return int(n.value)
+
+
+def pkv_workspace_layout(cfg: pkv_config) -> pkv_layout:
+    lay = pkv_layout()
+    _check(lib().pkv_workspace_layout(C.byref(cfg), C.byref(lay)), "pkv_workspace_layout")
+    return lay
+
+
+def _stream_ptr(stream) -> int:
+    if stream is None:
+        return 0
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def pkv_create(cfg: pkv_config, workspace, stream=None) -> int:
+    """workspace: a uint8 device tensor of at least pkv_workspace_size bytes."""
+    h = C.c_void_p(0)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().pkv_create(C.byref(cfg), C.c_void_p(workspace.data_ptr()), nbytes,
+                            C.c_void_p(_stream_ptr(stream)), C.byref(h)), "pkv_create")
+    return h.value
+
+
+def pkv_build_queue(handle: int, ctx_lens) -> pkv_queue_info:
+    arr = np.ascontiguousarray(np.asarray(ctx_lens, dtype=np.int32))
+    info = pkv_queue_info()
+    ptr = arr.ctypes.data_as(C.POINTER(C.c_int32))
+    _check(lib().pkv_build_queue(C.c_void_p(handle), ptr, int(arr.shape[0]), C.byref(info)),
+           "pkv_build_queue", C.c_void_p(handle))
+    return info
+
+
+def pkv_build_queue_device(handle: int, ctx_lens_dev, stream=None) -> None:
+    _check(lib().pkv_build_queue_device(C.c_void_p(handle), C.c_void_p(ctx_lens_dev.data_ptr()),
+                                        int(ctx_lens_dev.numel()), C.c_void_p(_stream_ptr(stream))),
+           "pkv_build_queue_device", C.c_void_p(handle))
+
+
+def make_tensors(q, k_pool, v_pool, block_table, ctx_lens, out, lse, batch=None,
+                 block_table_stride=0) -> pkv_tensors:
+    t = pkv_tensors()
+    t.q, t.k_pool, t.v_pool = q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr()
+    t.block_table = block_table.data_ptr()
+    t.ctx_lens = ctx_lens.data_ptr() if ctx_lens is not None else None
+    t.out, t.lse = out.data_ptr(), lse.data_ptr()
+    t.batch = int(q.shape[0]) if batch is None else int(batch)
+    t.block_table_stride = int(block_table_stride or block_table.shape[1])
+    return t
+
+
+def pkv_decode(handle: int, tensors: pkv_tensors, stream=None) -> None:
+    _check(lib().pkv_decode(C.c_void_p(handle), C.byref(tensors), C.c_void_p(_stream_ptr(stream))),
+           "pkv_decode", C.c_void_p(handle))
+
+
+def pkv_set_decode_events(handle: int, before=None, after=None) -> None:
+    b = int(before.cuda_event) if before is not None else None
+    a = int(after.cuda_event) if after is not None else None
+    _check(lib().pkv_set_decode_events(C.c_void_p(handle), C.c_void_p(b), C.c_void_p(a)),
+           "pkv_set_decode_events", C.c_void_p(handle))
+
+
+def pkv_query(handle: int, raise_on_fault: bool = True) -> dict:
+    info = pkv_runtime_info()
+    st = lib().pkv_query(C.c_void_p(handle), C.byref(info))
+    if st != PKV_ERR_DEVICE_FAULT or raise_on_fault:
+        _check(st, "pkv_query", C.c_void_p(handle))
+    d = info.as_dict()
+    d["status"] = st
+    return d
+
+
+def pkv_clear_error(handle: int) -> None:
+    _check(lib().pkv_clear_error(C.c_void_p(handle)), "pkv_clear_error", C.c_void_p(handle))
+
+
+def pkv_destroy(handle: int) -> None:
+    _check(lib().pkv_destroy(C.c_void_p(handle)), "pkv_destroy")
+
+
+def pkv_status_string(status: int) -> str:
+    return lib().pkv_status_string(status).decode()
+
+
+def pkv_plan_queue(cfg: pkv_config, ctx_lens, items_cap: int | None = None):
+    """Host-only planning: (items ITEM_DTYPE array, n_chunks, part_off, merge_rows, info)."""
+    arr = np.ascontiguousarray(np.asarray(ctx_lens, dtype=np.int32))
+    bsz = int(arr.shape[0])
+    if items_cap is None:
+        items_cap = pkv_workspace_layout(cfg).max_items
+    items = np.zeros(max(items_cap, 1), dtype=ITEM_DTYPE)
+    n_chunks = np.zeros(max(bsz, 1), dtype=np.int32)
+    part_off = np.zeros(bsz + 1, dtype=np.int32)
+    merge_rows = np.zeros(max(bsz, 1), dtype=np.int32)
+    info = pkv_queue_info()
+    P32 = C.POINTER(C.c_int32)
+    st = lib().pkv_plan_queue(C.byref(cfg), arr.ctypes.data_as(P32), bsz,
+                              items.ctypes.data_as(C.c_void_p), int(items_cap),
+                              n_chunks.ctypes.data_as(P32), part_off.ctypes.data_as(P32),
+                              merge_rows.ctypes.data_as(P32), C.byref(info))
+    _check(st, "pkv_plan_queue")
+    return (items[:info.n_items].copy(), n_chunks[:bsz].copy(), part_off,
+            merge_rows[:info.n_merge_rows].copy(), info)
+
+
+def pkv_debug_gather(handle: int, tensors: pkv_tensors, item_index: int, k_out, v_out,
+                     stream=None) -> None:
+    _check(lib().pkv_debug_gather(C.c_void_p(handle), C.byref(tensors), int(item_index),
+                                  C.c_void_p(k_out.data_ptr()), C.c_void_p(v_out.data_ptr()),
+                                  C.c_void_p(_stream_ptr(stream))),
+           "pkv_debug_gather", C.c_void_p(handle))
+
+
+class PagedDecoder:
+    """A handle plus its workspace tensor, for one model shape.
+
+    Owns nothing but the handle; the workspace is an ordinary torch tensor
+    allocated here and kept alive with the handle.
+    """
+
+    def __init__(self, cfg: pkv_config, device="cuda", stream=None):
+        import torch
+        self.cfg = cfg
+        self.layout = pkv_workspace_layout(cfg)
+        self.workspace = torch.empty(self.layout.total_bytes, dtype=torch.uint8, device=device)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(device)
+        self.handle = pkv_create(cfg, self.workspace, self.stream)
+        self.info = None
+
+    def build_queue(self, ctx_lens) -> pkv_queue_info:
+        self.info = pkv_build_queue(self.handle, ctx_lens)
+        return self.info
+
+    def build_queue_device(self, ctx_lens_dev) -> None:
+        pkv_build_queue_device(self.handle, ctx_lens_dev, self.stream)
+
+    def decode(self, q, k_pool, v_pool, block_table, ctx_lens, out, lse, stream=None):
+        t = make_tensors(q, k_pool, v_pool, block_table, ctx_lens, out, lse)
+        pkv_decode(self.handle, t, stream if stream is not None else self.stream)
+
+    def query(self, raise_on_fault=True) -> dict:
+        return pkv_query(self.handle, raise_on_fault)
+
+    def region(self, name: str, nbytes: int):
+        """A uint8 view of a workspace region (for inspection in tests)."""
+        off = getattr(self.layout, name + "_off")
+        return self.workspace[off:off + nbytes]
+
+    def close(self):
+        if self.handle:
+            pkv_destroy(self.handle)
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

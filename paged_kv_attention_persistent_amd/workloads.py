@@ -180,6 +180,17 @@ class Workload:
         return _to_bf16(bits).view(len(pages), self.num_kv_heads, self.page_size,
                                    self.head_dim)
 
+    def pool_slabs(self, which: str, pages, kv_head: int) -> torch.Tensor:
+        """Regenerate on the CPU only the (page, kv_head) slabs of the given
+        pages, shaped [len(pages)][P][D] (unpoisoned values)."""
+        slab = self.page_size * self.head_dim
+        per_page = self.num_kv_heads * slab
+        pages = torch.as_tensor(np.asarray(pages, dtype=np.int64))
+        idx = (pages[:, None] * per_page + kv_head * slab
+               + torch.arange(slab, dtype=torch.int64)[None, :])
+        bits = normal_bf16_bits(self.seed, self.name + "/" + which, idx.reshape(-1))
+        return _to_bf16(bits).view(len(pages), self.page_size, self.head_dim)
+
     def poison(self, pool: torch.Tensor) -> None:
         """Write NaN into unreferenced pages and past-the-end slots."""
         used = np.zeros(self.num_pages, dtype=bool)

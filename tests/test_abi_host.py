@@ -1,0 +1,155 @@
+"""CPU tests of the C-ABI library: it loads, exports every entry point that
+include/pkv.h declares, and its host-side logic (config checks, workspace
+layout, the adaptive policy and the compact queue) matches the oracle's
+queue byte for byte.  No kernel is launched here."""
+
+import ctypes as C
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from oracle import work_queue as wq
+from paged_kv_attention_persistent_amd import pkv, workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"PKV_API\s+[\w\s\*]+?\b(pkv_\w+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = pkv.lib()
+    names = declared_symbols()
+    assert len(names) >= 14, names
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in pkv.h but not exported"
+    assert set(names) == set(pkv.SIGNATURES), "binding and header disagree"
+    out = subprocess.run(["nm", "-D", "--defined-only", pkv.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r" T (pkv_\w+)", out))
+    assert exported == set(names), exported ^ set(names)
+
+
+def test_struct_sizes_match_the_header():
+    src = r"""
+#include <stdio.h>
+#include "pkv.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu\n", sizeof(pkv_config), sizeof(pkv_tensors),
+         sizeof(pkv_queue_info), sizeof(pkv_runtime_info), sizeof(pkv_layout));
+  return 0; }
+"""
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "s.c")
+        open(c, "w").write(src)
+        exe = os.path.join(d, "s")
+        subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        sizes = [int(x) for x in subprocess.run([exe], capture_output=True, text=True).stdout.split()]
+    assert sizes == [C.sizeof(pkv.pkv_config), C.sizeof(pkv.pkv_tensors),
+                     C.sizeof(pkv.pkv_queue_info), C.sizeof(pkv.pkv_runtime_info),
+                     C.sizeof(pkv.pkv_layout)]
+
+
+def test_status_strings():
+    assert pkv.pkv_status_string(0) == "ok"
+    assert pkv.pkv_status_string(pkv.PKV_ERR_DEVICE_FAULT) == "device fault"
+    assert pkv.pkv_status_string(-99) == "unknown status"
+
+
+def cfg_for(wl, num_cus=256, **kw):
+    return pkv.make_config(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages,
+                           max(wl.batch, 1), wl.max_pages_per_seq, num_cus=num_cus, **kw)
+
+
+def compare_with_oracle(cfg, lens, hkv, num_cus, chunk, policy, order):
+    items, n_chunks, part_off, merge_rows, info = pkv.pkv_plan_queue(cfg, lens)
+    ref = wq.build_queue(lens, hkv, num_cus, chunk, policy, order)
+    assert items.tobytes() == ref["items"].tobytes()
+    assert np.array_equal(n_chunks[:len(lens)], ref["n_chunks"])
+    assert np.array_equal(part_off, ref["part_off"])
+    assert np.array_equal(merge_rows, ref["merge_rows"])
+    assert bool(info.split) == ref["split"]
+    assert info.n_items == len(ref["items"])
+    assert info.launches_per_step == 1 + (len(ref["merge_rows"]) > 0)
+    return info
+
+
+@pytest.mark.parametrize("name", ["tiny", "long", "mixed", "short"])
+@pytest.mark.parametrize("order", [pkv.PKV_ORDER_CANONICAL, pkv.PKV_ORDER_LPT])
+def test_host_queue_matches_oracle_on_workloads(name, order):
+    for seed in (workloads.MEASURE_SEED, workloads.CALIBRATION_SEED):
+        wl = workloads.CONFIGS[name](seed)
+        cfg = cfg_for(wl, order=order)
+        info = compare_with_oracle(cfg, wl.ctx_lens, wl.num_kv_heads, 256, 4096,
+                                   wq.POLICY_AUTO, order)
+        assert info.kv_bytes == wl.kv_bytes
+
+
+def test_host_queue_matches_oracle_random():
+    rng = np.random.default_rng(7)
+    for trial in range(300):
+        bsz = int(rng.integers(0, 20))
+        hkv = int(rng.choice([1, 2, 8]))
+        chunk = int(rng.choice([16, 64, 4096]))
+        maxp = int(rng.integers(1, 40))
+        lens = rng.integers(0, maxp * 16 + 1, size=bsz)
+        if bsz and rng.random() < 0.3:
+            lens[rng.integers(0, bsz)] = 0
+        policy = int(rng.integers(0, 3))
+        order = int(rng.integers(0, 2))
+        cus = int(rng.choice([1, 8, 256]))
+        cfg = pkv.make_config(hkv * 4, hkv, 128, 1000, max(bsz, 1), maxp, policy=policy,
+                              order=order, kv_chunk_tokens=chunk, num_cus=cus)
+        compare_with_oracle(cfg, lens.tolist(), hkv, cus, chunk, policy, order)
+
+
+def test_config_validation():
+    good = pkv.make_config(32, 8, 128, 100, 4, 10, num_cus=256)
+    assert pkv.pkv_workspace_size(good) > 0
+    bad = [dict(num_q_heads=30), dict(head_dim=96), dict(page_size=32), dict(kv_chunk_tokens=100),
+           dict(num_pages=0), dict(wg_per_cu=9), dict(policy=7), dict(num_q_heads=64)]
+    base = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, num_pages=100, max_batch=4,
+                max_pages_per_seq=10, num_cus=256)
+    for b in bad:
+        kw = dict(base)
+        kw.update(b)
+        with pytest.raises(pkv.PkvError):
+            pkv.pkv_workspace_size(pkv.make_config(**kw))
+    c = pkv.make_config(**base)
+    c.struct_size = 4
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_workspace_size(c)
+
+
+def test_plan_rejects_bad_lengths_and_capacity():
+    cfg = pkv.make_config(4, 1, 64, 100, 4, 4, num_cus=256)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_plan_queue(cfg, [10, 65])              # 65 > 4 pages * 16
+    assert e.value.status == pkv.PKV_ERR_CAPACITY
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_plan_queue(cfg, [10, -1])
+    assert e.value.status == pkv.PKV_ERR_INVALID_ARG
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_plan_queue(cfg, [1] * 5)                # batch > max_batch
+    assert e.value.status == pkv.PKV_ERR_CAPACITY
+    small = pkv.make_config(4, 1, 64, 100, 4, 4, num_cus=256, max_items=2)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_plan_queue(small, [1, 1, 1])
+    assert e.value.status == pkv.PKV_ERR_CAPACITY
+
+
+def test_layout_regions_are_ordered_and_aligned():
+    cfg = pkv.make_config(32, 8, 128, 8192, 1, 8192, num_cus=256)
+    lay = pkv.pkv_workspace_layout(cfg)
+    offs = [lay.ctrl_off, lay.queue_off, lay.n_chunks_off, lay.part_off_off, lay.merge_rows_off,
+            lay.items_off, lay.partial_o_off, lay.partial_lse_off, lay.total_bytes]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert lay.max_items == 8 * 32
+    assert lay.partial_lse_off - lay.partial_o_off >= lay.max_items * 4 * 128 * 4

@@ -1,0 +1,333 @@
+"""GPU parity of the HIP path against the float64 oracle, through the C ABI.
+
+Tolerance (stated for bf16 inputs with fp32 accumulation): every output
+element within max-abs 2e-2 and mean-abs 2e-3 of the oracle, compared in
+float64 after widening the kernel's bf16 output; the same bounds apply to the
+fp32 LSE.  Queue bytes and gathered K/V bits must match exactly.
+
+Small cases compare every output; full-size workloads compare sampled
+(sequence, KV head) units, each recomputed by the oracle from pages
+regenerated on the CPU by the seeded generator.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import paged_attention as pa
+from oracle import work_queue as wq
+from paged_kv_attention_persistent_amd import pkv, workloads
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+MEAN_ABS = 2e-3
+
+
+def say(*a):
+    print("[gpu-parity]", *a, flush=True)
+
+
+def cfg_for(wl, **kw):
+    return pkv.make_config(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages,
+                           max(wl.batch, 1), wl.max_pages_per_seq, scale=wl.scale, **kw)
+
+
+class Run:
+    """Inputs of one workload on the GPU plus one decode through the C ABI."""
+
+    def __init__(self, wl, poison=True, **cfgkw):
+        self.wl = wl
+        dev = "cuda"
+        self.q = wl.q(dev)
+        self.k = wl.pool("k", dev, poison)
+        self.v = wl.pool("v", dev, poison)
+        self.bt = wl.block_table_t(dev)
+        self.lens = wl.ctx_lens_t(dev)
+        self.out = torch.full((wl.batch, wl.num_q_heads, wl.head_dim), float("nan"),
+                              dtype=torch.bfloat16, device=dev)
+        self.lse = torch.full((wl.batch, wl.num_q_heads), float("nan"), dtype=torch.float32,
+                              device=dev)
+        self.cfg = cfg_for(wl, **cfgkw)
+        self.dec = pkv.PagedDecoder(self.cfg)
+        self.info = None
+
+    def tensors(self):
+        return pkv.make_tensors(self.q, self.k, self.v, self.bt, self.lens, self.out, self.lse)
+
+    def decode(self, device_queue=False):
+        if device_queue:
+            self.dec.build_queue_device(self.lens)
+        else:
+            self.info = self.dec.build_queue(self.wl.ctx_lens)
+        pkv.pkv_decode(self.dec.handle, self.tensors(), self.dec.stream)
+        torch.cuda.synchronize()
+        st = self.dec.query()
+        assert st["error_code"] == 0
+        return self.out.float().cpu().numpy().astype(np.float64), self.lse.cpu().numpy().astype(np.float64)
+
+    def queue_bytes(self):
+        torch.cuda.synchronize()
+        lay = self.dec.layout
+        ws = self.dec.workspace
+        n = int(ws[lay.queue_off:lay.queue_off + 4].cpu().view(torch.int32)[0])
+        items = ws[lay.items_off:lay.items_off + 16 * n].cpu().numpy().tobytes()
+        B = self.wl.batch
+        nch = ws[lay.n_chunks_off:lay.n_chunks_off + 4 * B].cpu().view(torch.int32).numpy()
+        po = ws[lay.part_off_off:lay.part_off_off + 4 * (B + 1)].cpu().view(torch.int32).numpy()
+        hdr = ws[lay.queue_off:lay.queue_off + 20].cpu().view(torch.int32).numpy()
+        nm = int(hdr[1])
+        mr = ws[lay.merge_rows_off:lay.merge_rows_off + 4 * nm].cpu().view(torch.int32).numpy()
+        return {"items": items, "n_chunks": nch, "part_off": po, "merge_rows": mr, "hdr": hdr}
+
+    def close(self):
+        self.dec.close()
+
+
+def oracle_full(wl, poison=True):
+    q = workloads.bits_u16(wl.q("cpu"))
+    k = workloads.bits_u16(wl.pool("k", "cpu", poison))
+    v = workloads.bits_u16(wl.pool("v", "cpu", poison))
+    return pa.decode_attention(q, k, v, wl.block_table, wl.ctx_lens, wl.scale, wl.page_size)
+
+
+def oracle_unit(wl, q_bits, b, hk):
+    """Oracle for one (sequence, KV head) from regenerated slabs."""
+    L = int(wl.ctx_lens[b])
+    G = wl.num_q_heads // wl.num_kv_heads
+    if L == 0:
+        return np.zeros((G, wl.head_dim)), np.full(G, -np.inf)
+    npg = -(-L // wl.page_size)
+    pages = wl.block_table[b, :npg]
+    ks = workloads.bits_u16(wl.pool_slabs("k", pages, hk))[:, None]     # [n][1][P][D]
+    vs = workloads.bits_u16(wl.pool_slabs("v", pages, hk))[:, None]
+    qg = q_bits[b:b + 1, hk * G:(hk + 1) * G]                           # [1][G][D]
+    bt = np.arange(npg)[None]
+    return pa.range_state(qg, ks, vs, bt, 0, 0, 0, L, wl.scale, wl.page_size)
+
+
+def check(o, l, ro, rl, where):
+    err = np.abs(o - ro)
+    assert np.all(np.isfinite(o)), f"{where}: non-finite output"
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(l), fin), f"{where}: LSE finiteness differs"
+    lerr = np.abs(l[fin] - rl[fin]) if fin.any() else np.zeros(1)
+    say(f"{where}: max_abs={err.max():.3e} mean_abs={err.mean():.3e} "
+        f"rel_l2={np.linalg.norm(o - ro) / max(np.linalg.norm(ro), 1e-30):.3e} lse_max={lerr.max():.3e}")
+    assert err.max() <= MAX_ABS, where
+    assert err.mean() <= MEAN_ABS, where
+    assert lerr.max() <= MAX_ABS, where
+
+
+# ----------------------------------------------------------- small cases ----
+
+SMALL = [
+    # name, lens, Hq, Hkv, D, policy, chunk
+    ("ragged_d128_nosplit", [1, 15, 16, 17, 100, 333, 0, 1024], 8, 2, 128, pkv.PKV_POLICY_NO_SPLIT, 0),
+    ("ragged_d128_split64", [1, 15, 16, 17, 100, 333, 0, 1024], 8, 2, 128, pkv.PKV_POLICY_SPLIT, 64),
+    ("ragged_d64_g8_split", [700, 5, 0, 2049], 16, 2, 64, pkv.PKV_POLICY_SPLIT, 256),
+    ("g1_d128", [64, 257, 31], 4, 4, 128, pkv.PKV_POLICY_AUTO, 0),
+    ("g2_d64", [1000, 3], 4, 2, 64, pkv.PKV_POLICY_SPLIT, 128),
+    ("long_tail_many_windows", [9000, 8191], 4, 1, 128, pkv.PKV_POLICY_NO_SPLIT, 0),
+    ("all_empty", [0, 0, 0], 8, 2, 128, pkv.PKV_POLICY_AUTO, 0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_cases_full_compare(case):
+    name, lens, hq, hkv, d, policy, chunk = case
+    say("case", name)
+    wl = workloads.custom(name, lens, hq, hkv, d, spare_pages=5)
+    run = Run(wl, policy=policy, kv_chunk_tokens=chunk)
+    o, l = run.decode()
+    ro, rl = oracle_full(wl)
+    check(o, l, ro, rl, name)
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(o[b] == 0) and np.all(np.isneginf(l[b]))
+    run.close()
+
+
+def test_tiny_workload_and_repeat_calls():
+    wl = workloads.tiny()
+    run = Run(wl)
+    ro, rl = oracle_full(wl)
+    for i in range(3):                                   # head counter re-arms each launch
+        o, l = run.decode()
+        check(o, l, ro, rl, f"tiny call {i}")
+    st = run.dec.query()
+    assert st["decode_calls"] == 3 and st["queue_head"] == 0 and st["items_done"] == 3
+    run.close()
+
+
+# ------------------------------------------------------ full-size cases ----
+
+FULL = {"long": [(0, 0), (0, 5)], "mixed": [(b, (3 * b) % 8) for b in range(8)],
+        "short": [(0, 0), (17, 3), (63, 7)]}
+
+
+@pytest.mark.parametrize("name", ["long", "mixed", "short"])
+def test_full_size_sampled_units(name):
+    say("full", name)
+    wl = workloads.CONFIGS[name]()
+    run = Run(wl, poison=True)
+    o, l = run.decode()
+    info = run.info
+    ref = wq.build_queue(wl.ctx_lens, wl.num_kv_heads, run.dec.query()["num_cus"], 4096)
+    assert info.n_items == len(ref["items"]) and bool(info.split) == ref["split"]
+    qb = workloads.bits_u16(run.q)
+    G = wl.num_q_heads // wl.num_kv_heads
+    for b, hk in FULL[name]:
+        ro, rl = oracle_unit(wl, qb, b, hk)
+        check(o[b, hk * G:(hk + 1) * G], l[b, hk * G:(hk + 1) * G], ro, rl, f"{name} b={b} hk={hk}")
+    # every output finite: no stray read of a poisoned slot anywhere
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+    run.close()
+
+
+def test_split_equals_unsplit_on_gpu_partials():
+    """Merge identity on the kernel's own partials: forced split vs no split,
+    and each partial state vs the oracle's state for its range."""
+    wl = workloads.custom("merge_id", [20000, 5000, 3], 8, 2, 128, spare_pages=2)
+    a = Run(wl, policy=pkv.PKV_POLICY_SPLIT, kv_chunk_tokens=1024)
+    oa, la = a.decode()
+    b = Run(wl, policy=pkv.PKV_POLICY_NO_SPLIT)
+    ob, lb = b.decode()
+    check(oa, la, ob, lb, "split vs unsplit")
+    # partial states in the workspace vs oracle range_state
+    lay = a.dec.layout
+    ws = a.dec.workspace
+    items, n_chunks, part_off, _, info = pkv.pkv_plan_queue(a.cfg, wl.ctx_lens)
+    G = 4
+    po = ws[lay.partial_o_off:lay.partial_o_off + 4 * lay.max_items * G * 128].cpu().view(torch.float32)
+    pl = ws[lay.partial_lse_off:lay.partial_lse_off + 4 * lay.max_items * G].cpu().view(torch.float32)
+    po = po.numpy().reshape(lay.max_items, G, 128)
+    pl = pl.numpy().reshape(lay.max_items, G)
+    q = workloads.bits_u16(wl.q("cpu"))
+    k = workloads.bits_u16(wl.pool("k", "cpu"))
+    v = workloads.bits_u16(wl.pool("v", "cpu"))
+    checked = 0
+    for it in items[::7]:
+        if n_chunks[int(it["seq"])] <= 1:
+            continue
+        s = wq.partial_slot(it, part_off, 2)
+        ro, rl = pa.range_state(q, k, v, wl.block_table, int(it["seq"]), int(it["kv_head"]),
+                                int(it["tok_begin"]), int(it["tok_end"]), wl.scale, 16)
+        assert np.abs(po[s] - ro).max() <= MAX_ABS and np.abs(pl[s] - rl).max() <= MAX_ABS
+        checked += 1
+    assert checked >= 3
+    a.close()
+    b.close()
+
+
+# --------------------------------------------------- queue and gather ----
+
+@pytest.mark.parametrize("name", ["tiny", "long", "mixed", "short"])
+def test_queue_bytes_on_device_match_oracle(name):
+    wl = workloads.CONFIGS[name]()
+    run = Run(wl, poison=False)
+    cus = run.dec.query()["num_cus"]
+    ref = wq.build_queue(wl.ctx_lens, wl.num_kv_heads, cus, 4096)
+    for device_queue in (False, True):
+        if device_queue:
+            run.dec.build_queue_device(run.lens)
+        else:
+            run.dec.build_queue(wl.ctx_lens)
+        got = run.queue_bytes()
+        assert got["items"] == ref["items"].tobytes(), f"{name} device={device_queue}"
+        assert np.array_equal(got["n_chunks"], ref["n_chunks"])
+        assert np.array_equal(got["part_off"], ref["part_off"])
+        assert np.array_equal(got["merge_rows"], ref["merge_rows"])
+        assert list(got["hdr"]) == [len(ref["items"]), len(ref["merge_rows"]), int(ref["split"]),
+                                    4096, wl.batch]
+    run.close()
+
+
+def test_device_queue_decode_matches():
+    wl = workloads.custom("devq", [5000, 0, 77, 12000], 8, 2, 128, spare_pages=3)
+    run = Run(wl, policy=pkv.PKV_POLICY_AUTO)
+    o, l = run.decode(device_queue=True)
+    ro, rl = oracle_full(wl)
+    check(o, l, ro, rl, "device-built queue")
+    run.close()
+
+
+@pytest.mark.parametrize("name", ["tiny", "mixed"])
+def test_gather_bits_match_oracle(name):
+    wl = workloads.CONFIGS[name]() if name != "mixed" else workloads.custom(
+        "gather_mixed", [100, 4097, 33, 5000], 8, 2, 128, spare_pages=4)
+    run = Run(wl, policy=pkv.PKV_POLICY_SPLIT if name == "mixed" else pkv.PKV_POLICY_AUTO,
+              kv_chunk_tokens=1024 if name == "mixed" else 0)
+    run.dec.build_queue(wl.ctx_lens)
+    items, *_ = pkv.pkv_plan_queue(run.cfg, wl.ctx_lens)
+    kp = workloads.bits_u16(wl.pool("k", "cpu"))
+    vp = workloads.bits_u16(wl.pool("v", "cpu"))
+    for i in range(len(items)):
+        it = items[i]
+        n = int(it["tok_end"] - it["tok_begin"])
+        ko = torch.zeros(n, wl.head_dim, dtype=torch.bfloat16, device="cuda")
+        vo = torch.zeros_like(ko)
+        pkv.pkv_debug_gather(run.dec.handle, run.tensors(), i, ko, vo, run.dec.stream)
+        torch.cuda.synchronize()
+        rk = pa.gather_tokens(kp, wl.block_table, int(it["seq"]), int(it["kv_head"]),
+                              int(it["tok_begin"]), int(it["tok_end"]), 16)
+        rv = pa.gather_tokens(vp, wl.block_table, int(it["seq"]), int(it["kv_head"]),
+                              int(it["tok_begin"]), int(it["tok_end"]), 16)
+        assert np.array_equal(workloads.bits_u16(ko), rk), f"K item {i}"
+        assert np.array_equal(workloads.bits_u16(vo), rv), f"V item {i}"
+    run.close()
+
+
+# --------------------------------------------------------- error paths ----
+
+def test_bad_block_table_entry_is_reported_not_read():
+    wl = workloads.custom("badpage", [40, 50], 4, 1, 128, spare_pages=1)
+    run = Run(wl)
+    bt = run.bt.clone()
+    bt[1, 2] = wl.num_pages + 1000                    # outside the pool
+    run.dec.build_queue(wl.ctx_lens)
+    t = pkv.make_tensors(run.q, run.k, run.v, bt, run.lens, run.out, run.lse)
+    pkv.pkv_decode(run.dec.handle, t, run.dec.stream)
+    torch.cuda.synchronize()
+    st = run.dec.query(raise_on_fault=False)
+    assert st["status"] == pkv.PKV_ERR_DEVICE_FAULT
+    assert st["error_code"] == pkv.PKV_DEVERR_PAGE_OOB and st["error_detail"] == wl.num_pages + 1000
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_decode(run.dec.handle, t, run.dec.stream)
+    assert e.value.status == pkv.PKV_ERR_DEVICE_FAULT
+    pkv.pkv_clear_error(run.dec.handle)
+    o, l = run.decode()                                 # good table again
+    ro, rl = oracle_full(wl)
+    check(o, l, ro, rl, "after clear")
+    run.close()
+
+
+def test_argument_errors_enqueue_nothing():
+    wl = workloads.tiny()
+    run = Run(wl)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_decode(run.dec.handle, run.tensors(), run.dec.stream)   # before build
+    assert e.value.status == pkv.PKV_ERR_STATE
+    run.dec.build_queue(wl.ctx_lens)
+    t = run.tensors()
+    t.batch = 2
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_decode(run.dec.handle, t, run.dec.stream)
+    t = run.tensors()
+    t.q = t.q + 2                                      # misaligned
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_decode(run.dec.handle, t, run.dec.stream)
+    assert e.value.status == pkv.PKV_ERR_INVALID_ARG
+    with pytest.raises(pkv.PkvError) as e:
+        run.dec.build_queue([10 ** 6])
+    assert e.value.status == pkv.PKV_ERR_CAPACITY
+    st = run.dec.query()
+    assert st["decode_calls"] == 0
+    run.close()
+
+
+def test_generator_identical_on_cpu_and_gpu():
+    idx = torch.arange(0, 1 << 20, dtype=torch.int64) * 4099 + (1 << 33)
+    a = workloads.normal_bf16_bits(7, "t", idx)
+    b = workloads.normal_bf16_bits(7, "t", idx.cuda()).cpu()
+    assert torch.equal(a, b)
