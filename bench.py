@@ -43,12 +43,14 @@ def parse():
                     help="bounded oracle sample for cpu_baseline (0 disables)")
     ap.add_argument("--order", default="canonical", choices=["canonical", "lpt"])
     ap.add_argument("--wg-per-cu", type=int, default=0)
+    ap.add_argument("--merge", default="fused", choices=["fused", "separate"])
     ap.add_argument("--copies", type=int, default=2)
     ap.add_argument("--no-gate", action="store_true")
     return ap.parse_args()
 
 
-def measure(torch, pkv, workloads, name, steps, warmup, order, wg_per_cu, copies, gate, say):
+def measure(torch, pkv, workloads, name, steps, warmup, order, wg_per_cu, copies, gate, say,
+            merge="fused"):
     wl = workloads.CONFIGS[name]()
     dev = "cuda"
     q = wl.q(dev)
@@ -62,7 +64,8 @@ def measure(torch, pkv, workloads, name, steps, warmup, order, wg_per_cu, copies
     cfg = pkv.make_config(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages, wl.batch,
                           wl.max_pages_per_seq, scale=wl.scale,
                           order=pkv.PKV_ORDER_LPT if order == "lpt" else pkv.PKV_ORDER_CANONICAL,
-                          wg_per_cu=wg_per_cu)
+                          wg_per_cu=wg_per_cu,
+                          merge_mode=pkv.PKV_MERGE_SEPARATE if merge == "separate" else pkv.PKV_MERGE_FUSED)
     stream = torch.cuda.current_stream()
     dec = pkv.PagedDecoder(cfg, stream=stream)
     info = dec.build_queue(wl.ctx_lens)
@@ -184,13 +187,13 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     pkv.lib()
     main_res, wl = measure(torch, pkv, workloads, args.workload, args.steps, args.warmup,
-                           args.order, args.wg_per_cu, args.copies, not args.no_gate, say)
+                           args.order, args.wg_per_cu, args.copies, not args.no_gate, say, args.merge)
     say(f"{args.workload}: {main_res['gbs']:.1f} GB/s per step, decode kernel "
         f"{main_res['decode_gbs']:.1f} GB/s ({main_res['decode_ms_mean'] * 1e3:.1f} us)")
     others = {}
     for name in [x for x in args.others.split(",") if x and x != args.workload]:
         r, _ = measure(torch, pkv, workloads, name, max(args.steps // 2, 10), args.warmup,
-                       args.order, args.wg_per_cu, args.copies, not args.no_gate, say)
+                       args.order, args.wg_per_cu, args.copies, not args.no_gate, say, args.merge)
         others[name] = {k: r[k] for k in ("gbs", "decode_gbs", "ms_per_step", "decode_ms_mean",
                                           "items", "split", "kv_bytes", "launches_per_step")}
         others[name]["pct_of_hbm_peak"] = 100.0 * r["gbs"] / HBM_PEAK_GBS
@@ -218,7 +221,7 @@ def main():
                    "kv_chunk_tokens": 4096, "items": main_res["items"],
                    "launches_per_step": main_res["launches_per_step"],
                    "kv_bytes_per_step": main_res["kv_bytes"], "grid": main_res["grid"],
-                   "order": args.order} if args.workload == "long" else
+                   "order": args.order, "merge": args.merge} if args.workload == "long" else
                   {"workload": args.workload, "items": main_res["items"],
                    "kv_bytes_per_step": main_res["kv_bytes"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,

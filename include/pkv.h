@@ -79,6 +79,12 @@ enum { PKV_POLICY_AUTO = 0, PKV_POLICY_NO_SPLIT = 1, PKV_POLICY_SPLIT = 2 };
  * of the canonical list by item length, longest first. */
 enum { PKV_ORDER_CANONICAL = 0, PKV_ORDER_LPT = 1 };
 
+/* How split rows are merged.  FUSED: inside the decode kernel, the last
+ * workgroup to finish a split (row, KV head) merges its partial states (one
+ * launch per step).  SEPARATE: a second kernel merges every split row (the
+ * two-kernel split + merge scheme).  Both compute the same exact merge. */
+enum { PKV_MERGE_FUSED = 0, PKV_MERGE_SEPARATE = 1 };
+
 /* Device error words (pkv_runtime_info.error_code). */
 enum {
     PKV_DEVERR_NONE = 0,
@@ -102,7 +108,8 @@ typedef struct pkv_config {
     int32_t num_cus;            /* policy input; 0 -> the device's CU count */
     int32_t max_items;          /* queue capacity; 0 -> bound from the shape */
     int32_t wg_per_cu;          /* persistent grid = CUs * wg_per_cu; 0 -> 1 */
-    int32_t reserved[9];        /* must be zero */
+    int32_t merge_mode;         /* PKV_MERGE_* */
+    int32_t reserved[8];        /* must be zero */
 } pkv_config;
 
 typedef struct pkv_tensors {
@@ -125,7 +132,7 @@ typedef struct pkv_queue_info {
     int32_t n_split_rows;       /* rows with more than one range */
     int32_t n_merge_rows;       /* rows finished by the merge kernel (split or empty) */
     int32_t n_partial_slots;    /* partial states written by the decode kernel */
-    int32_t launches_per_step;  /* kernels pkv_decode enqueues: 1 or 2 */
+    int32_t launches_per_step;  /* kernels pkv_decode enqueues (1, or 2 with a separate merge) */
     int32_t reserved;
     uint64_t kv_bytes;          /* K+V bytes of valid tokens (algorithmic read volume) */
     uint64_t partial_bytes;     /* bytes of partial states written and re-read */
@@ -155,6 +162,7 @@ typedef struct pkv_layout {
                                    u16 chunk, u32 tok_begin, u32 tok_end */
     uint64_t partial_o_off;     /* fp32 [max_items][G][D], normalised partial outputs */
     uint64_t partial_lse_off;   /* fp32 [max_items][G], natural-log partial LSE */
+    uint64_t arrive_off;        /* uint32 [max_batch][Hkv] arrival counters of the fused merge */
     uint64_t total_bytes;
     int32_t max_items;
     int32_t reserved;
@@ -199,6 +207,21 @@ PKV_API pkv_status pkv_decode(pkv_handle* h, const pkv_tensors* t, void* stream)
  * before and right after the persistent decode kernel (not the merge).  Pass
  * nulls to stop recording. */
 PKV_API pkv_status pkv_set_decode_events(pkv_handle* h, void* before, void* after);
+
+/* Optional per-item trace (diagnostics): when buf (device memory, 32 bytes x
+ * capacity) is set, every decode launch writes, for each item it runs,
+ * uint64 {item index | workgroup << 32, start clock, end clock,
+ * hardware id | XCC id << 32} at slot item index (items at or beyond
+ * capacity are not traced).  Clocks are the 100 MHz device wall clock.
+ * Pass null to stop tracing. */
+PKV_API pkv_status pkv_set_trace(pkv_handle* h, void* buf, int32_t capacity);
+
+/* Streaming copy of `bytes` (a multiple of 16) from src to dst on stream,
+ * by a grid of `grid` workgroups (0 -> 4 per CU) of 256 threads, with
+ * dwordx4 loads and stores: a known-size reference for measured HBM
+ * bandwidth and for normalising hardware traffic counters. */
+PKV_API pkv_status pkv_copy_probe(void* dst, const void* src, size_t bytes, int32_t grid,
+                                  void* stream);
 
 /* Read the control words (synchronises the device).  Returns
  * PKV_ERR_DEVICE_FAULT when the device error word is set. */

@@ -40,6 +40,8 @@ struct pkv_handle {
     pkv_queue_info qinfo{};
     hipEvent_t ev_before = nullptr;
     hipEvent_t ev_after = nullptr;
+    uint64_t* trace = nullptr;
+    int32_t trace_cap = 0;
     std::string last_error;
 };
 
@@ -73,6 +75,9 @@ DecodeParams make_params(const pkv_handle* h, const pkv_tensors* t) {
     p.items = reinterpret_cast<const Item*>(h->ws + h->lay.items_off);
     p.partial_o = reinterpret_cast<float*>(h->ws + h->lay.partial_o_off);
     p.partial_lse = reinterpret_cast<float*>(h->ws + h->lay.partial_lse_off);
+    p.arrive = reinterpret_cast<uint32_t*>(h->ws + h->lay.arrive_off);
+    p.trace = h->trace;
+    p.trace_cap = h->trace_cap;
     p.host_error = h->host_err_dev;
     p.batch = t ? t->batch : 0;
     p.bt_stride = (t && t->block_table_stride) ? t->block_table_stride : h->r.max_pages_per_seq;
@@ -81,6 +86,7 @@ DecodeParams make_params(const pkv_handle* h, const pkv_tensors* t) {
     p.hkv = h->r.hkv;
     p.max_tokens = h->r.max_pages_per_seq * h->r.page;
     p.max_items = h->r.max_items;
+    p.fused_merge = h->r.merge_mode == PKV_MERGE_FUSED ? 1 : 0;
     p.scale_log2 = h->r.scale * 1.44269504088896340736f;
     return p;
 }
@@ -190,7 +196,9 @@ PKV_API pkv_status pkv_create(const pkv_config* cfg, void* workspace, size_t wor
         return PKV_ERR_HIP;
     }
     memset(h->host_err, 0, 64);
-    int rc = launch_init_ctrl(reinterpret_cast<Ctrl*>(h->ws + h->lay.ctrl_off), h->stream);
+    int rc = launch_init_ctrl(reinterpret_cast<Ctrl*>(h->ws + h->lay.ctrl_off),
+                              reinterpret_cast<uint32_t*>(h->ws + h->lay.arrive_off),
+                              h->r.max_batch * h->r.hkv, h->stream);
     if (rc != 0) { pkv_destroy(h); return PKV_ERR_HIP; }
     // an empty queue until the first build
     QHdr* qh = reinterpret_cast<QHdr*>(h->staging[0]);
@@ -300,7 +308,7 @@ PKV_API pkv_status pkv_decode(pkv_handle* h, const pkv_tensors* t, void* stream)
     if (rc != 0) return hip_fail(h, (hipError_t)rc, "decode launch");
     if (h->ev_after && (e = hipEventRecord(h->ev_after, st)) != hipSuccess) return hip_fail(h, e, "event record");
     const int merge_rows = h->built_on_device ? h->batch : h->qinfo.n_merge_rows;
-    if (merge_rows > 0) {
+    if (h->r.merge_mode == PKV_MERGE_SEPARATE && merge_rows > 0) {
         rc = launch_merge(p, h->r.d, h->r.g, merge_rows, st);
         if (rc != 0) return hip_fail(h, (hipError_t)rc, "merge launch");
     }
@@ -313,6 +321,28 @@ PKV_API pkv_status pkv_set_decode_events(pkv_handle* h, void* before, void* afte
     h->ev_before = static_cast<hipEvent_t>(before);
     h->ev_after = static_cast<hipEvent_t>(after);
     return PKV_OK;
+}
+
+PKV_API pkv_status pkv_set_trace(pkv_handle* h, void* buf, int32_t capacity) {
+    if (!h) return PKV_ERR_INVALID_ARG;
+    if (buf && (capacity <= 0 || !aligned(buf, 8))) return fail(h, PKV_ERR_INVALID_ARG, "bad trace buffer");
+    h->trace = static_cast<uint64_t*>(buf);
+    h->trace_cap = buf ? capacity : 0;
+    return PKV_OK;
+}
+
+PKV_API pkv_status pkv_copy_probe(void* dst, const void* src, size_t bytes, int32_t grid, void* stream) {
+    if (!dst || !src || bytes == 0 || bytes % 16 || !aligned(dst, 16) || !aligned(src, 16) || grid < 0)
+        return PKV_ERR_INVALID_ARG;
+    int g = grid;
+    if (g == 0) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return PKV_ERR_HIP;
+        g = 4 * cus;
+    }
+    return launch_copy_probe(dst, src, bytes, g, stream) == 0 ? PKV_OK : PKV_ERR_HIP;
 }
 
 PKV_API pkv_status pkv_query(pkv_handle* h, pkv_runtime_info* info) {

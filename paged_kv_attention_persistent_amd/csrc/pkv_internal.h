@@ -54,7 +54,7 @@ inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 struct Resolved {
     int hq, hkv, g, d, page, num_pages, max_batch, max_pages_per_seq;
     float scale;
-    int policy, order, chunk, num_cus, max_items, wg_per_cu;
+    int policy, order, chunk, num_cus, max_items, wg_per_cu, merge_mode;
 };
 
 pkv_status resolve_config(const pkv_config* cfg, int device_cus, Resolved* r, const char** why);
@@ -82,6 +82,9 @@ struct DecodeParams {
     const Item* items;
     float* partial_o;
     float* partial_lse;
+    uint32_t* arrive;           // [max_batch][Hkv] arrival counters (fused merge)
+    uint64_t* trace;            // per-item trace records (nullable)
+    int32_t trace_cap;
     uint32_t* host_error;       // mapped host word mirrored on device faults (nullable)
     int32_t batch;
     int32_t bt_stride;
@@ -90,6 +93,7 @@ struct DecodeParams {
     int32_t hkv;
     int32_t max_tokens;         // max_pages_per_seq * page size
     int32_t max_items;          // capacity of items and partial slots
+    int32_t fused_merge;        // 1: last arriver merges inside the decode kernel
     float scale_log2;           // scale * log2(e)
 };
 
@@ -112,12 +116,13 @@ struct BuildParams {
 };
 
 // Launch wrappers (pkv_kernels.hip).  Return a hipError_t as int.
-int launch_init_ctrl(Ctrl* ctrl, void* stream);
+int launch_init_ctrl(Ctrl* ctrl, uint32_t* arrive, int n_arrive, void* stream);
 int launch_decode(const DecodeParams& p, int head_dim, int group, int grid, void* stream);
 int launch_merge(const DecodeParams& p, int head_dim, int group, int n_rows, void* stream);
 int launch_build_queue(const BuildParams& p, void* stream);
 int launch_debug_gather(const DecodeParams& p, int head_dim, int item_index, uint16_t* k_out,
                         uint16_t* v_out, void* stream);
 bool supported_shape(int head_dim, int group);
+int launch_copy_probe(void* dst, const void* src, size_t bytes, int grid, void* stream);
 
 }  // namespace pkv

@@ -55,7 +55,7 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
 // Sum over the 8 consecutive lanes of a half-row.
@@ -92,29 +92,30 @@ struct Tile {
     u32x4 v[2][NPC];
 };
 
-// Element offset of lane (r, p)'s piece k of token row `tok` in a slab.
+// Byte offsets of the lane's two token rows inside a (page, head) slab.  Rows
+// at or beyond `valid` are never read: their lanes re-read row 0 of the same
+// page (always a valid token) and the consumer masks them.
+struct LaneOff {
+    uint32_t o0, o1;
+};
+
 template <int D>
-__device__ __forceinline__ int piece_off(int tok, int k, int p) {
-    return tok * D + (8 * k + p) * 8;
+__device__ __forceinline__ LaneOff lane_offsets(int r, int p, int valid) {
+    const int t0 = r < valid ? r : 0;
+    const int t1 = 8 + r < valid ? 8 + r : 0;
+    return {(uint32_t)(t0 * D * 2 + p * 16), (uint32_t)(t1 * D * 2 + p * 16)};
 }
 
-// The gather: load the lane's share of page `pg` (slab of KV head hk).  Rows
-// at or beyond `valid` are not read: their lanes re-read row 0 of the same
-// page (always a valid token) and the caller masks them.
+// The gather of one page: ks / vs are the wave-uniform slab addresses, the
+// lane adds its 32-bit row offset; piece k sits 128 bytes further on.
 template <int D>
-__device__ __forceinline__ void load_tile(Tile<D>& t, const uint16_t* __restrict__ kp,
-                                          const uint16_t* __restrict__ vp, size_t slab, int r,
-                                          int p, int valid) {
-    const uint16_t* ks = kp + slab;
-    const uint16_t* vs = vp + slab;
-    const int t0 = (r < valid) ? r : 0;
-    const int t1 = (8 + r < valid) ? 8 + r : 0;
+__device__ __forceinline__ void load_tile(Tile<D>& t, const char* ks, const char* vs, LaneOff o) {
 #pragma unroll
     for (int k = 0; k < Tile<D>::NPC; ++k) {
-        t.k[0][k] = *reinterpret_cast<const u32x4*>(ks + piece_off<D>(t0, k, p));
-        t.k[1][k] = *reinterpret_cast<const u32x4*>(ks + piece_off<D>(t1, k, p));
-        t.v[0][k] = *reinterpret_cast<const u32x4*>(vs + piece_off<D>(t0, k, p));
-        t.v[1][k] = *reinterpret_cast<const u32x4*>(vs + piece_off<D>(t1, k, p));
+        t.k[0][k] = *reinterpret_cast<const u32x4*>(ks + o.o0 + 128 * k);
+        t.k[1][k] = *reinterpret_cast<const u32x4*>(ks + o.o1 + 128 * k);
+        t.v[0][k] = *reinterpret_cast<const u32x4*>(vs + o.o0 + 128 * k);
+        t.v[1][k] = *reinterpret_cast<const u32x4*>(vs + o.o1 + 128 * k);
     }
 }
 
@@ -125,7 +126,7 @@ struct State {
     float acc[G][D / 8];
 };
 
-template <int D, int G>
+template <int D, int G, bool MASKED>
 __device__ __forceinline__ void consume_tile(const Tile<D>& t, const u32x4 (&qv)[G][D / 64],
                                              State<D, G>& st, float c, int r, int valid) {
     constexpr int NPC = D / 64;
@@ -148,7 +149,7 @@ __device__ __forceinline__ void consume_tile(const Tile<D>& t, const u32x4 (&qv)
     u32x4 v[2][NPC];
 #pragma unroll
     for (int k = 0; k < NPC; ++k) { v[0][k] = t.v[0][k]; v[1][k] = t.v[1][k]; }
-    if (valid < kPageSize) {                      // uniform: only the last page of a row
+    if (MASKED) {                                 // the last, partial page of a row
         const bool ok0 = r < valid, ok1 = 8 + r < valid;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -206,62 +207,95 @@ struct PipelineDepth {
     static constexpr int value = (G * D / 8 <= 64) ? 2 : 1;
 };
 
+// Wave-uniform description of one item as seen by one wave.
+struct WaveItem {
+    uint32_t tb, te;       // token range of the item
+    int w;                 // wave index in the workgroup
+    int hk;                // KV head
+};
+
 // One window of up to 64 of this wave's pages: i = wb .. wb + n - 1 of the
-// wave's page list (item page w + 8 i).  Loads run two pages ahead; past the
-// end the prefetch re-reads the window's last page (a cache hit) so that every
-// iteration issues the same loads and the wait counts stay exact.
+// wave's page list (item page w + 8 i).  Loads run ahead of the page being
+// consumed; past the end the prefetch re-reads the last full page (a cache
+// hit) so that every iteration issues the same loads and the wait counts the
+// compiler derives stay exact.  btv holds the window's validated page ids.
 template <int D, int G>
 __device__ __forceinline__ void run_window(const DecodeParams& P, const u32x4 (&qv)[G][D / 64],
-                                           State<D, G>& st, int32_t btv, int n, int wb, int w,
-                                           int hk, uint32_t tb, uint32_t te, int r, int p, int lane) {
-    const size_t slab_elems = (size_t)kPageSize * D;
-    auto page_of = [&](int ii, int& valid) -> size_t {
-        int32_t pg = __builtin_amdgcn_readlane(btv, ii);
-        if ((uint32_t)pg >= (uint32_t)P.num_pages) {
-            if (lane == 0) report(P.ctrl, P.host_error, PKV_DEVERR_PAGE_OOB, (uint32_t)pg);
-            pg = 0;
-        }
-        const int64_t tok0 = (int64_t)tb + (int64_t)(w + 8 * (wb + ii)) * kPageSize;
-        const int64_t rem = (int64_t)te - tok0;
-        valid = rem < kPageSize ? (int)rem : kPageSize;
-        return ((size_t)pg * P.hkv + hk) * slab_elems;
+                                           State<D, G>& st, int32_t btv, int n, int wb,
+                                           const WaveItem& wi, int r, int p) {
+    constexpr uint64_t kSlabBytes = (uint64_t)kPageSize * D * 2;
+    const char* kbase = reinterpret_cast<const char*>(P.k_pool);
+    const char* vbase = reinterpret_cast<const char*>(P.v_pool);
+    const uint64_t head_off = (uint64_t)wi.hk * kSlabBytes;
+    const uint64_t page_stride = (uint64_t)P.hkv * kSlabBytes;
+    // page ii of the window: slab byte offset and number of valid rows (both uniform)
+    auto page_of = [&](int ii, int& valid) -> uint64_t {
+        const int32_t pg = __builtin_amdgcn_readlane(btv, ii);
+        const uint32_t tok0 = wi.tb + (uint32_t)(wi.w + kWaves * (wb + ii)) * kPageSize;
+        const uint32_t rem = wi.te - tok0;
+        valid = rem < (uint32_t)kPageSize ? (int)rem : kPageSize;
+        return (uint64_t)(uint32_t)pg * page_stride + head_off;
     };
     const float c = P.scale_log2;
-    auto clamp = [n](int ii) { return ii < n ? ii : n - 1; };
-    if constexpr (PipelineDepth<D, G>::value == 2) {     // three tiles, two pages ahead
-        Tile<D> A, B, C;
-        int va, vb, vc;
-        size_t sa = page_of(0, va);
-        load_tile<D>(A, P.k_pool, P.v_pool, sa, r, p, va);
-        size_t sb = page_of(clamp(1), vb);
-        load_tile<D>(B, P.k_pool, P.v_pool, sb, r, p, vb);
-        for (int ii = 0; ii < n; ii += 3) {
-            size_t sc = page_of(clamp(ii + 2), vc);
-            load_tile<D>(C, P.k_pool, P.v_pool, sc, r, p, vc);
-            consume_tile<D, G>(A, qv, st, c, r, va);
-            if (ii + 1 >= n) break;
-            sa = page_of(clamp(ii + 3), va);
-            load_tile<D>(A, P.k_pool, P.v_pool, sa, r, p, va);
-            consume_tile<D, G>(B, qv, st, c, r, vb);
-            if (ii + 2 >= n) break;
-            sb = page_of(clamp(ii + 4), vb);
-            load_tile<D>(B, P.k_pool, P.v_pool, sb, r, p, vb);
-            consume_tile<D, G>(C, qv, st, c, r, vc);
+    // Only the item's last page can be partial; keep it out of the pipelined
+    // loop so that the loop issues full-page loads with loop-invariant lane
+    // offsets (no per-page VGPR temporaries competing with in-flight tiles).
+    int vlast;
+    const uint64_t slast = page_of(n - 1, vlast);
+    const int nf = vlast < kPageSize ? n - 1 : n;               // full pages in the window
+    const LaneOff full = lane_offsets<D>(r, p, kPageSize);
+    auto issue = [&](Tile<D>& T, int ii) {
+        int unused;
+        const uint64_t so = page_of(ii < nf ? ii : nf - 1, unused);
+        LaneOff o = full;
+        // Keep the lane offset a 32-bit VGPR inside the loop so the loads use
+        // the scalar-base + 32-bit-offset form (no 64-bit per-lane address math).
+        __asm__ volatile("" : "+v"(o.o0), "+v"(o.o1));
+        load_tile<D>(T, kbase + so, vbase + so, o);
+    };
+    // The loop is rotated so that every iteration first consumes a tile and
+    // then refills the registers it just freed: no instruction at the loop
+    // head writes a register that a load may still be filling.
+    if (nf > 0) {
+        if constexpr (PipelineDepth<D, G>::value == 2) {     // three tiles, two pages ahead
+            Tile<D> A, B, C;
+            issue(A, 0);
+            issue(B, 1);
+            issue(C, 2);
+            for (int ii = 0;; ii += 3) {
+                consume_tile<D, G, false>(A, qv, st, c, r, kPageSize);
+                if (ii + 1 >= nf) break;
+                issue(A, ii + 3);
+                consume_tile<D, G, false>(B, qv, st, c, r, kPageSize);
+                if (ii + 2 >= nf) break;
+                issue(B, ii + 4);
+                consume_tile<D, G, false>(C, qv, st, c, r, kPageSize);
+                if (ii + 3 >= nf) break;
+                issue(C, ii + 5);
+            }
+        } else {                                              // two tiles, one page ahead
+            Tile<D> A, B;
+            issue(A, 0);
+            issue(B, 1);
+            for (int ii = 0;; ii += 2) {
+                consume_tile<D, G, false>(A, qv, st, c, r, kPageSize);
+                if (ii + 1 >= nf) break;
+                issue(A, ii + 2);
+                consume_tile<D, G, false>(B, qv, st, c, r, kPageSize);
+                if (ii + 2 >= nf) break;
+                issue(B, ii + 3);
+            }
         }
-    } else {                                              // two tiles, one page ahead
-        Tile<D> A, B;
-        int va, vb;
-        size_t sa = page_of(0, va);
-        load_tile<D>(A, P.k_pool, P.v_pool, sa, r, p, va);
-        for (int ii = 0; ii < n; ii += 2) {
-            size_t sb = page_of(clamp(ii + 1), vb);
-            load_tile<D>(B, P.k_pool, P.v_pool, sb, r, p, vb);
-            consume_tile<D, G>(A, qv, st, c, r, va);
-            if (ii + 1 >= n) break;
-            sa = page_of(clamp(ii + 2), va);
-            load_tile<D>(A, P.k_pool, P.v_pool, sa, r, p, va);
-            consume_tile<D, G>(B, qv, st, c, r, vb);
-        }
+    }
+    // Drain the prefetches issued past the window's end (cache hits) once
+    // here, so that no later code, and no later loop entry, inherits loads
+    // still in flight into registers it reuses.  s_waitcnt vmcnt(0) with the
+    // other counters left at their maxima (GFX9 encoding).
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (nf < n) {                                             // the partial last page
+        Tile<D> T;
+        load_tile<D>(T, kbase + slast, vbase + slast, lane_offsets<D>(r, p, vlast));
+        consume_tile<D, G, true>(T, qv, st, c, r, vlast);
     }
 }
 
@@ -271,25 +305,69 @@ struct Smem {
     float m[kWaves][G];
     float l[kWaves][G];
     uint32_t next;
+    uint32_t last;
 };
 
+// Exact merge of the partial states of one split (row, KV head) (PersistentKV
+// page, Methodology 1, "Sequence Splitting"): with M = max_c lse_c and
+// w_c = exp(lse_c - M), O = sum_c w_c o_c / sum_c w_c and
+// LSE = M + ln sum_c w_c.  A row with no ranges gets O = 0, LSE = -inf.
+template <int D, int G, int NT>
+__device__ void merge_row(const DecodeParams& P, int b, int hk, int nc, int base, int tid) {
+    for (int t = tid; t < G * D; t += NT) {
+        const int g = t / D, d = t % D;
+        const size_t h = (size_t)hk * G + g;
+        float M = -INFINITY;
+#pragma unroll 8
+        for (int c = 0; c < nc; ++c)
+            M = fmaxf(M, P.partial_lse[((size_t)(base + c) * P.hkv + hk) * G + g]);
+        float O = 0.0f, lse = -INFINITY;
+        if (M != -INFINITY) {
+            float L = 0.0f;
+#pragma unroll 8
+            for (int c = 0; c < nc; ++c) {
+                const size_t s = ((size_t)(base + c) * P.hkv + hk) * G + g;
+                const float l = P.partial_lse[s];
+                const float wgt = l == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((l - M) * kLog2e);
+                L += wgt;
+                O = fmaf(wgt, P.partial_o[s * D + d], O);
+            }
+            O = O / L;
+            lse = M + logf(L);
+        }
+        P.out[((size_t)b * P.hq + h) * D + d] = f32_to_bf16_rne(O);
+        if (d == 0) P.lse[(size_t)b * P.hq + h] = lse;
+    }
+}
+
+// Claim the next item for this workgroup: the grid's first round is static
+// (workgroup i runs item i), later items are popped from the shared head.
+__device__ __forceinline__ uint32_t pop_next(const DecodeParams& P) {
+    return gridDim.x + atomicAdd(&P.ctrl->head, 1u);
+}
+
 template <int D, int G>
-__device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, uint32_t idx) {
+__device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, uint32_t idx, uint32_t& nxt) {
     constexpr int NPC = D / 64;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane >> 3;
     const int p = lane & 7;
 
-    const Item it = P.items[idx];
-    const int b = (int)it.seq;
-    const int hk = (int)it.kv_head;
-    const uint32_t tb = it.tok_begin, te = it.tok_end;
-    const bool bad = b >= P.batch || hk >= P.hkv || tb >= te || te > (uint32_t)P.max_tokens ||
-                     (tb % kPageSize) != 0;
+    const Item* itp = P.items + idx;
+    const int b = __builtin_amdgcn_readfirstlane((int)itp->seq);
+    const int hk = __builtin_amdgcn_readfirstlane((int)itp->kv_head);
+    const int chunk = __builtin_amdgcn_readfirstlane((int)itp->chunk);
+    const uint32_t tb = (uint32_t)__builtin_amdgcn_readfirstlane((int)itp->tok_begin);
+    const uint32_t te = (uint32_t)__builtin_amdgcn_readfirstlane((int)itp->tok_end);
+    const bool bad = b < 0 || b >= P.batch || hk >= P.hkv || tb >= te ||
+                     te > (uint32_t)P.max_tokens || (tb % kPageSize) != 0;
     if (bad) {                                     // uniform over the workgroup
-        if (tid == 0) report(P.ctrl, P.host_error, PKV_DEVERR_BAD_ITEM, idx);
+        if (tid == 0) {
+            report(P.ctrl, P.host_error, PKV_DEVERR_BAD_ITEM, idx);
+            nxt = pop_next(P);
+        }
         return;
     }
     const int n_pages = (int)((te - tb + kPageSize - 1) / kPageSize);
@@ -313,12 +391,23 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, uint32_t idx
         for (int e = 0; e < D / 8; ++e) st.acc[g][e] = 0.0f;
     }
 
+    const WaveItem wi{tb, te, w, hk};
     const int32_t* bt_row = P.block_table + (size_t)b * P.bt_stride + first_page + w;
     for (int wb = 0; wb < nw; wb += 64) {
         const int n = nw - wb < 64 ? nw - wb : 64;
-        const int32_t btv = lane < n ? bt_row[(size_t)kWaves * (wb + lane)] : 0;
-        run_window<D, G>(P, qv, st, btv, n, wb, w, hk, tb, te, r, p, lane);
+        int32_t btv = lane < n ? bt_row[(size_t)kWaves * (wb + lane)] : 0;
+        const bool badl = lane < n && (uint32_t)btv >= (uint32_t)P.num_pages;
+        const unsigned long long badm = __ballot(badl);
+        if (badm) {                                   // never read outside the pool
+            if (lane == __ffsll(badm) - 1) report(P.ctrl, P.host_error, PKV_DEVERR_PAGE_OOB, (uint32_t)btv);
+            btv = badl ? 0 : btv;
+        }
+        run_window<D, G>(P, qv, st, btv, n, wb, wi, r, p);
     }
+    // Claim the next item only now, near the end of this one: a claim made
+    // earlier would hold an item this workgroup cannot start while another
+    // workgroup runs dry.  Its latency hides behind the combine below.
+    if (tid == 0) nxt = pop_next(P);
 
     // Combine the 8 token groups of this wave (lanes r = 0..7 with equal p).
 #pragma unroll
@@ -357,10 +446,11 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, uint32_t idx
 
     const int nch = P.n_chunks[b];
     const bool split = nch > 1;
-    const int slot = split ? (P.part_off[b] + (int)it.chunk) * P.hkv + hk : 0;
-    if (split && ((int)it.chunk >= nch || slot < 0 || slot >= P.max_items)) {
+    const int base = split ? P.part_off[b] : 0;
+    const int slot = split ? (base + chunk) * P.hkv + hk : 0;
+    if (split && (chunk >= nch || slot < 0 || (base + nch) * P.hkv > P.max_items)) {
         if (tid == 0) report(P.ctrl, P.host_error, PKV_DEVERR_BAD_ITEM, idx);
-        return;                                    // uniform over the workgroup
+        return;                                    // uniform over the workgroup (next already claimed)
     }
     for (int t = tid; t < G * D; t += kThreads) {
         const int g = t / D, d = t % D;
@@ -385,6 +475,23 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, uint32_t idx
             if (d == 0) P.lse[(size_t)b * P.hq + h] = lse;
         }
     }
+    if (split && P.fused_merge) {
+        // Last arriver of this (row, KV head) merges all its ranges: every
+        // workgroup publishes its partial (release), counts itself in, and the
+        // one that completes the count reads the others' partials (acquire).
+        __threadfence();
+        __syncthreads();
+        if (tid == 0) {
+            const uint32_t old = atomicAdd(&P.arrive[(size_t)b * P.hkv + hk], 1u);
+            sm.last = (old + 1 == (uint32_t)nch) ? 1u : 0u;
+        }
+        __syncthreads();
+        if (sm.last) {
+            __threadfence();
+            merge_row<D, G, kThreads>(P, b, hk, nch, base, tid);
+            if (tid == 0) atomicExch(&P.arrive[(size_t)b * P.hkv + hk], 0u);
+        }
+    }
 }
 
 template <int D, int G>
@@ -393,23 +500,54 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     const int tid = threadIdx.x;
     Ctrl* ctrl = P.ctrl;
     const uint32_t n_items = (uint32_t)P.qhdr->n_items;
-    if (tid == 0) sm.next = atomicAdd(&ctrl->head, 1u);
-    __syncthreads();
-    uint32_t idx = sm.next;
+    const uint64_t t_enter = P.trace ? wall_clock64() : 0;
+    if (P.fused_merge) {                 // rows with no tokens take the neutral state
+        const int n_rows = P.qhdr->n_merge_rows;
+        for (int ri = blockIdx.x; ri < n_rows; ri += gridDim.x) {
+            const int b = P.merge_rows[ri];
+            if (b < 0 || b >= P.batch || P.n_chunks[b] != 0) continue;
+            for (int t = tid; t < P.hq * D; t += kThreads) {
+                P.out[(size_t)b * P.hq * D + t] = 0;
+                if (t % D == 0) P.lse[(size_t)b * P.hq + t / D] = -INFINITY;
+            }
+        }
+    }
+    uint32_t idx = blockIdx.x;                     // first round: static assignment
     uint32_t done_here = 0;
+    if (P.trace && tid == 0 && n_items + blockIdx.x < (uint32_t)P.trace_cap) {
+        // workgroup record after the item records: entry time, first pop returned
+        uint64_t* rec = P.trace + 4ull * (n_items + blockIdx.x);
+        rec[0] = (uint64_t)blockIdx.x | (1ull << 63) | ((uint64_t)idx << 32);
+        rec[1] = t_enter;
+        rec[2] = wall_clock64();
+        rec[3] = (uint64_t)__builtin_amdgcn_s_getreg((4 << 0) | (0 << 6) | (31 << 11)) |
+                 ((uint64_t)__builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (31 << 11)) << 32);
+    }
     while (idx < n_items) {
         uint32_t nxt = 0;
-        if (tid == 0) nxt = atomicAdd(&ctrl->head, 1u);   // claim the next item early
-        process_item<D, G>(P, sm, idx);
+        uint64_t t_start = 0;
+        if (P.trace) t_start = wall_clock64();
+        process_item<D, G>(P, sm, idx, nxt);
         ++done_here;
+        if (P.trace && tid == 0 && idx < (uint32_t)P.trace_cap) {
+            const uint64_t t_end = wall_clock64();
+            const uint32_t hw = __builtin_amdgcn_s_getreg((4 << 0) | (0 << 6) | (31 << 11));   // HW_ID
+            const uint32_t xcc = __builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (31 << 11)); // XCC_ID
+            uint64_t* rec = P.trace + 4ull * idx;
+            rec[0] = (uint64_t)idx | ((uint64_t)blockIdx.x << 32);
+            rec[1] = t_start;
+            rec[2] = t_end;
+            rec[3] = (uint64_t)hw | ((uint64_t)xcc << 32);
+        }
         __syncthreads();
         if (tid == 0) sm.next = nxt;
         __syncthreads();
-        idx = sm.next;
+        idx = __builtin_amdgcn_readfirstlane(sm.next);
     }
     if (tid == 0) {
+        // Thread 0's last pop has returned before this point, so when the
+        // done count completes no workgroup can pop again: re-arm the head.
         if (done_here) atomicAdd(&ctrl->items_done, done_here);
-        __threadfence();
         const uint32_t prev = atomicAdd(&ctrl->done, 1u);
         if (prev == gridDim.x - 1) {                        // last workgroup out re-arms
             atomicExch(&ctrl->head, 0u);
@@ -419,10 +557,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     }
 }
 
-// Exact merge of split partial states (PersistentKV page, Methodology 1,
-// "Sequence Splitting"): with M = max_c lse_c and w_c = exp(lse_c - M),
-// O = sum_c w_c o_c / sum_c w_c and LSE = M + ln sum_c w_c.  Rows with no
-// items (L = 0) receive the neutral state O = 0, LSE = -inf.
+// The separate merge kernel: one workgroup per (merge row, KV head).
 template <int D, int G>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
     const int n_rows = P.qhdr->n_merge_rows;
@@ -430,29 +565,10 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
     const int hk = blockIdx.x % P.hkv;
     if (ri >= n_rows) return;
     const int b = P.merge_rows[ri];
+    if (b < 0 || b >= P.batch) return;
     const int nc = P.n_chunks[b];
-    const int base = P.part_off[b];
-    for (int t = threadIdx.x; t < G * D; t += 256) {
-        const int g = t / D, d = t % D;
-        const size_t h = (size_t)hk * G + g;
-        float M = -INFINITY;
-        for (int c = 0; c < nc; ++c)
-            M = fmaxf(M, P.partial_lse[((size_t)(base + c) * P.hkv + hk) * G + g]);
-        float O = 0.0f, L = 0.0f, lse = -INFINITY;
-        if (M != -INFINITY) {
-            for (int c = 0; c < nc; ++c) {
-                const size_t s = ((size_t)(base + c) * P.hkv + hk) * G + g;
-                const float l = P.partial_lse[s];
-                const float wgt = l == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((l - M) * kLog2e);
-                L += wgt;
-                O = fmaf(wgt, P.partial_o[s * D + d], O);
-            }
-            O = O / L;
-            lse = M + logf(L);
-        }
-        P.out[((size_t)b * P.hq + h) * D + d] = f32_to_bf16_rne(O);
-        if (d == 0) P.lse[(size_t)b * P.hq + h] = lse;
-    }
+    if (nc == 1 || (P.part_off[b] + nc) * P.hkv > P.max_items) return;
+    merge_row<D, G, 256>(P, b, hk, nc, P.part_off[b], threadIdx.x);
 }
 
 // Device queue builder: the same bytes as the host builder, from device
@@ -593,7 +709,9 @@ __global__ __launch_bounds__(64) void debug_gather_kernel(DecodeParams P, int it
         const int rem = (int)(it.tok_end - it.tok_begin) - j * kPageSize;
         const int valid = rem < kPageSize ? rem : kPageSize;
         Tile<D> t;
-        load_tile<D>(t, P.k_pool, P.v_pool, ((size_t)pg * P.hkv + it.kv_head) * kPageSize * D, r, p, valid);
+        const uint64_t slab = ((uint64_t)(uint32_t)pg * P.hkv + it.kv_head) * kPageSize * D * 2;
+        load_tile<D>(t, reinterpret_cast<const char*>(P.k_pool) + slab,
+                     reinterpret_cast<const char*>(P.v_pool) + slab, lane_offsets<D>(r, p, valid));
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
             const int tok = 8 * jj + r;
@@ -608,9 +726,27 @@ __global__ __launch_bounds__(64) void debug_gather_kernel(DecodeParams P, int it
     }
 }
 
-__global__ void init_ctrl_kernel(Ctrl* c) {
+// Streaming copy used as a bandwidth and traffic-counter reference: each
+// thread moves four independent 16-byte vectors per step (grid-stride).
+__global__ __launch_bounds__(256) void copy_probe_kernel(u32x4* __restrict__ dst,
+                                                         const u32x4* __restrict__ src, size_t n) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n; i += 4 * stride) {
+        const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+        dst[i] = a;
+        dst[i + stride] = b;
+        dst[i + 2 * stride] = c;
+        dst[i + 3 * stride] = d;
+    }
+    for (; i < n; i += stride) dst[i] = src[i];
+}
+
+__global__ void init_ctrl_kernel(Ctrl* c, uint32_t* arrive, int n_arrive) {
     uint32_t* w = reinterpret_cast<uint32_t*>(c);
-    w[threadIdx.x] = 0u;
+    if (blockIdx.x == 0 && threadIdx.x < sizeof(Ctrl) / 4) w[threadIdx.x] = 0u;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_arrive; i += gridDim.x * blockDim.x)
+        arrive[i] = 0u;
 }
 
 template <int D, int G>
@@ -648,8 +784,14 @@ bool supported_shape(int head_dim, int group) {
         return (int)hipErrorInvalidValue;                                       \
     } while (0)
 
-int launch_init_ctrl(Ctrl* ctrl, void* stream) {
-    hipLaunchKernelGGL(init_ctrl_kernel, dim3(1), dim3(sizeof(Ctrl) / 4), 0, (hipStream_t)stream, ctrl);
+int launch_init_ctrl(Ctrl* ctrl, uint32_t* arrive, int n_arrive, void* stream) {
+    hipLaunchKernelGGL(init_ctrl_kernel, dim3(64), dim3(256), 0, (hipStream_t)stream, ctrl, arrive, n_arrive);
+    return (int)hipGetLastError();
+}
+
+int launch_copy_probe(void* dst, const void* src, size_t bytes, int grid, void* stream) {
+    hipLaunchKernelGGL(copy_probe_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                       static_cast<u32x4*>(dst), static_cast<const u32x4*>(src), bytes / 16);
     return (int)hipGetLastError();
 }
 

@@ -24,7 +24,7 @@ pkv_status resolve_config(const pkv_config* cfg, int device_cus, Resolved* r, co
     *why = "";
     if (!cfg || !r) { *why = "null config"; return PKV_ERR_INVALID_ARG; }
     if (cfg->struct_size != sizeof(pkv_config)) { *why = "pkv_config.struct_size mismatch"; return PKV_ERR_INVALID_ARG; }
-    for (int i = 0; i < 9; ++i)
+    for (int i = 0; i < 8; ++i)
         if (cfg->reserved[i]) { *why = "reserved config fields must be zero"; return PKV_ERR_INVALID_ARG; }
     if (cfg->num_q_heads <= 0 || cfg->num_kv_heads <= 0 || cfg->num_q_heads % cfg->num_kv_heads) {
         *why = "num_q_heads must be a positive multiple of num_kv_heads"; return PKV_ERR_INVALID_ARG;
@@ -69,6 +69,10 @@ pkv_status resolve_config(const pkv_config* cfg, int device_cus, Resolved* r, co
     }
     r->wg_per_cu = cfg->wg_per_cu == 0 ? 1 : cfg->wg_per_cu;
     if (r->wg_per_cu < 1 || r->wg_per_cu > 8) { *why = "wg_per_cu must be 1..8"; return PKV_ERR_INVALID_ARG; }
+    if (cfg->merge_mode != PKV_MERGE_FUSED && cfg->merge_mode != PKV_MERGE_SEPARATE) {
+        *why = "unknown merge_mode"; return PKV_ERR_INVALID_ARG;
+    }
+    r->merge_mode = cfg->merge_mode;
     return PKV_OK;
 }
 
@@ -91,6 +95,8 @@ void compute_layout(const Resolved& r, pkv_layout* lay) {
     off = align256(off + 4ull * r.max_items * r.g * r.d);
     lay->partial_lse_off = off;
     off = align256(off + 4ull * r.max_items * r.g);
+    lay->arrive_off = off;
+    off = align256(off + 4ull * r.max_batch * r.hkv);
     lay->total_bytes = off;
     lay->max_items = r.max_items;
 }
@@ -163,7 +169,7 @@ pkv_status plan_queue(const Resolved& r, const int32_t* ctx_lens, int32_t batch,
         info->n_split_rows = n_split_rows;
         info->n_merge_rows = n_merge;
         info->n_partial_slots = part_off[batch] * r.hkv;
-        info->launches_per_step = 1 + (n_merge > 0 ? 1 : 0);
+        info->launches_per_step = 1 + ((r.merge_mode == PKV_MERGE_SEPARATE && n_merge > 0) ? 1 : 0);
         info->kv_bytes = (uint64_t)sum_len * r.hkv * r.d * 2ull * 2ull;
         info->partial_bytes = (uint64_t)info->n_partial_slots * r.g * (r.d + 1) * 4ull * 2ull;
     }

@@ -27,6 +27,7 @@ PKV_ERR_TIMEOUT = -7
 
 PKV_POLICY_AUTO, PKV_POLICY_NO_SPLIT, PKV_POLICY_SPLIT = 0, 1, 2
 PKV_ORDER_CANONICAL, PKV_ORDER_LPT = 0, 1
+PKV_MERGE_FUSED, PKV_MERGE_SEPARATE = 0, 1
 PKV_DEVERR_NONE, PKV_DEVERR_PAGE_OOB, PKV_DEVERR_BAD_ITEM = 0, 1, 2
 
 ITEM_DTYPE = np.dtype([("seq", "<u4"), ("kv_head", "<u2"), ("chunk", "<u2"),
@@ -41,7 +42,7 @@ class pkv_config(C.Structure):
                 ("scale", C.c_float), ("policy", C.c_int32), ("order", C.c_int32),
                 ("kv_chunk_tokens", C.c_int32), ("num_cus", C.c_int32),
                 ("max_items", C.c_int32), ("wg_per_cu", C.c_int32),
-                ("reserved", C.c_int32 * 9)]
+                ("merge_mode", C.c_int32), ("reserved", C.c_int32 * 8)]
 
 
 class pkv_tensors(C.Structure):
@@ -77,7 +78,7 @@ class pkv_layout(C.Structure):
                 ("n_chunks_off", C.c_uint64), ("part_off_off", C.c_uint64),
                 ("merge_rows_off", C.c_uint64), ("items_off", C.c_uint64),
                 ("partial_o_off", C.c_uint64), ("partial_lse_off", C.c_uint64),
-                ("total_bytes", C.c_uint64), ("max_items", C.c_int32),
+                ("arrive_off", C.c_uint64), ("total_bytes", C.c_uint64), ("max_items", C.c_int32),
                 ("reserved", C.c_int32)]
 
 
@@ -103,6 +104,8 @@ SIGNATURES = {
                                    C.POINTER(pkv_queue_info)]),
     "pkv_debug_gather": (C.c_int32, [C.c_void_p, C.POINTER(pkv_tensors), C.c_int32,
                                      C.c_void_p, C.c_void_p, C.c_void_p]),
+    "pkv_set_trace": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_int32]),
+    "pkv_copy_probe": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int32, C.c_void_p]),
 }
 
 _LIB = None
@@ -139,7 +142,8 @@ def _check(status: int, where: str, handle=None) -> None:
 
 def make_config(num_q_heads, num_kv_heads, head_dim, num_pages, max_batch, max_pages_per_seq,
                 page_size=16, scale=0.0, policy=PKV_POLICY_AUTO, order=PKV_ORDER_CANONICAL,
-                kv_chunk_tokens=0, num_cus=0, max_items=0, wg_per_cu=0) -> pkv_config:
+                kv_chunk_tokens=0, num_cus=0, max_items=0, wg_per_cu=0,
+                merge_mode=PKV_MERGE_FUSED) -> pkv_config:
     cfg = pkv_config()
     cfg.struct_size = C.sizeof(pkv_config)
     cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim = num_q_heads, num_kv_heads, head_dim
@@ -148,6 +152,7 @@ def make_config(num_q_heads, num_kv_heads, head_dim, num_pages, max_batch, max_p
     cfg.scale, cfg.policy, cfg.order = scale, policy, order
     cfg.kv_chunk_tokens, cfg.num_cus, cfg.max_items, cfg.wg_per_cu = \
         kv_chunk_tokens, num_cus, max_items, wg_per_cu
+    cfg.merge_mode = merge_mode
     return cfg
 
 
@@ -268,6 +273,19 @@ def pkv_debug_gather(handle: int, tensors: pkv_tensors, item_index: int, k_out, 
                                   C.c_void_p(k_out.data_ptr()), C.c_void_p(v_out.data_ptr()),
                                   C.c_void_p(_stream_ptr(stream))),
            "pkv_debug_gather", C.c_void_p(handle))
+
+
+def pkv_set_trace(handle: int, buf=None) -> None:
+    """buf: a device int64 tensor of 4 * capacity elements, or None."""
+    ptr = buf.data_ptr() if buf is not None else None
+    cap = buf.numel() // 4 if buf is not None else 0
+    _check(lib().pkv_set_trace(C.c_void_p(handle), C.c_void_p(ptr), int(cap)), "pkv_set_trace",
+           C.c_void_p(handle))
+
+
+def pkv_copy_probe(dst, src, nbytes: int, grid: int = 0, stream=None) -> None:
+    _check(lib().pkv_copy_probe(C.c_void_p(dst.data_ptr()), C.c_void_p(src.data_ptr()), int(nbytes),
+                                int(grid), C.c_void_p(_stream_ptr(stream))), "pkv_copy_probe")
 
 
 class PagedDecoder:

@@ -77,7 +77,8 @@ def compare_with_oracle(cfg, lens, hkv, num_cus, chunk, policy, order):
     assert np.array_equal(merge_rows, ref["merge_rows"])
     assert bool(info.split) == ref["split"]
     assert info.n_items == len(ref["items"])
-    assert info.launches_per_step == 1 + (len(ref["merge_rows"]) > 0)
+    sep = cfg.merge_mode == pkv.PKV_MERGE_SEPARATE
+    assert info.launches_per_step == 1 + (sep and len(ref["merge_rows"]) > 0)
     return info
 
 
@@ -106,7 +107,8 @@ def test_host_queue_matches_oracle_random():
         order = int(rng.integers(0, 2))
         cus = int(rng.choice([1, 8, 256]))
         cfg = pkv.make_config(hkv * 4, hkv, 128, 1000, max(bsz, 1), maxp, policy=policy,
-                              order=order, kv_chunk_tokens=chunk, num_cus=cus)
+                              order=order, kv_chunk_tokens=chunk, num_cus=cus,
+                              merge_mode=int(rng.integers(0, 2)))
         compare_with_oracle(cfg, lens.tolist(), hkv, cus, chunk, policy, order)
 
 
@@ -114,7 +116,8 @@ def test_config_validation():
     good = pkv.make_config(32, 8, 128, 100, 4, 10, num_cus=256)
     assert pkv.pkv_workspace_size(good) > 0
     bad = [dict(num_q_heads=30), dict(head_dim=96), dict(page_size=32), dict(kv_chunk_tokens=100),
-           dict(num_pages=0), dict(wg_per_cu=9), dict(policy=7), dict(num_q_heads=64)]
+           dict(num_pages=0), dict(wg_per_cu=9), dict(policy=7), dict(num_q_heads=64),
+           dict(merge_mode=2)]
     base = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, num_pages=100, max_batch=4,
                 max_pages_per_seq=10, num_cus=256)
     for b in bad:
@@ -149,7 +152,7 @@ def test_layout_regions_are_ordered_and_aligned():
     cfg = pkv.make_config(32, 8, 128, 8192, 1, 8192, num_cus=256)
     lay = pkv.pkv_workspace_layout(cfg)
     offs = [lay.ctrl_off, lay.queue_off, lay.n_chunks_off, lay.part_off_off, lay.merge_rows_off,
-            lay.items_off, lay.partial_o_off, lay.partial_lse_off, lay.total_bytes]
+            lay.items_off, lay.partial_o_off, lay.partial_lse_off, lay.arrive_off, lay.total_bytes]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert lay.max_items == 8 * 32
     assert lay.partial_lse_off - lay.partial_o_off >= lay.max_items * 4 * 128 * 4

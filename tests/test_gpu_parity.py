@@ -48,6 +48,7 @@ class Run:
                               dtype=torch.bfloat16, device=dev)
         self.lse = torch.full((wl.batch, wl.num_q_heads), float("nan"), dtype=torch.float32,
                               device=dev)
+        cfgkw.setdefault("num_cus", torch.cuda.get_device_properties(0).multi_processor_count)
         self.cfg = cfg_for(wl, **cfgkw)
         self.dec = pkv.PagedDecoder(self.cfg)
         self.info = None
@@ -133,18 +134,27 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("merge", [pkv.PKV_MERGE_FUSED, pkv.PKV_MERGE_SEPARATE],
+                         ids=["fused_merge", "separate_merge"])
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
-def test_small_cases_full_compare(case):
+def test_small_cases_full_compare(case, merge):
     name, lens, hq, hkv, d, policy, chunk = case
-    say("case", name)
+    say("case", name, "merge", merge)
     wl = workloads.custom(name, lens, hq, hkv, d, spare_pages=5)
-    run = Run(wl, policy=policy, kv_chunk_tokens=chunk)
-    o, l = run.decode()
+    run = Run(wl, policy=policy, kv_chunk_tokens=chunk, merge_mode=merge)
     ro, rl = oracle_full(wl)
-    check(o, l, ro, rl, name)
-    for b, L in enumerate(lens):
-        if L == 0:
-            assert np.all(o[b] == 0) and np.all(np.isneginf(l[b]))
+    for call in range(2):                 # second call: counters and head re-armed
+        o, l = run.decode()
+        check(o, l, ro, rl, f"{name} call {call}")
+        for b, L in enumerate(lens):
+            if L == 0:
+                assert np.all(o[b] == 0) and np.all(np.isneginf(l[b]))
+        run.out.fill_(float("nan"))
+        run.lse.fill_(float("nan"))
+    if run.info.split:
+        lay = run.dec.layout
+        arrive = run.dec.workspace[lay.arrive_off:lay.arrive_off + 4 * len(lens) * hkv]
+        assert int(arrive.cpu().view(torch.int32).abs().sum()) == 0
     run.close()
 
 
@@ -166,11 +176,13 @@ FULL = {"long": [(0, 0), (0, 5)], "mixed": [(b, (3 * b) % 8) for b in range(8)],
         "short": [(0, 0), (17, 3), (63, 7)]}
 
 
+@pytest.mark.parametrize("merge", [pkv.PKV_MERGE_FUSED, pkv.PKV_MERGE_SEPARATE],
+                         ids=["fused_merge", "separate_merge"])
 @pytest.mark.parametrize("name", ["long", "mixed", "short"])
-def test_full_size_sampled_units(name):
+def test_full_size_sampled_units(name, merge):
     say("full", name)
     wl = workloads.CONFIGS[name]()
-    run = Run(wl, poison=True)
+    run = Run(wl, poison=True, merge_mode=merge)
     o, l = run.decode()
     info = run.info
     ref = wq.build_queue(wl.ctx_lens, wl.num_kv_heads, run.dec.query()["num_cus"], 4096)
