@@ -223,6 +223,13 @@ PKV_API pkv_status pkv_set_trace(pkv_handle* h, void* buf, int32_t capacity);
 PKV_API pkv_status pkv_copy_probe(void* dst, const void* src, size_t bytes, int32_t grid,
                                   void* stream);
 
+/* Streaming read of `bytes` (a multiple of 16) from src by `grid`
+ * workgroups (0 -> 4 per CU) of 256 threads, four independent dwordx4 loads
+ * per thread per step; each thread stores one xor-folded word to sink
+ * (uint32 [grid * 256]).  Measures the HBM read ceiling. */
+PKV_API pkv_status pkv_read_probe(const void* src, size_t bytes, void* sink, int32_t grid,
+                                  void* stream);
+
 /* Read the control words (synchronises the device).  Returns
  * PKV_ERR_DEVICE_FAULT when the device error word is set. */
 PKV_API pkv_status pkv_query(pkv_handle* h, pkv_runtime_info* info);

@@ -345,6 +345,20 @@ PKV_API pkv_status pkv_copy_probe(void* dst, const void* src, size_t bytes, int3
     return launch_copy_probe(dst, src, bytes, g, stream) == 0 ? PKV_OK : PKV_ERR_HIP;
 }
 
+PKV_API pkv_status pkv_read_probe(const void* src, size_t bytes, void* sink, int32_t grid, void* stream) {
+    if (!src || !sink || bytes == 0 || bytes % 16 || !aligned(src, 16) || !aligned(sink, 4) || grid < 0)
+        return PKV_ERR_INVALID_ARG;
+    int g = grid;
+    if (g == 0) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return PKV_ERR_HIP;
+        g = 4 * cus;
+    }
+    return launch_read_probe(src, bytes, sink, g, stream) == 0 ? PKV_OK : PKV_ERR_HIP;
+}
+
 PKV_API pkv_status pkv_query(pkv_handle* h, pkv_runtime_info* info) {
     if (!h || !info) return PKV_ERR_INVALID_ARG;
     hipError_t e = hipDeviceSynchronize();

@@ -308,35 +308,66 @@ struct Smem {
     uint32_t last;
 };
 
+// Partial states travel between workgroups of one launch in the fused merge;
+// there they are stored and loaded as relaxed agent-scope atomics, which the
+// hardware keeps coherent across the XCDs' separate L2 caches, so no
+// L2-wide write-back or invalidate is needed.
+template <bool COHERENT>
+__device__ __forceinline__ float ld_partial(const float* p) {
+    if constexpr (COHERENT) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else return *p;
+}
+
+template <bool COHERENT>
+__device__ __forceinline__ void st_partial(float* p, float v) {
+    if constexpr (COHERENT) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *p = v;
+}
+
 // Exact merge of the partial states of one split (row, KV head) (PersistentKV
 // page, Methodology 1, "Sequence Splitting"): with M = max_c lse_c and
 // w_c = exp(lse_c - M), O = sum_c w_c o_c / sum_c w_c and
 // LSE = M + ln sum_c w_c.  A row with no ranges gets O = 0, LSE = -inf.
-template <int D, int G, int NT>
+// Ranges are read 32 at a time, all loads of a block issued together; blocks
+// after the first fold in by rescaling (the same identity, applied twice).
+template <int D, int G, int NT, bool COHERENT>
 __device__ void merge_row(const DecodeParams& P, int b, int hk, int nc, int base, int tid) {
+    constexpr int CB = 32;
     for (int t = tid; t < G * D; t += NT) {
         const int g = t / D, d = t % D;
         const size_t h = (size_t)hk * G + g;
-        float M = -INFINITY;
-#pragma unroll 8
-        for (int c = 0; c < nc; ++c)
-            M = fmaxf(M, P.partial_lse[((size_t)(base + c) * P.hkv + hk) * G + g]);
-        float O = 0.0f, lse = -INFINITY;
-        if (M != -INFINITY) {
-            float L = 0.0f;
-#pragma unroll 8
-            for (int c = 0; c < nc; ++c) {
-                const size_t s = ((size_t)(base + c) * P.hkv + hk) * G + g;
-                const float l = P.partial_lse[s];
-                const float wgt = l == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((l - M) * kLog2e);
-                L += wgt;
-                O = fmaf(wgt, P.partial_o[s * D + d], O);
+        float M = -INFINITY, L = 0.0f, O = 0.0f;
+        for (int c0 = 0; c0 < nc; c0 += CB) {
+            float lv[CB], ov[CB];
+#pragma unroll
+            for (int j = 0; j < CB; ++j) {
+                lv[j] = -INFINITY;
+                ov[j] = 0.0f;
+                if (c0 + j < nc) {
+                    const size_t s = ((size_t)(base + c0 + j) * P.hkv + hk) * G + g;
+                    lv[j] = ld_partial<COHERENT>(P.partial_lse + s);
+                    ov[j] = ld_partial<COHERENT>(P.partial_o + s * D + d);
+                }
             }
-            O = O / L;
-            lse = M + logf(L);
+            float Mb = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < CB; ++j) Mb = fmaxf(Mb, lv[j]);
+            if (Mb == -INFINITY) continue;
+            const float Mn = fmaxf(M, Mb);
+            const float a = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((M - Mn) * kLog2e);
+            L *= a;
+            O *= a;
+#pragma unroll
+            for (int j = 0; j < CB; ++j) {
+                const float wgt = lv[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((lv[j] - Mn) * kLog2e);
+                L += wgt;
+                O = fmaf(wgt, ov[j], O);
+            }
+            M = Mn;
         }
-        P.out[((size_t)b * P.hq + h) * D + d] = f32_to_bf16_rne(O);
-        if (d == 0) P.lse[(size_t)b * P.hq + h] = lse;
+        const bool any = L > 0.0f;
+        P.out[((size_t)b * P.hq + h) * D + d] = f32_to_bf16_rne(any ? O / L : 0.0f);
+        if (d == 0) P.lse[(size_t)b * P.hq + h] = any ? M + logf(L) : -INFINITY;
     }
 }
 
@@ -467,8 +498,13 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, uint32_t idx
         O = O / L;
         const float lse = (M + log2f(L)) * kLn2;
         if (split) {
-            P.partial_o[((size_t)slot * G + g) * D + d] = O;
-            if (d == 0) P.partial_lse[(size_t)slot * G + g] = lse;
+            if (P.fused_merge) {
+                st_partial<true>(P.partial_o + ((size_t)slot * G + g) * D + d, O);
+                if (d == 0) st_partial<true>(P.partial_lse + (size_t)slot * G + g, lse);
+            } else {
+                P.partial_o[((size_t)slot * G + g) * D + d] = O;
+                if (d == 0) P.partial_lse[(size_t)slot * G + g] = lse;
+            }
         } else {
             const size_t h = (size_t)hk * G + g;
             P.out[((size_t)b * P.hq + h) * D + d] = f32_to_bf16_rne(O);
@@ -476,10 +512,12 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, uint32_t idx
         }
     }
     if (split && P.fused_merge) {
-        // Last arriver of this (row, KV head) merges all its ranges: every
-        // workgroup publishes its partial (release), counts itself in, and the
-        // one that completes the count reads the others' partials (acquire).
-        __threadfence();
+        // Last arriver of this (row, KV head) merges all its ranges.  Each
+        // thread waits until its coherent partial stores have completed
+        // (s_waitcnt vmcnt(0)), the workgroup then counts itself in with one
+        // atomic, and the workgroup that completes the count reads every
+        // partial with coherent loads issued after it saw the count.
+        __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
         if (tid == 0) {
             const uint32_t old = atomicAdd(&P.arrive[(size_t)b * P.hkv + hk], 1u);
@@ -487,8 +525,7 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, uint32_t idx
         }
         __syncthreads();
         if (sm.last) {
-            __threadfence();
-            merge_row<D, G, kThreads>(P, b, hk, nch, base, tid);
+            merge_row<D, G, kThreads, true>(P, b, hk, nch, base, tid);
             if (tid == 0) atomicExch(&P.arrive[(size_t)b * P.hkv + hk], 0u);
         }
     }
@@ -568,7 +605,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
     if (b < 0 || b >= P.batch) return;
     const int nc = P.n_chunks[b];
     if (nc == 1 || (P.part_off[b] + nc) * P.hkv > P.max_items) return;
-    merge_row<D, G, 256>(P, b, hk, nc, P.part_off[b], threadIdx.x);
+    merge_row<D, G, 256, false>(P, b, hk, nc, P.part_off[b], threadIdx.x);
 }
 
 // Device queue builder: the same bytes as the host builder, from device
@@ -742,6 +779,21 @@ __global__ __launch_bounds__(256) void copy_probe_kernel(u32x4* __restrict__ dst
     for (; i < n; i += stride) dst[i] = src[i];
 }
 
+// Read-only stream: four independent 16-byte loads per thread per step,
+// folded with xor into one word per thread (kept live by the final store).
+__global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* __restrict__ src, size_t n,
+                                                         uint32_t* __restrict__ sink) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (; i + 3 * stride < n; i += 4 * stride) {
+        const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+        acc ^= a ^ b ^ c ^ d;
+    }
+    for (; i < n; i += stride) acc ^= src[i];
+    sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
 __global__ void init_ctrl_kernel(Ctrl* c, uint32_t* arrive, int n_arrive) {
     uint32_t* w = reinterpret_cast<uint32_t*>(c);
     if (blockIdx.x == 0 && threadIdx.x < sizeof(Ctrl) / 4) w[threadIdx.x] = 0u;
@@ -792,6 +844,12 @@ int launch_init_ctrl(Ctrl* ctrl, uint32_t* arrive, int n_arrive, void* stream) {
 int launch_copy_probe(void* dst, const void* src, size_t bytes, int grid, void* stream) {
     hipLaunchKernelGGL(copy_probe_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
                        static_cast<u32x4*>(dst), static_cast<const u32x4*>(src), bytes / 16);
+    return (int)hipGetLastError();
+}
+
+int launch_read_probe(const void* src, size_t bytes, void* sink, int grid, void* stream) {
+    hipLaunchKernelGGL(read_probe_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                       static_cast<const u32x4*>(src), bytes / 16, static_cast<uint32_t*>(sink));
     return (int)hipGetLastError();
 }
 

@@ -106,6 +106,7 @@ SIGNATURES = {
                                      C.c_void_p, C.c_void_p, C.c_void_p]),
     "pkv_set_trace": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_int32]),
     "pkv_copy_probe": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int32, C.c_void_p]),
+    "pkv_read_probe": (C.c_int32, [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int32, C.c_void_p]),
 }
 
 _LIB = None
@@ -286,6 +287,12 @@ def pkv_set_trace(handle: int, buf=None) -> None:
 def pkv_copy_probe(dst, src, nbytes: int, grid: int = 0, stream=None) -> None:
     _check(lib().pkv_copy_probe(C.c_void_p(dst.data_ptr()), C.c_void_p(src.data_ptr()), int(nbytes),
                                 int(grid), C.c_void_p(_stream_ptr(stream))), "pkv_copy_probe")
+
+
+def pkv_read_probe(src, nbytes: int, sink, grid: int = 0, stream=None) -> None:
+    """sink: a device int32 tensor of at least grid * 256 elements."""
+    _check(lib().pkv_read_probe(C.c_void_p(src.data_ptr()), int(nbytes), C.c_void_p(sink.data_ptr()),
+                                int(grid), C.c_void_p(_stream_ptr(stream))), "pkv_read_probe")
 
 
 class PagedDecoder:

@@ -343,3 +343,25 @@ def test_generator_identical_on_cpu_and_gpu():
     a = workloads.normal_bf16_bits(7, "t", idx)
     b = workloads.normal_bf16_bits(7, "t", idx.cuda()).cpu()
     assert torch.equal(a, b)
+
+
+def test_fused_merge_bitwise_equals_separate_merge_over_repeats():
+    """Both merge modes run the same merge arithmetic; only how partial
+    states travel differs (coherent atomics inside one launch vs a kernel
+    boundary).  Their outputs must agree bit for bit on every call."""
+    wl = workloads.custom("fused_vs_sep", [70000, 4096 * 3 + 5, 9000, 1], 32, 8, 128, spare_pages=3)
+    a = Run(wl, policy=pkv.PKV_POLICY_SPLIT, kv_chunk_tokens=2048, merge_mode=pkv.PKV_MERGE_FUSED)
+    b = Run(wl, policy=pkv.PKV_POLICY_SPLIT, kv_chunk_tokens=2048, merge_mode=pkv.PKV_MERGE_SEPARATE)
+    ob, lb = b.decode()
+    ro, rl = oracle_full(wl)
+    check(ob, lb, ro, rl, "separate merge")
+    a.dec.build_queue(wl.ctx_lens)
+    for i in range(25):
+        a.out.fill_(float("nan"))
+        pkv.pkv_decode(a.dec.handle, a.tensors(), a.dec.stream)
+        torch.cuda.synchronize()
+        assert torch.equal(a.out.view(torch.int16), b.out.view(torch.int16)), f"call {i}"
+        assert torch.equal(a.lse.view(torch.int32), b.lse.view(torch.int32)), f"call {i}"
+    assert a.dec.query()["error_code"] == 0
+    a.close()
+    b.close()
