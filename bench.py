@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--merge", default="fused", choices=["fused", "separate"])
     ap.add_argument("--copies", type=int, default=2)
     ap.add_argument("--no-gate", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="for hardware-counter runs: a few untimed decode steps of the workload, "
+                         "then a 1 GiB copy probe of known size (the counter reference)")
     return ap.parse_args()
 
 
@@ -142,6 +145,24 @@ def measure(torch, pkv, workloads, name, steps, warmup, order, wg_per_cu, copies
     return res, wl
 
 
+def measured_traffic(root):
+    """HBM bytes per decode launch from the committed counter summary, if it
+    was taken on the kernel source as it is now (else None)."""
+    import hashlib
+    import re
+    prof = os.path.join(root, "profiles", "decode_kernel_long_context_traffic.md")
+    src = os.path.join(root, "paged_kv_attention_persistent_amd", "csrc", "pkv_kernels.hip")
+    try:
+        text = open(prof).read()
+        rec = json.loads(re.search(r"```json\n(.*?)\n```", text, re.S).group(1))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except Exception:
+        return None
+    if rec.get("source_sha256_prefix") != sha:
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(workloads, wl, seconds, say):
     """The oracle as it stands, on whole (sequence, KV head) units of the same
     workload, for about `seconds` of CPU time."""
@@ -177,6 +198,41 @@ def cpu_baseline(workloads, wl, seconds, say):
                       f"on the host and excluded from the time"}
 
 
+def profile_pass(torch, pkv, workloads, args, say):
+    """Untimed work for rocprofv3 counter passes: `steps` decode calls of the
+    workload (alternating two pool copies), then one copy probe moving
+    exactly 1 GiB (read 1 GiB, write 1 GiB), whose counter readings give the
+    scale from counter units to bytes."""
+    wl = workloads.CONFIGS[args.workload]()
+    dev = "cuda"
+    q = wl.q(dev)
+    pools = [(wl.pool("k", dev, False), wl.pool("v", dev, False)) for _ in range(2)]
+    bt, lens = wl.block_table_t(dev), wl.ctx_lens_t(dev)
+    out = torch.empty(wl.batch, wl.num_q_heads, wl.head_dim, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(wl.batch, wl.num_q_heads, dtype=torch.float32, device=dev)
+    cfg = pkv.make_config(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages, wl.batch,
+                          wl.max_pages_per_seq, scale=wl.scale,
+                          merge_mode=pkv.PKV_MERGE_SEPARATE if args.merge == "separate" else pkv.PKV_MERGE_FUSED)
+    dec = pkv.PagedDecoder(cfg)
+    info = dec.build_queue(wl.ctx_lens)
+    tens = [pkv.make_tensors(q, k, v, bt, lens, out, lse) for k, v in pools]
+    steps = min(args.steps, 20)
+    for i in range(steps):
+        pkv.pkv_decode(dec.handle, tens[i % 2], dec.stream)
+    torch.cuda.synchronize()
+    dec.query()
+    dec.close()
+    del pools, tens
+    torch.cuda.empty_cache()
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    pkv.pkv_copy_probe(dst, src, n)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_pass": args.workload, "decode_steps": steps,
+                      "kv_bytes_per_step": info.kv_bytes, "copy_probe_bytes": n}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -193,6 +249,9 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     pkv.lib()
+    if args.profile_pass:
+        profile_pass(torch, pkv, workloads, args, say)
+        return
     main_res, wl = measure(torch, pkv, workloads, args.workload, args.steps, args.warmup,
                            args.order, args.wg_per_cu, args.copies, not args.no_gate, say, args.merge)
     say(f"{args.workload}: {main_res['gbs']:.1f} GB/s per step, decode kernel "
@@ -232,7 +291,9 @@ def main():
                   {"workload": args.workload, "items": main_res["items"],
                    "kv_bytes_per_step": main_res["kv_bytes"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__)))
+                     if args.workload == "long" else None,
                      "kernel": "decode_kernel<128,4>",
                      "decode_us_mean": round(main_res["decode_ms_mean"] * 1e3, 3)},
         "cpu_baseline": cpu,

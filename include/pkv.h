@@ -224,8 +224,8 @@ PKV_API pkv_status pkv_copy_probe(void* dst, const void* src, size_t bytes, int3
                                   void* stream);
 
 /* Streaming read of `bytes` (a multiple of 16) from src by `grid`
- * workgroups (0 -> 4 per CU) of 256 threads, four independent dwordx4 loads
- * per thread per step; each thread stores one xor-folded word to sink
+ * workgroups (0 -> 4 per CU) of 256 threads, four independent non-temporal
+ * dwordx4 loads per thread per step; each thread stores one xor-folded word to sink
  * (uint32 [grid * 256]).  Measures the HBM read ceiling. */
 PKV_API pkv_status pkv_read_probe(const void* src, size_t bytes, void* sink, int32_t grid,
                                   void* stream);
