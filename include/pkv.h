@@ -109,7 +109,10 @@ typedef struct pkv_config {
     int32_t max_items;          /* queue capacity; 0 -> bound from the shape */
     int32_t wg_per_cu;          /* persistent grid = CUs * wg_per_cu; 0 -> 1 */
     int32_t merge_mode;         /* PKV_MERGE_* */
-    int32_t reserved[8];        /* must be zero */
+    int32_t persistent;         /* 0: one launch per pkv_decode; 1: resident loop (below) */
+    int32_t num_layers;         /* resident loop: layers per step (0 -> 1) */
+    int32_t timeout_ms;         /* resident loop: wait limit, device and host (0 -> 10000) */
+    int32_t reserved[5];        /* must be zero */
 } pkv_config;
 
 typedef struct pkv_tensors {
@@ -123,6 +126,10 @@ typedef struct pkv_tensors {
     float* lse;                 /* fp32 [B][Hq] */
     int32_t batch;              /* B: must equal the batch of the built queue */
     int32_t block_table_stride; /* elements per block-table row; 0 -> max_pages_per_seq */
+    /* Resident loop with num_layers > 1: element distance between layer l and
+     * l + 1 of q, of each pool, of the block table, of out and of lse (the
+     * same queue serves every layer).  Ignored when num_layers is 1. */
+    int64_t layer_stride_q, layer_stride_kv, layer_stride_bt, layer_stride_out, layer_stride_lse;
 } pkv_tensors;
 
 typedef struct pkv_queue_info {
@@ -147,6 +154,10 @@ typedef struct pkv_runtime_info {
     uint32_t decode_calls;      /* pkv_decode calls since create */
     int32_t grid;               /* persistent workgroups per decode launch */
     int32_t num_cus;            /* CUs of the device */
+    uint32_t loop_out_epoch;    /* resident loop: last completed step (0 before the first) */
+    uint32_t loop_alive;        /* resident loop: 1 while the kernel runs */
+    uint32_t loop_exit_reason;  /* 0 running, 1 exit flag, 2 idle timeout, 3 wait timeout */
+    uint32_t loop_steps_started;
 } pkv_runtime_info;
 
 /* Workspace regions (byte offsets into the caller's workspace), so that a
@@ -160,9 +171,11 @@ typedef struct pkv_layout {
     uint64_t merge_rows_off;    /* int32 [max_batch] */
     uint64_t items_off;         /* 16-byte items [max_items]: u32 seq, u16 kv_head,
                                    u16 chunk, u32 tok_begin, u32 tok_end */
-    uint64_t partial_o_off;     /* fp32 [max_items][G][D], normalised partial outputs */
-    uint64_t partial_lse_off;   /* fp32 [max_items][G], natural-log partial LSE */
-    uint64_t arrive_off;        /* uint32 [max_batch][Hkv] arrival counters of the fused merge */
+    uint64_t partial_o_off;     /* fp32 [layers][max_items][G][D], normalised partial outputs */
+    uint64_t partial_lse_off;   /* fp32 [layers][max_items][G], natural-log partial LSE */
+    uint64_t arrive_off;        /* uint32 [layers][max_batch][Hkv] arrival counters of the fused merge */
+    uint64_t loop_off;          /* resident loop: control mirror and two slots of step counters */
+    uint64_t loop_mirror_off;   /* resident loop: device copies of the two host queue slots */
     uint64_t total_bytes;
     int32_t max_items;
     int32_t reserved;
@@ -175,6 +188,21 @@ PKV_API pkv_status pkv_workspace_size(const pkv_config* cfg, size_t* bytes);
 
 /* Workspace layout of a config (pure host computation). */
 PKV_API pkv_status pkv_workspace_layout(const pkv_config* cfg, pkv_layout* layout);
+
+/* Resident loop (persistent = 1).  pkv_create launches one resident kernel on
+ * `stream` (one workgroup per CU, for the handle's lifetime); no kernel is
+ * launched per step after that.  Per step the caller runs pkv_build_queue
+ * (host planning into a host-memory queue slot; two slots alternate) and
+ * pkv_decode, which writes the step descriptor, publishes the step's epoch
+ * with a release store to a control record in host memory, and blocks until
+ * the kernel publishes the same epoch back (or the timeout: PKV_ERR_TIMEOUT).
+ * The kernel drains the step's queue once per layer in layer order; layer
+ * l + 1 of a row starts after every item of layer l of that row finished.
+ * Outputs are stored system-coherently, so they are readable when pkv_decode
+ * returns.  pkv_destroy raises the exit flag and waits for the kernel.  This
+ * is the "publish the input, wait for the output" boundary of the Wave
+ * Persistent Kernel note ("What a persistent kernel is", "Runtime and timing
+ * boundary"); the host cannot run other kernels on the CUs meanwhile. */
 
 /* Create a handle on the current HIP device.  workspace: device memory of at
  * least pkv_workspace_size bytes, 256-byte aligned, owned by the caller and

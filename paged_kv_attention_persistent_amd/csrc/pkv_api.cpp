@@ -10,7 +10,9 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <chrono>
 #include <string>
+#include <thread>
 
 #include "pkv_internal.h"
 
@@ -42,6 +44,14 @@ struct pkv_handle {
     hipEvent_t ev_after = nullptr;
     uint64_t* trace = nullptr;
     int32_t trace_cap = 0;
+    // resident loop
+    LoopCtrl* lctrl = nullptr;          // host view (fine-grained, mapped)
+    LoopCtrl* lctrl_dev = nullptr;
+    unsigned char* slots = nullptr;     // two host queue slots (fine-grained, mapped)
+    unsigned char* slots_dev = nullptr;
+    uint64_t slot_bytes = 0;
+    uint32_t epoch = 0;                 // last published step
+    bool loop_running = false;
     std::string last_error;
 };
 
@@ -78,6 +88,11 @@ DecodeParams make_params(const pkv_handle* h, const pkv_tensors* t) {
     p.arrive = reinterpret_cast<uint32_t*>(h->ws + h->lay.arrive_off);
     p.trace = h->trace;
     p.trace_cap = h->trace_cap;
+    p.head = &reinterpret_cast<Ctrl*>(h->ws + h->lay.ctrl_off)->head;
+    p.head_dim = h->r.d;
+    p.coherent_out = 0;
+    p.static_first = 1;
+    p.coherent_in = 0;
     p.host_error = h->host_err_dev;
     p.batch = t ? t->batch : 0;
     p.bt_stride = (t && t->block_table_stride) ? t->block_table_stride : h->r.max_pages_per_seq;
@@ -89,6 +104,110 @@ DecodeParams make_params(const pkv_handle* h, const pkv_tensors* t) {
     p.fused_merge = h->r.merge_mode == PKV_MERGE_FUSED ? 1 : 0;
     p.scale_log2 = h->r.scale * 1.44269504088896340736f;
     return p;
+}
+
+// Offset of the queue region inside a host slot (after the step descriptor).
+constexpr uint64_t kSlotQueue = sizeof(LoopDesc);
+
+unsigned char* slot_queue(pkv_handle* h, uint32_t epoch) {
+    return h->slots + (uint64_t)(epoch & 1u) * h->slot_bytes + kSlotQueue;
+}
+
+pkv_status start_loop(pkv_handle* h) {
+    h->slot_bytes = loop_slot_bytes(h->r, h->lay);
+    hipError_t e;
+    if ((e = hipHostMalloc((void**)&h->lctrl, sizeof(LoopCtrl), hipHostMallocMapped | hipHostMallocCoherent)) != hipSuccess ||
+        (e = hipHostGetDevicePointer((void**)&h->lctrl_dev, h->lctrl, 0)) != hipSuccess ||
+        (e = hipHostMalloc((void**)&h->slots, 2 * h->slot_bytes, hipHostMallocMapped | hipHostMallocCoherent)) != hipSuccess ||
+        (e = hipHostGetDevicePointer((void**)&h->slots_dev, h->slots, 0)) != hipSuccess)
+        return hip_fail(h, e, "loop host memory");
+    memset(h->lctrl, 0, sizeof(LoopCtrl));
+    memset(h->slots, 0, 2 * h->slot_bytes);
+    LoopParams lp;
+    memset(&lp, 0, sizeof(lp));
+    lp.base = make_params(h, nullptr);
+    lp.base.coherent_out = 1;
+    lp.base.static_first = 0;
+    lp.base.fused_merge = 1;           // the loop merges split rows inside the kernel
+    lp.base.coherent_in = 1;           // q / block tables may change between steps
+    lp.lctrl = h->lctrl_dev;
+    lp.slots = h->slots_dev;
+    lp.slot_bytes = h->slot_bytes;
+    lp.q_hdr_off = kSlotQueue;
+    lp.q_nch_off = kSlotQueue + (h->lay.n_chunks_off - h->lay.queue_off);
+    lp.q_poff_off = kSlotQueue + (h->lay.part_off_off - h->lay.queue_off);
+    lp.q_mrows_off = kSlotQueue + (h->lay.merge_rows_off - h->lay.queue_off);
+    lp.q_items_off = kSlotQueue + (h->lay.items_off - h->lay.queue_off);
+    lp.lglobal = reinterpret_cast<LoopGlobal*>(h->ws + h->lay.loop_off);
+    lp.mirror = h->ws + h->lay.loop_mirror_off;
+    lp.counters = h->ws + h->lay.loop_off + sizeof(LoopGlobal);
+    lp.counter_bytes = loop_counter_bytes(h->r);
+    lp.partial_o_layer = (uint64_t)h->r.max_items * h->r.g * h->r.d;
+    lp.partial_lse_layer = (uint64_t)h->r.max_items * h->r.g;
+    lp.arrive_layer = (uint64_t)h->r.max_batch * h->r.hkv;
+    int clock_khz = 0;
+    if ((e = hipDeviceGetAttribute(&clock_khz, hipDeviceAttributeWallClockRate, h->device)) != hipSuccess ||
+        clock_khz <= 0)
+        clock_khz = 100000;                                          // 100 MHz, the CDNA wall clock
+    lp.timeout_ticks = (uint64_t)h->r.timeout_ms * (uint64_t)clock_khz;
+    lp.max_batch = h->r.max_batch;
+    int rc = launch_resident(lp, h->r.d, h->r.g, h->grid, h->stream);
+    if (rc != 0) return hip_fail(h, (hipError_t)rc, "resident launch");
+    h->loop_running = true;
+    return PKV_OK;
+}
+
+void stop_loop(pkv_handle* h) {
+    if (h->loop_running) {
+        __atomic_store_n(&h->lctrl->exit_flag, 1u, __ATOMIC_RELEASE);
+        (void)hipStreamSynchronize(h->stream);
+        h->loop_running = false;
+    }
+    if (h->slots) (void)hipHostFree(h->slots);
+    if (h->lctrl) (void)hipHostFree(h->lctrl);
+    h->slots = nullptr;
+    h->lctrl = nullptr;
+}
+
+pkv_status decode_loop(pkv_handle* h, const pkv_tensors* t) {
+    if (!h->loop_running) return fail(h, PKV_ERR_STATE, "resident loop not running");
+    if (__atomic_load_n(&h->lctrl->alive, __ATOMIC_ACQUIRE) == 0 &&
+        __atomic_load_n(&h->lctrl->exit_reason, __ATOMIC_ACQUIRE) != 0)
+        return fail(h, PKV_ERR_TIMEOUT, "resident kernel has exited (idle or wait limit)");
+    const uint32_t e = h->epoch + 1;
+    LoopDesc* d = reinterpret_cast<LoopDesc*>(h->slots + (uint64_t)(e & 1u) * h->slot_bytes);
+    d->q = static_cast<const uint16_t*>(t->q);
+    d->k_pool = static_cast<const uint16_t*>(t->k_pool);
+    d->v_pool = static_cast<const uint16_t*>(t->v_pool);
+    d->block_table = t->block_table;
+    d->out = static_cast<uint16_t*>(t->out);
+    d->lse = t->lse;
+    const bool layered = h->r.num_layers > 1;
+    d->ls_q = layered ? t->layer_stride_q : 0;
+    d->ls_kv = layered ? t->layer_stride_kv : 0;
+    d->ls_bt = layered ? t->layer_stride_bt : 0;
+    d->ls_out = layered ? t->layer_stride_out : 0;
+    d->ls_lse = layered ? t->layer_stride_lse : 0;
+    d->batch = t->batch;
+    d->bt_stride = t->block_table_stride ? t->block_table_stride : h->r.max_pages_per_seq;
+    d->n_layers = h->r.num_layers;
+    d->epoch = e;
+    __atomic_store_n(&h->lctrl->in_epoch, e, __ATOMIC_RELEASE);     // publish the step
+    h->epoch = e;
+    const auto t0 = std::chrono::steady_clock::now();
+    const auto limit = std::chrono::milliseconds(h->r.timeout_ms);
+    uint32_t spins = 0;
+    while (__atomic_load_n(&h->lctrl->out_epoch, __ATOMIC_ACQUIRE) != e) {
+        if (__atomic_load_n(h->host_err, __ATOMIC_ACQUIRE) != 0)
+            return fail(h, PKV_ERR_DEVICE_FAULT, "device error word set (see pkv_query)");
+        if ((++spins & 1023u) == 0) {
+            if (std::chrono::steady_clock::now() - t0 > limit)
+                return fail(h, PKV_ERR_TIMEOUT, "step not completed within timeout_ms");
+            if (__atomic_load_n(&h->lctrl->exit_reason, __ATOMIC_ACQUIRE) != 0)
+                return fail(h, PKV_ERR_TIMEOUT, "resident kernel left the loop");
+        }
+    }
+    return PKV_OK;
 }
 
 pkv_status check_tensors(pkv_handle* h, const pkv_tensors* t) {
@@ -198,7 +317,9 @@ PKV_API pkv_status pkv_create(const pkv_config* cfg, void* workspace, size_t wor
     memset(h->host_err, 0, 64);
     int rc = launch_init_ctrl(reinterpret_cast<Ctrl*>(h->ws + h->lay.ctrl_off),
                               reinterpret_cast<uint32_t*>(h->ws + h->lay.arrive_off),
-                              h->r.max_batch * h->r.hkv, h->stream);
+                              h->r.max_batch * h->r.hkv * h->r.num_layers, h->stream);
+    if (rc == 0 && h->r.persistent)
+        rc = launch_zero(h->ws + h->lay.loop_off, sizeof(LoopGlobal) + 2 * loop_counter_bytes(h->r), h->stream);
     if (rc != 0) { pkv_destroy(h); return PKV_ERR_HIP; }
     // an empty queue until the first build
     QHdr* qh = reinterpret_cast<QHdr*>(h->staging[0]);
@@ -209,6 +330,10 @@ PKV_API pkv_status pkv_create(const pkv_config* cfg, void* workspace, size_t wor
     if (e != hipSuccess) { pkv_destroy(h); return PKV_ERR_HIP; }
     h->staging_pending[0] = true;
     h->staging_next = 1;
+    if (h->r.persistent) {
+        s = start_loop(h);
+        if (s != PKV_OK) { pkv_destroy(h); return s; }
+    }
     *out = h;
     return PKV_OK;
 }
@@ -218,6 +343,25 @@ PKV_API pkv_status pkv_build_queue(pkv_handle* h, const int32_t* ctx_lens_host, 
     if (!h) return PKV_ERR_INVALID_ARG;
     if (batch < 0 || batch > h->r.max_batch) return fail(h, PKV_ERR_CAPACITY, "batch outside [0, max_batch]");
     if (batch > 0 && !ctx_lens_host) return fail(h, PKV_ERR_INVALID_ARG, "null ctx_lens");
+    if (h->r.persistent) {
+        unsigned char* st = slot_queue(h, h->epoch + 1);
+        const uint64_t q0 = h->lay.queue_off;
+        pkv_queue_info qi;
+        const char* why;
+        pkv_status s = plan_queue(h->r, ctx_lens_host, batch, reinterpret_cast<QHdr*>(st),
+                                  reinterpret_cast<int32_t*>(st + (h->lay.n_chunks_off - q0)),
+                                  reinterpret_cast<int32_t*>(st + (h->lay.part_off_off - q0)),
+                                  reinterpret_cast<int32_t*>(st + (h->lay.merge_rows_off - q0)),
+                                  reinterpret_cast<Item*>(st + (h->lay.items_off - q0)), h->r.max_items, &qi, &why);
+        if (s != PKV_OK) return fail(h, s, why);
+        qi.launches_per_step = 0;             // nothing is launched per step
+        h->built = true;
+        h->built_on_device = false;
+        h->batch = batch;
+        h->qinfo = qi;
+        if (info) *info = qi;
+        return PKV_OK;
+    }
     const int i = h->staging_next;
     hipError_t e;
     if (h->staging_pending[i]) {          // the previous upload from this buffer must have left
@@ -259,6 +403,7 @@ PKV_API pkv_status pkv_build_queue_device(pkv_handle* h, const int32_t* ctx_lens
     if (batch > 0 && (!ctx_lens_device || !aligned(ctx_lens_device, 4)))
         return fail(h, PKV_ERR_INVALID_ARG, "null or misaligned ctx_lens");
     if (h->r.order != PKV_ORDER_CANONICAL) return fail(h, PKV_ERR_UNSUPPORTED, "device builder: canonical order only");
+    if (h->r.persistent) return fail(h, PKV_ERR_STATE, "the resident loop takes host-built queues");
     BuildParams p;
     memset(&p, 0, sizeof(p));
     p.ctx_lens = ctx_lens_device;
@@ -298,6 +443,13 @@ PKV_API pkv_status pkv_decode(pkv_handle* h, const pkv_tensors* t, void* stream)
     if (t->batch != h->batch) return fail(h, PKV_ERR_INVALID_ARG, "batch differs from the built queue");
     if (__atomic_load_n(h->host_err, __ATOMIC_ACQUIRE) != 0)
         return fail(h, PKV_ERR_DEVICE_FAULT, "device error word set (see pkv_query)");
+    if (h->r.persistent) {
+        if (h->r.num_layers > 1 && (t->layer_stride_q <= 0 || t->layer_stride_kv <= 0 ||
+                                    t->layer_stride_bt <= 0 || t->layer_stride_out <= 0 ||
+                                    t->layer_stride_lse <= 0))
+            return fail(h, PKV_ERR_INVALID_ARG, "layered tensors need positive layer strides");
+        return decode_loop(h, t);
+    }
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (st != h->stream && (e = hipStreamWaitEvent(st, h->upload_evt, 0)) != hipSuccess)
@@ -361,6 +513,19 @@ PKV_API pkv_status pkv_read_probe(const void* src, size_t bytes, void* sink, int
 
 PKV_API pkv_status pkv_query(pkv_handle* h, pkv_runtime_info* info) {
     if (!h || !info) return PKV_ERR_INVALID_ARG;
+    if (h->loop_running) {               // the resident kernel never idles: read host words only
+        memset(info, 0, sizeof(*info));
+        info->error_code = __atomic_load_n(h->host_err, __ATOMIC_ACQUIRE);
+        info->grid = h->grid;
+        info->num_cus = h->device_cus;
+        info->n_items = (uint32_t)h->qinfo.n_items;
+        info->loop_out_epoch = __atomic_load_n(&h->lctrl->out_epoch, __ATOMIC_ACQUIRE);
+        info->loop_alive = __atomic_load_n(&h->lctrl->alive, __ATOMIC_ACQUIRE);
+        info->loop_exit_reason = __atomic_load_n(&h->lctrl->exit_reason, __ATOMIC_ACQUIRE);
+        info->loop_steps_started = __atomic_load_n(&h->lctrl->heartbeat, __ATOMIC_ACQUIRE);
+        if (info->error_code != 0) return fail(h, PKV_ERR_DEVICE_FAULT, "device error word set");
+        return PKV_OK;
+    }
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(h, e, "device sync");
     Ctrl c;
@@ -384,6 +549,7 @@ PKV_API pkv_status pkv_query(pkv_handle* h, pkv_runtime_info* info) {
 
 PKV_API pkv_status pkv_clear_error(pkv_handle* h) {
     if (!h) return PKV_ERR_INVALID_ARG;
+    if (h->loop_running) return fail(h, PKV_ERR_STATE, "clear errors after pkv_destroy of a resident loop");
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(h, e, "device sync");
     const uint32_t z[2] = {0u, 0u};
@@ -397,6 +563,7 @@ PKV_API pkv_status pkv_debug_gather(pkv_handle* h, const pkv_tensors* t, int32_t
                                     void* k_out, void* v_out, void* stream) {
     if (!h) return PKV_ERR_INVALID_ARG;
     if (!h->built) return fail(h, PKV_ERR_STATE, "pkv_debug_gather before pkv_build_queue");
+    if (h->r.persistent) return fail(h, PKV_ERR_STATE, "pkv_debug_gather needs a one-shot handle");
     pkv_status s = check_tensors(h, t);
     if (s != PKV_OK) return s;
     if (!k_out || !v_out || !aligned(k_out, 16) || !aligned(v_out, 16))
@@ -415,6 +582,7 @@ PKV_API pkv_status pkv_debug_gather(pkv_handle* h, const pkv_tensors* t, int32_t
 
 PKV_API pkv_status pkv_destroy(pkv_handle* h) {
     if (!h) return PKV_ERR_INVALID_ARG;
+    stop_loop(h);
     if (h->stream || h->staging[0]) (void)hipStreamSynchronize(h->stream);
     for (int i = 0; i < 2; ++i) {
         if (h->staging_evt[i]) (void)hipEventDestroy(h->staging_evt[i]);

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <stddef.h>
+#include <cstddef>
 #include <stdint.h>
 
 #include "../../include/pkv.h"
@@ -50,15 +51,69 @@ static_assert(sizeof(QHdr) == 256, "queue header is 256 bytes");
 
 inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
+// Resident-loop control record, in fine-grained (coherent) host memory.
+// The host writes in_epoch / exit_flag; the device writes the rest.  The two
+// directions sit in different 64-byte lines.
+struct LoopCtrl {
+    uint32_t in_epoch;          // step the host has published
+    uint32_t exit_flag;         // 1: leave the loop
+    uint32_t pad0[14];
+    uint32_t out_epoch;         // last step the device completed
+    uint32_t alive;             // 1 while the resident kernel runs
+    uint32_t exit_reason;       // 0 running, 1 exit flag seen, 2 idle timeout, 3 wait timeout
+    uint32_t heartbeat;         // steps started
+    uint32_t pad1[12];
+};
+static_assert(sizeof(LoopCtrl) == 128, "loop ctrl is two 64-byte lines");
+
+// Per-step descriptor at the start of each host queue slot.
+struct LoopDesc {
+    const uint16_t* q;
+    const uint16_t* k_pool;
+    const uint16_t* v_pool;
+    const int32_t* block_table;
+    uint16_t* out;
+    float* lse;
+    int64_t ls_q, ls_kv, ls_bt, ls_out, ls_lse;   // layer strides, elements
+    int32_t batch;
+    int32_t bt_stride;
+    int32_t n_layers;
+    uint32_t epoch;
+    int32_t pad[38];
+};
+static_assert(sizeof(LoopDesc) == 256, "loop descriptor is 256 bytes");
+static_assert(offsetof(LoopDesc, batch) == 88 && offsetof(LoopDesc, bt_stride) == 92 &&
+              offsetof(LoopDesc, n_layers) == 96, "loop descriptor words read as 64-bit pairs");
+static_assert(offsetof(QHdr, n_merge_rows) == 4, "queue header words read as one 64-bit pair");
+
+// Device-memory mirror of the host control words, written by workgroup 0
+// (the only workgroup that polls host memory) and polled by the others.
+struct LoopGlobal {
+    uint32_t dev_epoch;         // last step workgroup 0 saw published
+    uint32_t dev_exit;          // nonzero: leave the loop (1 exit flag, 2 idle limit)
+    uint32_t pad[62];
+};
+
+// Device-memory counters of one slot of the resident loop.
+struct LoopSlotCtr {
+    uint32_t head;              // pop counter
+    uint32_t step_done;         // completed work units of the step
+    uint32_t pad[62];
+    // followed by uint32 done[max_batch]: completed items per row
+};
+
 // Resolved configuration: defaults filled in, checked.
 struct Resolved {
     int hq, hkv, g, d, page, num_pages, max_batch, max_pages_per_seq;
     float scale;
     int policy, order, chunk, num_cus, max_items, wg_per_cu, merge_mode;
+    int persistent, num_layers, timeout_ms;
 };
 
 pkv_status resolve_config(const pkv_config* cfg, int device_cus, Resolved* r, const char** why);
 void compute_layout(const Resolved& r, pkv_layout* lay);
+uint64_t loop_counter_bytes(const Resolved& r);
+uint64_t loop_slot_bytes(const Resolved& r, const pkv_layout& lay);
 
 // Host queue planner.  Writes the queue header, n_chunks, part_off, merge_rows
 // and items into the caller's arrays.  Returns PKV_OK or an error.
@@ -84,7 +139,12 @@ struct DecodeParams {
     float* partial_lse;
     uint32_t* arrive;           // [max_batch][Hkv] arrival counters (fused merge)
     uint64_t* trace;            // per-item trace records (nullable)
+    uint32_t* head;             // pop counter of this queue
     int32_t trace_cap;
+    int32_t head_dim;
+    int32_t coherent_out;       // 1: outputs stored system-coherently (resident loop)
+    int32_t static_first;       // 1: first round static (one-shot), 0: all pops (resident loop)
+    int32_t coherent_in;        // 1: q and block-table entries read with coherent loads
     uint32_t* host_error;       // mapped host word mirrored on device faults (nullable)
     int32_t batch;
     int32_t bt_stride;
@@ -95,6 +155,26 @@ struct DecodeParams {
     int32_t max_items;          // capacity of items and partial slots
     int32_t fused_merge;        // 1: last arriver merges inside the decode kernel
     float scale_log2;           // scale * log2(e)
+};
+
+// Resident-loop kernel parameters: the per-step constant part of the decode
+// parameters plus where the control record, the host queue slots and the
+// loop counters live.
+struct LoopParams {
+    DecodeParams base;          // ctrl, partials, arrive, head_dim, hq, hkv, ...
+    LoopCtrl* lctrl;            // device view of the host control record
+    unsigned char* slots;       // device view of the two host queue slots
+    uint64_t slot_bytes;
+    uint64_t q_hdr_off, q_nch_off, q_poff_off, q_mrows_off, q_items_off;  // within a slot
+    LoopGlobal* lglobal;        // device mirror of the control words
+    unsigned char* mirror;      // device copies of the two host slots (same layout)
+    unsigned char* counters;    // LoopSlotCtr + done[max_batch], two slots
+    uint64_t counter_bytes;     // per slot
+    uint64_t partial_o_layer;   // elements per layer of partial_o
+    uint64_t partial_lse_layer;
+    uint64_t arrive_layer;
+    uint64_t timeout_ticks;     // 100 MHz wall-clock ticks
+    int32_t max_batch;
 };
 
 struct BuildParams {
@@ -117,6 +197,7 @@ struct BuildParams {
 
 // Launch wrappers (pkv_kernels.hip).  Return a hipError_t as int.
 int launch_init_ctrl(Ctrl* ctrl, uint32_t* arrive, int n_arrive, void* stream);
+int launch_zero(void* p, size_t bytes, void* stream);
 int launch_decode(const DecodeParams& p, int head_dim, int group, int grid, void* stream);
 int launch_merge(const DecodeParams& p, int head_dim, int group, int n_rows, void* stream);
 int launch_build_queue(const BuildParams& p, void* stream);
@@ -125,5 +206,6 @@ int launch_debug_gather(const DecodeParams& p, int head_dim, int item_index, uin
 bool supported_shape(int head_dim, int group);
 int launch_copy_probe(void* dst, const void* src, size_t bytes, int grid, void* stream);
 int launch_read_probe(const void* src, size_t bytes, void* sink, int grid, void* stream);
+int launch_resident(const LoopParams& lp, int head_dim, int group, int grid, void* stream);
 
 }  // namespace pkv

@@ -332,29 +332,50 @@ __device__ __forceinline__ void st_partial(float* p, float v) {
     else *p = v;
 }
 
+// Final outputs.  Two adjacent bf16 outputs travel as one 32-bit word; in
+// the resident loop they are stored system-coherently (relaxed atomic
+// stores at system scope) so that the host may read them as soon as the step
+// is published, without cache write-backs.
+__device__ __forceinline__ void store_out_pair(const DecodeParams& P, int b, size_t h, int d, float o0,
+                                               float o1) {
+    const uint32_t w = (uint32_t)f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(P.out + ((size_t)b * P.hq + h) * P.head_dim + d);
+    if (P.coherent_out) __hip_atomic_store(dst, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    else *dst = w;
+}
+
+__device__ __forceinline__ void store_lse(const DecodeParams& P, int b, size_t h, float v) {
+    float* dst = P.lse + (size_t)b * P.hq + h;
+    if (P.coherent_out) __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    else *dst = v;
+}
+
 // Exact merge of the partial states of one split (row, KV head) (PersistentKV
 // page, Methodology 1, "Sequence Splitting"): with M = max_c lse_c and
 // w_c = exp(lse_c - M), O = sum_c w_c o_c / sum_c w_c and
 // LSE = M + ln sum_c w_c.  A row with no ranges gets O = 0, LSE = -inf.
 // Ranges are read 32 at a time, all loads of a block issued together; blocks
 // after the first fold in by rescaling (the same identity, applied twice).
+// Each thread merges two adjacent dims of one head.
 template <int D, int G, int NT, bool COHERENT>
 __device__ void merge_row(const DecodeParams& P, int b, int hk, int nc, int base, int tid) {
     constexpr int CB = 32;
-    for (int t = tid; t < G * D; t += NT) {
-        const int g = t / D, d = t % D;
+    for (int t = tid; t < G * D / 2; t += NT) {
+        const int g = (2 * t) / D, d = (2 * t) % D;
         const size_t h = (size_t)hk * G + g;
-        float M = -INFINITY, L = 0.0f, O = 0.0f;
+        float M = -INFINITY, L = 0.0f, O0 = 0.0f, O1 = 0.0f;
         for (int c0 = 0; c0 < nc; c0 += CB) {
-            float lv[CB], ov[CB];
+            float lv[CB], o0[CB], o1[CB];
 #pragma unroll
             for (int j = 0; j < CB; ++j) {
                 lv[j] = -INFINITY;
-                ov[j] = 0.0f;
+                o0[j] = 0.0f;
+                o1[j] = 0.0f;
                 if (c0 + j < nc) {
                     const size_t s = ((size_t)(base + c0 + j) * P.hkv + hk) * G + g;
                     lv[j] = ld_partial<COHERENT>(P.partial_lse + s);
-                    ov[j] = ld_partial<COHERENT>(P.partial_o + s * D + d);
+                    o0[j] = ld_partial<COHERENT>(P.partial_o + s * D + d);
+                    o1[j] = ld_partial<COHERENT>(P.partial_o + s * D + d + 1);
                 }
             }
             float Mb = -INFINITY;
@@ -364,47 +385,78 @@ __device__ void merge_row(const DecodeParams& P, int b, int hk, int nc, int base
             const float Mn = fmaxf(M, Mb);
             const float a = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((M - Mn) * kLog2e);
             L *= a;
-            O *= a;
+            O0 *= a;
+            O1 *= a;
 #pragma unroll
             for (int j = 0; j < CB; ++j) {
                 const float wgt = lv[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((lv[j] - Mn) * kLog2e);
                 L += wgt;
-                O = fmaf(wgt, ov[j], O);
+                O0 = fmaf(wgt, o0[j], O0);
+                O1 = fmaf(wgt, o1[j], O1);
             }
             M = Mn;
         }
         const bool any = L > 0.0f;
-        P.out[((size_t)b * P.hq + h) * D + d] = f32_to_bf16_rne(any ? O / L : 0.0f);
-        if (d == 0) P.lse[(size_t)b * P.hq + h] = any ? M + logf(L) : -INFINITY;
+        store_out_pair(P, b, h, d, any ? O0 / L : 0.0f, any ? O1 / L : 0.0f);
+        if (d == 0) store_lse(P, b, h, any ? M + logf(L) : -INFINITY);
     }
 }
 
-// Claim the next item for this workgroup: the grid's first round is static
-// (workgroup i runs item i), later items are popped from the shared head.
+// Claim the next item for this workgroup.  One-shot launches run a static
+// first round (workgroup i runs item i) and pop later items past it; the
+// resident loop pops every item (a workgroup claims work only while it runs).
 __device__ __forceinline__ uint32_t pop_next(const DecodeParams& P) {
-    return gridDim.x + atomicAdd(&P.ctrl->head, 1u);
+    return (P.static_first ? gridDim.x : 0u) + atomicAdd(P.head, 1u);
+}
+
+// One queue item, decoded and checked (all fields wave-uniform).
+struct ItemRef {
+    uint32_t idx;
+    int b, hk, chunk;
+    uint32_t tb, te;
+    int nch, base;
+    bool ok;
+};
+
+__device__ __forceinline__ ItemRef read_item(const DecodeParams& P, uint32_t idx) {
+    ItemRef it;
+    it.idx = idx;
+    const Item* itp = P.items + idx;
+    it.b = __builtin_amdgcn_readfirstlane((int)itp->seq);
+    it.hk = __builtin_amdgcn_readfirstlane((int)itp->kv_head);
+    it.chunk = __builtin_amdgcn_readfirstlane((int)itp->chunk);
+    it.tb = (uint32_t)__builtin_amdgcn_readfirstlane((int)itp->tok_begin);
+    it.te = (uint32_t)__builtin_amdgcn_readfirstlane((int)itp->tok_end);
+    it.ok = it.b >= 0 && it.b < P.batch && it.hk < P.hkv && it.tb < it.te &&
+            it.te <= (uint32_t)P.max_tokens && (it.tb % kPageSize) == 0;
+    it.nch = 1;
+    it.base = 0;
+    if (it.ok) {
+        it.nch = __builtin_amdgcn_readfirstlane(P.n_chunks[it.b]);
+        if (it.nch > 1) {
+            it.base = __builtin_amdgcn_readfirstlane(P.part_off[it.b]);
+            const int slot = (it.base + it.chunk) * P.hkv + it.hk;
+            it.ok = it.chunk < it.nch && slot >= 0 && (it.base + it.nch) * P.hkv <= P.max_items;
+        } else {
+            it.ok = it.nch == 1;
+        }
+    }
+    return it;
 }
 
 template <int D, int G>
-__device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, uint32_t idx, uint32_t& nxt) {
+__device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, const ItemRef& it, uint32_t& nxt) {
     constexpr int NPC = D / 64;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane >> 3;
     const int p = lane & 7;
-
-    const Item* itp = P.items + idx;
-    const int b = __builtin_amdgcn_readfirstlane((int)itp->seq);
-    const int hk = __builtin_amdgcn_readfirstlane((int)itp->kv_head);
-    const int chunk = __builtin_amdgcn_readfirstlane((int)itp->chunk);
-    const uint32_t tb = (uint32_t)__builtin_amdgcn_readfirstlane((int)itp->tok_begin);
-    const uint32_t te = (uint32_t)__builtin_amdgcn_readfirstlane((int)itp->tok_end);
-    const bool bad = b < 0 || b >= P.batch || hk >= P.hkv || tb >= te ||
-                     te > (uint32_t)P.max_tokens || (tb % kPageSize) != 0;
-    if (bad) {                                     // uniform over the workgroup
+    const int b = it.b, hk = it.hk;
+    const uint32_t tb = it.tb, te = it.te;
+    if (!it.ok) {                                  // uniform over the workgroup
         if (tid == 0) {
-            report(P.ctrl, P.host_error, PKV_DEVERR_BAD_ITEM, idx);
+            report(P.ctrl, P.host_error, PKV_DEVERR_BAD_ITEM, it.idx);
             nxt = pop_next(P);
         }
         return;
@@ -418,8 +470,17 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, uint32_t idx
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int k = 0; k < NPC; ++k)
-            qv[g][k] = *reinterpret_cast<const u32x4*>(qrow + g * D + (8 * k + p) * 8);
+        for (int k = 0; k < NPC; ++k) {
+            const uint16_t* src = qrow + g * D + (8 * k + p) * 8;
+            if (P.coherent_in) {            // the host may rewrite q between steps
+                const uint64_t* s64 = reinterpret_cast<const uint64_t*>(src);
+                const uint64_t lo = __hip_atomic_load(s64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                const uint64_t hi = __hip_atomic_load(s64 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                qv[g][k] = u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+            } else {
+                qv[g][k] = *reinterpret_cast<const u32x4*>(src);
+            }
+        }
 
     State<D, G> st;
 #pragma unroll
@@ -434,7 +495,13 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, uint32_t idx
     const int32_t* bt_row = P.block_table + (size_t)b * P.bt_stride + first_page + w;
     for (int wb = 0; wb < nw; wb += 64) {
         const int n = nw - wb < 64 ? nw - wb : 64;
-        int32_t btv = lane < n ? bt_row[(size_t)kWaves * (wb + lane)] : 0;
+        int32_t btv = 0;
+        if (lane < n) {
+            const int32_t* e = bt_row + (size_t)kWaves * (wb + lane);
+            btv = P.coherent_in ? (int32_t)__hip_atomic_load(reinterpret_cast<const uint32_t*>(e), __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_SYSTEM)
+                                : *e;
+        }
         const bool badl = lane < n && (uint32_t)btv >= (uint32_t)P.num_pages;
         const unsigned long long badm = __ballot(badl);
         if (badm) {                                   // never read outside the pool
@@ -483,40 +550,40 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, uint32_t idx
     }
     __syncthreads();
 
-    const int nch = P.n_chunks[b];
-    const bool split = nch > 1;
-    const int base = split ? P.part_off[b] : 0;
-    const int slot = split ? (base + chunk) * P.hkv + hk : 0;
-    if (split && (chunk >= nch || slot < 0 || (base + nch) * P.hkv > P.max_items)) {
-        if (tid == 0) report(P.ctrl, P.host_error, PKV_DEVERR_BAD_ITEM, idx);
-        return;                                    // uniform over the workgroup (next already claimed)
-    }
-    for (int t = tid; t < G * D; t += kThreads) {
-        const int g = t / D, d = t % D;
+    // Combine the 8 waves; each thread finishes two adjacent dims of one head.
+    const bool split = it.nch > 1;
+    const int slot = split ? (it.base + it.chunk) * P.hkv + hk : 0;
+    for (int t = tid; t < G * D / 2; t += kThreads) {
+        const int g = (2 * t) / D, d = (2 * t) % D;
         float M = kNegBig;
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm.m[ww][g]);
-        float L = 0.0f, O = 0.0f;
+        float L = 0.0f, O0 = 0.0f, O1 = 0.0f;
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) {
             const float a = __builtin_amdgcn_exp2f(sm.m[ww][g] - M);
             L = fmaf(sm.l[ww][g], a, L);
-            O = fmaf(sm.acc[ww][t], a, O);
+            O0 = fmaf(sm.acc[ww][g * D + d], a, O0);
+            O1 = fmaf(sm.acc[ww][g * D + d + 1], a, O1);
         }
-        O = O / L;
+        O0 = O0 / L;
+        O1 = O1 / L;
         const float lse = (M + log2f(L)) * kLn2;
         if (split) {
+            float* po = P.partial_o + ((size_t)slot * G + g) * D + d;
             if (P.fused_merge) {
-                st_partial<true>(P.partial_o + ((size_t)slot * G + g) * D + d, O);
+                st_partial<true>(po, O0);
+                st_partial<true>(po + 1, O1);
                 if (d == 0) st_partial<true>(P.partial_lse + (size_t)slot * G + g, lse);
             } else {
-                P.partial_o[((size_t)slot * G + g) * D + d] = O;
+                po[0] = O0;
+                po[1] = O1;
                 if (d == 0) P.partial_lse[(size_t)slot * G + g] = lse;
             }
         } else {
             const size_t h = (size_t)hk * G + g;
-            P.out[((size_t)b * P.hq + h) * D + d] = f32_to_bf16_rne(O);
-            if (d == 0) P.lse[(size_t)b * P.hq + h] = lse;
+            store_out_pair(P, b, h, d, O0, O1);
+            if (d == 0) store_lse(P, b, h, lse);
         }
     }
     if (split && P.fused_merge) {
@@ -529,11 +596,11 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, uint32_t idx
         __syncthreads();
         if (tid == 0) {
             const uint32_t old = atomicAdd(&P.arrive[(size_t)b * P.hkv + hk], 1u);
-            sm.last = (old + 1 == (uint32_t)nch) ? 1u : 0u;
+            sm.last = (old + 1 == (uint32_t)it.nch) ? 1u : 0u;
         }
         __syncthreads();
         if (sm.last) {
-            merge_row<D, G, kThreads, true>(P, b, hk, nch, base, tid);
+            merge_row<D, G, kThreads, true>(P, b, hk, it.nch, it.base, tid);
             if (tid == 0) atomicExch(&P.arrive[(size_t)b * P.hkv + hk], 0u);
         }
     }
@@ -551,16 +618,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
         for (int ri = blockIdx.x; ri < n_rows; ri += gridDim.x) {
             const int b = P.merge_rows[ri];
             if (b < 0 || b >= P.batch || P.n_chunks[b] != 0) continue;
-            for (int t = tid; t < P.hq * D; t += kThreads) {
-                P.out[(size_t)b * P.hq * D + t] = 0;
-                if (t % D == 0) P.lse[(size_t)b * P.hq + t / D] = -INFINITY;
+            for (int t = tid; t < P.hq * D / 2; t += kThreads) {
+                const int h = (2 * t) / D, d = (2 * t) % D;
+                store_out_pair(P, b, h, d, 0.0f, 0.0f);
+                if (d == 0) store_lse(P, b, h, -INFINITY);
             }
         }
     }
     uint32_t idx = blockIdx.x;                     // first round: static assignment
     uint32_t done_here = 0;
     if (P.trace && tid == 0 && n_items + blockIdx.x < (uint32_t)P.trace_cap) {
-        // workgroup record after the item records: entry time, first pop returned
+        // workgroup record after the item records: entry time, start of work
         uint64_t* rec = P.trace + 4ull * (n_items + blockIdx.x);
         rec[0] = (uint64_t)blockIdx.x | (1ull << 63) | ((uint64_t)idx << 32);
         rec[1] = t_enter;
@@ -572,7 +640,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
         uint32_t nxt = 0;
         uint64_t t_start = 0;
         if (P.trace) t_start = wall_clock64();
-        process_item<D, G>(P, sm, idx, nxt);
+        process_item<D, G>(P, sm, read_item(P, idx), nxt);
         ++done_here;
         if (P.trace && tid == 0 && idx < (uint32_t)P.trace_cap) {
             const uint64_t t_end = wall_clock64();
@@ -600,6 +668,295 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
             atomicAdd(&ctrl->decode_calls, 1u);
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Resident session loop.  Launched once; it serves steps that the host
+// publishes through an epoch word in host memory, the "publish the input,
+// wait for the output" boundary of a persistent kernel (Wave Persistent
+// Kernel note, "What a persistent kernel is"; the control record of
+// "Runtime and timing boundary").  A step's work is the step's compact queue
+// repeated over the layers, in layer-major order: work unit u is item
+// u mod n_items of layer u / n_items.  Layer l + 1 of a row starts only after
+// every item of layer l of that row has finished, the ordering a layer
+// stack imposes.  Waiting cannot deadlock: every grid workgroup is resident
+// (one per CU), units are claimed in increasing order, and the unfinished
+// unit with the smallest index has all of its predecessors finished.  Every
+// wait has a wall-clock limit, so the kernel always exits.
+
+__device__ __forceinline__ uint32_t ld_sys(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ uint64_t ld_sys64(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ void st_sys(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Wave-uniform copies (scalar registers) of values every lane loaded alike.
+__device__ __forceinline__ uint32_t uni(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
+__device__ __forceinline__ uint64_t uni64(uint64_t x) {
+    return (uint64_t)uni((uint32_t)x) | ((uint64_t)uni((uint32_t)(x >> 32)) << 32);
+}
+__device__ __forceinline__ uint64_t ld_desc64(const void* p) {
+    return uni64(ld_sys64(reinterpret_cast<const uint64_t*>(p)));
+}
+__device__ __forceinline__ uint32_t ld_desc32(const void* p) {
+    return uni(ld_sys(reinterpret_cast<const uint32_t*>(p)));
+}
+
+__device__ __forceinline__ uint32_t ld_agt(const void* p) {
+    return __hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_agt64(const void* p) {
+    return __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Item and row metadata come from the device mirror of the step's queue,
+// rewritten every other step: agent-coherent loads (no stale L2 lines).
+__device__ __forceinline__ ItemRef read_item_mirror(const DecodeParams& P, uint32_t idx) {
+    ItemRef it;
+    it.idx = idx;
+    const uint64_t a = ld_agt64(P.items + idx), b = ld_agt64(reinterpret_cast<const uint64_t*>(P.items + idx) + 1);
+    const uint32_t w0 = (uint32_t)a, w1 = (uint32_t)(a >> 32), w2 = (uint32_t)b, w3 = (uint32_t)(b >> 32);
+    it.b = __builtin_amdgcn_readfirstlane((int)w0);
+    it.hk = __builtin_amdgcn_readfirstlane((int)(w1 & 0xFFFFu));
+    it.chunk = __builtin_amdgcn_readfirstlane((int)(w1 >> 16));
+    it.tb = (uint32_t)__builtin_amdgcn_readfirstlane((int)w2);
+    it.te = (uint32_t)__builtin_amdgcn_readfirstlane((int)w3);
+    it.ok = it.b >= 0 && it.b < P.batch && it.hk < P.hkv && it.tb < it.te &&
+            it.te <= (uint32_t)P.max_tokens && (it.tb % kPageSize) == 0;
+    it.nch = 1;
+    it.base = 0;
+    if (it.ok) {
+        it.nch = __builtin_amdgcn_readfirstlane((int)ld_agt(P.n_chunks + it.b));
+        if (it.nch > 1) {
+            it.base = __builtin_amdgcn_readfirstlane((int)ld_agt(P.part_off + it.b));
+            const int slot = (it.base + it.chunk) * P.hkv + it.hk;
+            it.ok = it.chunk < it.nch && slot >= 0 && (it.base + it.nch) * P.hkv <= P.max_items;
+        } else {
+            it.ok = it.nch == 1;
+        }
+    }
+    return it;
+}
+
+// Spin (thread 0) until *p >= target, the exit flag rises, or the limit.
+__device__ __forceinline__ bool wait_at_least(const uint32_t* p, uint32_t target, const LoopParams& L) {
+    const uint64_t t0 = wall_clock64();
+    while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        if (__hip_atomic_load(&L.lglobal->dev_exit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return false;
+        if (wall_clock64() - t0 > L.timeout_ticks) return false;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return true;
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void resident_kernel(LoopParams L) {
+    __shared__ Smem<D, G> sm;
+    __shared__ uint32_t s_epoch, s_exit;
+    const int tid = threadIdx.x;
+    if (blockIdx.x == 0 && tid == 0) st_sys(&L.lctrl->alive, 1u);
+    uint32_t seen = 0;
+    for (;;) {
+        // 1. wait for the next published step.  Only workgroup 0 polls host
+        // memory (one PCIe read per poll); it mirrors what it sees into device
+        // memory, which the other workgroups poll.
+        if (tid == 0) {
+            const uint64_t t0 = wall_clock64();
+            uint32_t e = seen, x = 0;
+            if (blockIdx.x == 0) {
+                for (;;) {
+                    // in_epoch and exit_flag share one 64-bit word
+                    const uint64_t both = ld_sys64(reinterpret_cast<const uint64_t*>(&L.lctrl->in_epoch));
+                    if ((uint32_t)(both >> 32)) { x = 1; break; }
+                    e = (uint32_t)both;
+                    if (e != seen) break;
+                    if (wall_clock64() - t0 > L.timeout_ticks) { x = 2; break; }
+                    __builtin_amdgcn_s_sleep(16);
+                }
+                if (x) {
+                    __hip_atomic_store(&L.lglobal->dev_exit, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (x == 2) st_sys(&L.lctrl->exit_reason, 2u);
+                }
+            } else {
+                for (;;) {
+                    x = __hip_atomic_load(&L.lglobal->dev_exit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (x) break;
+                    e = __hip_atomic_load(&L.lglobal->dev_epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (e != seen) break;
+                    if (wall_clock64() - t0 > L.timeout_ticks + L.timeout_ticks / 4) { x = 2; break; }
+                    __builtin_amdgcn_s_sleep(16);
+                }
+            }
+            s_epoch = e;
+            s_exit = x;
+        }
+        __syncthreads();
+        if (s_exit) break;
+        const uint32_t e = s_epoch;
+        seen = e;
+        if (blockIdx.x == 0) {
+            // Workgroup 0 copies the step's slot (descriptor, queue header,
+            // row tables, items) from host memory into the device mirror with
+            // all its threads, then releases the step to the other workgroups.
+            const uint64_t* src = reinterpret_cast<const uint64_t*>(L.slots + (uint64_t)(e & 1u) * L.slot_bytes);
+            uint64_t* dst = reinterpret_cast<uint64_t*>(L.mirror + (uint64_t)(e & 1u) * L.slot_bytes);
+            __shared__ uint32_t s_nitems;
+            if (tid == 0) s_nitems = ld_sys(reinterpret_cast<const uint32_t*>(
+                                  reinterpret_cast<const unsigned char*>(src) + L.q_hdr_off));
+            __syncthreads();
+            const uint32_t ni = uni(s_nitems);
+            const uint64_t bytes = L.q_items_off + 16ull * (ni < (uint32_t)L.base.max_items ? ni : (uint32_t)L.base.max_items);
+            for (uint64_t w = tid; w < bytes / 8; w += kThreads)
+                __hip_atomic_store(dst + w, ld_sys64(src + w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            __syncthreads();
+            if (tid == 0) __hip_atomic_store(&L.lglobal->dev_epoch, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // 2. the step's descriptor and queue header, from the device mirror,
+        // shared through LDS.
+        const unsigned char* slot = L.mirror + (uint64_t)(e & 1u) * L.slot_bytes;
+        const LoopDesc* dsc = reinterpret_cast<const LoopDesc*>(slot);
+        __shared__ uint64_t s_desc[16];
+        if (tid < 14) {                           // 13 descriptor words + n_items | n_merge_rows << 32
+            const uint64_t* d64 = tid < 13 ? reinterpret_cast<const uint64_t*>(dsc) + tid
+                                           : reinterpret_cast<const uint64_t*>(slot + L.q_hdr_off);
+            s_desc[tid] = ld_agt64(d64);
+        }
+        __syncthreads();
+        DecodeParams P = L.base;
+        P.q = reinterpret_cast<const uint16_t*>(uni64(s_desc[0]));
+        P.k_pool = reinterpret_cast<const uint16_t*>(uni64(s_desc[1]));
+        P.v_pool = reinterpret_cast<const uint16_t*>(uni64(s_desc[2]));
+        P.block_table = reinterpret_cast<const int32_t*>(uni64(s_desc[3]));
+        P.out = reinterpret_cast<uint16_t*>(uni64(s_desc[4]));
+        P.lse = reinterpret_cast<float*>(uni64(s_desc[5]));
+        const int64_t ls_q = (int64_t)uni64(s_desc[6]);
+        const int64_t ls_kv = (int64_t)uni64(s_desc[7]);
+        const int64_t ls_bt = (int64_t)uni64(s_desc[8]);
+        const int64_t ls_out = (int64_t)uni64(s_desc[9]);
+        const int64_t ls_lse = (int64_t)uni64(s_desc[10]);
+        P.batch = (int32_t)uni((uint32_t)s_desc[11]);
+        P.bt_stride = (int32_t)uni((uint32_t)(s_desc[11] >> 32));
+        const int n_layers = (int)uni((uint32_t)s_desc[12]);
+        P.qhdr = reinterpret_cast<const QHdr*>(slot + L.q_hdr_off);
+        P.n_chunks = reinterpret_cast<const int32_t*>(slot + L.q_nch_off);
+        P.part_off = reinterpret_cast<const int32_t*>(slot + L.q_poff_off);
+        P.merge_rows = reinterpret_cast<const int32_t*>(slot + L.q_mrows_off);
+        P.items = reinterpret_cast<const Item*>(slot + L.q_items_off);
+        const uint32_t n_items = uni((uint32_t)s_desc[13]);
+        const uint32_t n_mrows = uni((uint32_t)(s_desc[13] >> 32));
+        LoopSlotCtr* ctr = reinterpret_cast<LoopSlotCtr*>(L.counters + (uint64_t)(e & 1u) * L.counter_bytes);
+        uint32_t* done = reinterpret_cast<uint32_t*>(ctr + 1);
+        P.head = &ctr->head;
+        const uint32_t total = n_items * (uint32_t)n_layers;
+        const uint32_t units = total + 1;        // + one unit: rows with no tokens
+        bool ok = true;
+        if (tid == 0) sm.next = pop_next(P);     // every unit is popped
+        __syncthreads();
+        uint32_t idx = __builtin_amdgcn_readfirstlane(sm.next);
+        while (idx < units) {
+            uint32_t nxt = 0;
+            int row = -1;
+            if (idx < total) {
+                const int layer = (int)(idx / n_items);
+                const uint32_t i = idx - (uint32_t)layer * n_items;
+                DecodeParams Q = P;
+                Q.q = P.q + layer * ls_q;
+                Q.k_pool = P.k_pool + layer * ls_kv;
+                Q.v_pool = P.v_pool + layer * ls_kv;
+                Q.block_table = P.block_table + layer * ls_bt;
+                Q.out = P.out + layer * ls_out;
+                Q.lse = P.lse + layer * ls_lse;
+                Q.partial_o = P.partial_o + (uint64_t)layer * L.partial_o_layer;
+                Q.partial_lse = P.partial_lse + (uint64_t)layer * L.partial_lse_layer;
+                Q.arrive = P.arrive + (uint64_t)layer * L.arrive_layer;
+                // one thread reads the item over PCIe; the workgroup shares it
+                __shared__ ItemRef s_it;
+                if (tid == 0) s_it = read_item_mirror(Q, i);
+                __syncthreads();
+                ItemRef it;
+                it.idx = uni(s_it.idx);
+                it.b = (int)uni((uint32_t)s_it.b);
+                it.hk = (int)uni((uint32_t)s_it.hk);
+                it.chunk = (int)uni((uint32_t)s_it.chunk);
+                it.tb = uni(s_it.tb);
+                it.te = uni(s_it.te);
+                it.nch = (int)uni((uint32_t)s_it.nch);
+                it.base = (int)uni((uint32_t)s_it.base);
+                it.ok = uni(s_it.ok ? 1u : 0u) != 0u;
+                row = it.ok ? it.b : -1;
+                if (layer > 0 && it.ok) {            // the row's previous layer must be complete
+                    if (tid == 0) {
+                        const uint32_t need = (uint32_t)layer * (uint32_t)it.nch * (uint32_t)P.hkv;
+                        s_exit = wait_at_least(done + it.b, need, L) ? 0u : 3u;
+                    }
+                    __syncthreads();
+                    if (s_exit) { ok = false; break; }
+                }
+                process_item<D, G>(Q, sm, it, nxt);
+            } else {
+                // rows with no tokens take the neutral state, in every layer;
+                // thread 0 finds them (64 merge rows at a time), all threads write
+                __shared__ int32_t s_rows[64];
+                __shared__ int32_t s_nrows;
+                for (uint32_t r0 = 0; r0 < n_mrows; r0 += 64) {
+                    if (tid == 0) {
+                        int cnt = 0;
+                        for (uint32_t ri = r0; ri < n_mrows && ri < r0 + 64; ++ri) {
+                            const int b = (int)ld_agt(P.merge_rows + ri);
+                            if (b < 0 || b >= P.batch) continue;
+                            if (ld_agt(P.n_chunks + b) == 0) s_rows[cnt++] = b;
+                        }
+                        s_nrows = cnt;
+                    }
+                    __syncthreads();
+                    const int cnt = (int)uni((uint32_t)s_nrows);
+                    for (int j = 0; j < cnt; ++j) {
+                        const int b = (int)uni((uint32_t)s_rows[j]);
+                        for (int l = 0; l < n_layers; ++l) {
+                            DecodeParams Q = P;
+                            Q.out = P.out + l * ls_out;
+                            Q.lse = P.lse + l * ls_lse;
+                            for (int t = tid; t < P.hq * D / 2; t += kThreads) {
+                                const int h = (2 * t) / D, d = (2 * t) % D;
+                                store_out_pair(Q, b, h, d, 0.0f, 0.0f);
+                                if (d == 0) store_lse(Q, b, h, -INFINITY);
+                            }
+                        }
+                    }
+                    __syncthreads();
+                }
+                if (tid == 0) nxt = pop_next(P);
+            }
+            // publish completion: this unit's outputs are stored, then count it
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            __syncthreads();
+            if (tid == 0) {
+                if (row >= 0) atomicAdd(done + row, 1u);
+                const uint32_t old = atomicAdd(&ctr->step_done, 1u);
+                if (old + 1 == units) {              // last unit of the step: re-arm, publish
+                    atomicExch(&ctr->head, 0u);
+                    atomicExch(&ctr->step_done, 0u);
+                    for (int b = 0; b < P.batch && b < L.max_batch; ++b) atomicExch(done + b, 0u);
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
+                    st_sys(&L.lctrl->out_epoch, e);
+                }
+                sm.next = nxt;
+            }
+            __syncthreads();
+            idx = __builtin_amdgcn_readfirstlane(sm.next);
+        }
+        if (!ok) {
+            if (tid == 0) st_sys(&L.lctrl->exit_reason, 3u);
+            break;
+        }
+        if (blockIdx.x == 0 && tid == 0) st_sys(&L.lctrl->heartbeat, e);
+    }
+    if (blockIdx.x == 0 && tid == 0) st_sys(&L.lctrl->alive, 0u);
 }
 
 // The separate merge kernel: one workgroup per (merge row, KV head).
@@ -862,6 +1219,27 @@ int launch_read_probe(const void* src, size_t bytes, void* sink, int grid, void*
     hipLaunchKernelGGL(read_probe_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
                        static_cast<const u32x4*>(src), bytes / 16, static_cast<uint32_t*>(sink));
     return (int)hipGetLastError();
+}
+
+__global__ void zero_kernel(uint32_t* p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+int launch_zero(void* p, size_t bytes, void* stream) {
+    hipLaunchKernelGGL(zero_kernel, dim3(256), dim3(256), 0, (hipStream_t)stream,
+                       static_cast<uint32_t*>(p), bytes / 4);
+    return (int)hipGetLastError();
+}
+
+template <int D, int G>
+int launch_resident_t(const LoopParams& lp, int grid, hipStream_t s) {
+    hipLaunchKernelGGL((resident_kernel<D, G>), dim3(grid), dim3(kThreads), 0, s, lp);
+    return (int)hipGetLastError();
+}
+
+int launch_resident(const LoopParams& lp, int head_dim, int group, int grid, void* stream) {
+    PKV_DISPATCH(launch_resident_t, head_dim, group, lp, grid, (hipStream_t)stream);
 }
 
 int launch_decode(const DecodeParams& p, int head_dim, int group, int grid, void* stream) {

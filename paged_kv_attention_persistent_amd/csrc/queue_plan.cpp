@@ -24,7 +24,7 @@ pkv_status resolve_config(const pkv_config* cfg, int device_cus, Resolved* r, co
     *why = "";
     if (!cfg || !r) { *why = "null config"; return PKV_ERR_INVALID_ARG; }
     if (cfg->struct_size != sizeof(pkv_config)) { *why = "pkv_config.struct_size mismatch"; return PKV_ERR_INVALID_ARG; }
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 5; ++i)
         if (cfg->reserved[i]) { *why = "reserved config fields must be zero"; return PKV_ERR_INVALID_ARG; }
     if (cfg->num_q_heads <= 0 || cfg->num_kv_heads <= 0 || cfg->num_q_heads % cfg->num_kv_heads) {
         *why = "num_q_heads must be a positive multiple of num_kv_heads"; return PKV_ERR_INVALID_ARG;
@@ -73,7 +73,26 @@ pkv_status resolve_config(const pkv_config* cfg, int device_cus, Resolved* r, co
         *why = "unknown merge_mode"; return PKV_ERR_INVALID_ARG;
     }
     r->merge_mode = cfg->merge_mode;
+    if (cfg->persistent != 0 && cfg->persistent != 1) { *why = "persistent must be 0 or 1"; return PKV_ERR_INVALID_ARG; }
+    r->persistent = cfg->persistent;
+    r->num_layers = cfg->num_layers == 0 ? 1 : cfg->num_layers;
+    if (r->num_layers < 1 || r->num_layers > 1024) { *why = "num_layers must be 1..1024"; return PKV_ERR_INVALID_ARG; }
+    if (!r->persistent && r->num_layers != 1) { *why = "num_layers > 1 needs the resident loop"; return PKV_ERR_INVALID_ARG; }
+    r->timeout_ms = cfg->timeout_ms == 0 ? 10000 : cfg->timeout_ms;
+    if (r->timeout_ms < 1 || r->timeout_ms > 3600000) { *why = "timeout_ms must be 1..3600000"; return PKV_ERR_INVALID_ARG; }
+    if (r->persistent && r->wg_per_cu != 1) { *why = "the resident loop runs one workgroup per CU"; return PKV_ERR_INVALID_ARG; }
+    if ((int64_t)r->max_items * r->num_layers > ((int64_t)1 << 31) / (4 * r->g * r->d)) {
+        *why = "partial-state storage too large"; return PKV_ERR_CAPACITY;
+    }
     return PKV_OK;
+}
+
+uint64_t loop_slot_bytes(const Resolved& r, const pkv_layout& lay) {
+    return align256(sizeof(LoopDesc) + (lay.items_off - lay.queue_off) + 16ull * r.max_items);
+}
+
+uint64_t loop_counter_bytes(const Resolved& r) {
+    return align256(sizeof(LoopSlotCtr) + 4ull * r.max_batch);
 }
 
 void compute_layout(const Resolved& r, pkv_layout* lay) {
@@ -91,12 +110,17 @@ void compute_layout(const Resolved& r, pkv_layout* lay) {
     off = align256(off + 4ull * r.max_batch);
     lay->items_off = off;
     off = align256(off + 16ull * r.max_items);
+    const uint64_t layers = (uint64_t)r.num_layers;
     lay->partial_o_off = off;
-    off = align256(off + 4ull * r.max_items * r.g * r.d);
+    off = align256(off + 4ull * r.max_items * r.g * r.d * layers);
     lay->partial_lse_off = off;
-    off = align256(off + 4ull * r.max_items * r.g);
+    off = align256(off + 4ull * r.max_items * r.g * layers);
     lay->arrive_off = off;
-    off = align256(off + 4ull * r.max_batch * r.hkv);
+    off = align256(off + 4ull * r.max_batch * r.hkv * layers);
+    lay->loop_off = off;
+    if (r.persistent) off = align256(off + sizeof(LoopGlobal) + 2ull * loop_counter_bytes(r));
+    lay->loop_mirror_off = off;
+    if (r.persistent) off = align256(off + 2ull * loop_slot_bytes(r, *lay));
     lay->total_bytes = off;
     lay->max_items = r.max_items;
 }

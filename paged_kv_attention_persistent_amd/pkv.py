@@ -42,14 +42,17 @@ class pkv_config(C.Structure):
                 ("scale", C.c_float), ("policy", C.c_int32), ("order", C.c_int32),
                 ("kv_chunk_tokens", C.c_int32), ("num_cus", C.c_int32),
                 ("max_items", C.c_int32), ("wg_per_cu", C.c_int32),
-                ("merge_mode", C.c_int32), ("reserved", C.c_int32 * 8)]
+                ("merge_mode", C.c_int32), ("persistent", C.c_int32), ("num_layers", C.c_int32),
+                ("timeout_ms", C.c_int32), ("reserved", C.c_int32 * 5)]
 
 
 class pkv_tensors(C.Structure):
     _fields_ = [("q", C.c_void_p), ("k_pool", C.c_void_p), ("v_pool", C.c_void_p),
                 ("block_table", C.c_void_p), ("ctx_lens", C.c_void_p),
                 ("out", C.c_void_p), ("lse", C.c_void_p), ("batch", C.c_int32),
-                ("block_table_stride", C.c_int32)]
+                ("block_table_stride", C.c_int32), ("layer_stride_q", C.c_int64),
+                ("layer_stride_kv", C.c_int64), ("layer_stride_bt", C.c_int64),
+                ("layer_stride_out", C.c_int64), ("layer_stride_lse", C.c_int64)]
 
 
 class pkv_queue_info(C.Structure):
@@ -67,7 +70,9 @@ class pkv_runtime_info(C.Structure):
     _fields_ = [("error_code", C.c_uint32), ("error_detail", C.c_uint32),
                 ("queue_head", C.c_uint32), ("n_items", C.c_uint32),
                 ("items_done", C.c_uint32), ("decode_calls", C.c_uint32),
-                ("grid", C.c_int32), ("num_cus", C.c_int32)]
+                ("grid", C.c_int32), ("num_cus", C.c_int32), ("loop_out_epoch", C.c_uint32),
+                ("loop_alive", C.c_uint32), ("loop_exit_reason", C.c_uint32),
+                ("loop_steps_started", C.c_uint32)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -78,7 +83,9 @@ class pkv_layout(C.Structure):
                 ("n_chunks_off", C.c_uint64), ("part_off_off", C.c_uint64),
                 ("merge_rows_off", C.c_uint64), ("items_off", C.c_uint64),
                 ("partial_o_off", C.c_uint64), ("partial_lse_off", C.c_uint64),
-                ("arrive_off", C.c_uint64), ("total_bytes", C.c_uint64), ("max_items", C.c_int32),
+                ("arrive_off", C.c_uint64), ("loop_off", C.c_uint64),
+                ("loop_mirror_off", C.c_uint64), ("total_bytes", C.c_uint64),
+                ("max_items", C.c_int32),
                 ("reserved", C.c_int32)]
 
 
@@ -144,7 +151,8 @@ def _check(status: int, where: str, handle=None) -> None:
 def make_config(num_q_heads, num_kv_heads, head_dim, num_pages, max_batch, max_pages_per_seq,
                 page_size=16, scale=0.0, policy=PKV_POLICY_AUTO, order=PKV_ORDER_CANONICAL,
                 kv_chunk_tokens=0, num_cus=0, max_items=0, wg_per_cu=0,
-                merge_mode=PKV_MERGE_FUSED) -> pkv_config:
+                merge_mode=PKV_MERGE_FUSED, persistent=0, num_layers=0,
+                timeout_ms=0) -> pkv_config:
     cfg = pkv_config()
     cfg.struct_size = C.sizeof(pkv_config)
     cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim = num_q_heads, num_kv_heads, head_dim
@@ -154,6 +162,7 @@ def make_config(num_q_heads, num_kv_heads, head_dim, num_pages, max_batch, max_p
     cfg.kv_chunk_tokens, cfg.num_cus, cfg.max_items, cfg.wg_per_cu = \
         kv_chunk_tokens, num_cus, max_items, wg_per_cu
     cfg.merge_mode = merge_mode
+    cfg.persistent, cfg.num_layers, cfg.timeout_ms = persistent, num_layers, timeout_ms
     return cfg
 
 
@@ -202,14 +211,18 @@ def pkv_build_queue_device(handle: int, ctx_lens_dev, stream=None) -> None:
 
 
 def make_tensors(q, k_pool, v_pool, block_table, ctx_lens, out, lse, batch=None,
-                 block_table_stride=0) -> pkv_tensors:
+                 block_table_stride=0, layer_strides=None) -> pkv_tensors:
+    """layer_strides: (q, kv, bt, out, lse) element strides for layered tensors."""
     t = pkv_tensors()
     t.q, t.k_pool, t.v_pool = q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr()
     t.block_table = block_table.data_ptr()
     t.ctx_lens = ctx_lens.data_ptr() if ctx_lens is not None else None
     t.out, t.lse = out.data_ptr(), lse.data_ptr()
     t.batch = int(q.shape[0]) if batch is None else int(batch)
-    t.block_table_stride = int(block_table_stride or block_table.shape[1])
+    t.block_table_stride = int(block_table_stride or block_table.shape[-1])
+    if layer_strides is not None:
+        (t.layer_stride_q, t.layer_stride_kv, t.layer_stride_bt, t.layer_stride_out,
+         t.layer_stride_lse) = [int(x) for x in layer_strides]
     return t
 
 

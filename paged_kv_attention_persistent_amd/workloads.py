@@ -277,3 +277,95 @@ def custom(name: str, lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
 
 
 CONFIGS = {"tiny": tiny, "long": long_context, "mixed": mixed, "short": many_short}
+
+
+@dataclass
+class SessionLoop:
+    """Many concurrent real-time sessions, each a stack of decode-attention
+    layers, stepped in lockstep by a resident kernel (the Wave Persistent
+    Kernel note's session cohort).  Session s starts with context L0_s drawn
+    uniformly from [lo, hi] and grows by one token per step: at step t its
+    context is L0_s + t.  Pages for L0_s + steps tokens are allocated up front
+    in every layer; each layer has its own randomly permuted pool.  K/V of the
+    tokens a later step adds are generated with the rest (the append of new
+    tokens is not part of the step)."""
+    name: str
+    sessions: int
+    layers: int
+    steps: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    l0: np.ndarray                    # int32 [sessions]
+    block_tables: np.ndarray          # int32 [layers][sessions][max_pages]
+    pages_per_layer: int
+    seed: int
+    page_size: int = 16
+    scale: float = 0.0
+
+    def __post_init__(self):
+        if self.scale == 0.0:
+            self.scale = 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def max_pages(self) -> int:
+        return int(self.block_tables.shape[2])
+
+    def ctx_lens(self, t: int) -> np.ndarray:
+        return (self.l0 + t).astype(np.int32)
+
+    def kv_bytes(self, t: int) -> int:
+        return int(self.ctx_lens(t).astype(np.int64).sum()) * self.layers * self.num_kv_heads \
+            * self.head_dim * 2 * 2
+
+    def pools(self, which: str, device) -> torch.Tensor:
+        """[layers][pages][Hkv][P][D] bf16 (one stream per tensor name)."""
+        t = torch.empty(self.layers, self.pages_per_layer, self.num_kv_heads, self.page_size,
+                        self.head_dim, dtype=torch.bfloat16, device=device)
+        return fill_normal_bf16(t, self.seed, self.name + "/" + which)
+
+    def queries(self, device) -> torch.Tensor:
+        """[steps][layers][sessions][Hq][D] bf16."""
+        t = torch.empty(self.steps, self.layers, self.sessions, self.num_q_heads, self.head_dim,
+                        dtype=torch.bfloat16, device=device)
+        return fill_normal_bf16(t, self.seed, self.name + "/q")
+
+    def query_unit(self, t: int, layer: int, s: int) -> torch.Tensor:
+        """CPU regeneration of q[t][layer][s] ([Hq][D])."""
+        per = self.num_q_heads * self.head_dim
+        off = ((t * self.layers + layer) * self.sessions + s) * per
+        idx = torch.arange(off, off + per, dtype=torch.int64)
+        return _to_bf16(normal_bf16_bits(self.seed, self.name + "/q", idx)).view(
+            self.num_q_heads, self.head_dim)
+
+    def slabs(self, which: str, layer: int, pages, kv_head: int) -> torch.Tensor:
+        """CPU regeneration of the (page, kv_head) slabs of one layer."""
+        slab = self.page_size * self.head_dim
+        per_page = self.num_kv_heads * slab
+        base = layer * self.pages_per_layer * per_page
+        pages = torch.as_tensor(np.asarray(pages, dtype=np.int64))
+        idx = (base + pages[:, None] * per_page + kv_head * slab
+               + torch.arange(slab, dtype=torch.int64)[None, :])
+        bits = normal_bf16_bits(self.seed, self.name + "/" + which, idx.reshape(-1))
+        return _to_bf16(bits).view(len(pages), self.page_size, self.head_dim)
+
+
+def session_loop(seed: int = MEASURE_SEED, sessions: int = 56, layers: int = 32,
+                 steps: int = 200, lo: int = 2048, hi: int = 16384, num_q_heads: int = 32,
+                 num_kv_heads: int = 8, head_dim: int = 128, name: str = "loop") -> SessionLoop:
+    """56 sessions x 32 layers, contexts U[2048, 16384] growing one token per
+    step for 200 steps, 32/8 heads, head_dim 128."""
+    rng = np.random.default_rng([seed, 5, zlib.crc32(name.encode())])
+    l0 = rng.integers(lo, hi + 1, size=sessions).astype(np.int32)
+    need = [-(-int(L + steps) // 16) for L in l0]
+    npg = int(sum(need))
+    maxp = max(need)
+    bts = np.full((layers, sessions, maxp), -1, dtype=np.int32)
+    for layer in range(layers):
+        perm = rng.permutation(npg).astype(np.int32)
+        pos = 0
+        for s, n in enumerate(need):
+            bts[layer, s, :n] = perm[pos:pos + n]
+            pos += n
+    return SessionLoop(name, sessions, layers, steps, num_q_heads, num_kv_heads, head_dim,
+                       l0, bts, npg, seed)
