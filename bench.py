@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--merge", default="fused", choices=["fused", "separate"])
     ap.add_argument("--copies", type=int, default=2)
     ap.add_argument("--no-gate", action="store_true")
+    ap.add_argument("--loop-steps", type=int, default=200,
+                    help="steps per run of the 56-session resident loop (0 skips the loop)")
+    ap.add_argument("--loop-runs", type=int, default=3)
     ap.add_argument("--profile-pass", action="store_true",
                     help="for hardware-counter runs: a few untimed decode steps of the workload, "
                          "then a 1 GiB copy probe of known size (the counter reference)")
@@ -143,6 +146,106 @@ def measure(torch, pkv, workloads, name, steps, warmup, order, wg_per_cu, copies
     del pools, tens
     torch.cuda.empty_cache()
     return res, wl
+
+
+def measure_loop(torch, pkv, workloads, steps, runs, gate, say):
+    """The 56-session resident loop: 32 layers of 32/8-head, head_dim 128
+    decode attention per session, contexts U[2048, 16384] growing one token
+    per step.  The resident kernel is launched once per run; per step the host
+    plans the queue, publishes the step and waits for its completion.  Step
+    latency = pkv_decode wall time (publish -> completion observed)."""
+    from oracle import paged_attention as pa
+    sl = workloads.session_loop(steps=max(steps, 3))
+    dev = "cuda"
+    t0 = time.perf_counter()
+    k, v, q = sl.pools("k", dev), sl.pools("v", dev), sl.queries(dev)
+    bt = torch.as_tensor(sl.block_tables).to(dev)
+    out = torch.empty((sl.steps, sl.layers, sl.sessions, sl.num_q_heads, sl.head_dim),
+                      dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((sl.steps, sl.layers, sl.sessions, sl.num_q_heads), dtype=torch.float32,
+                      device=dev)
+    lens = torch.zeros(sl.sessions, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    say(f"loop inputs generated in {time.perf_counter() - t0:.1f} s "
+        f"({2 * k.numel() * 2 / 1e9:.1f} GB of K/V)")
+    S, H, D = sl.sessions, sl.num_q_heads, sl.head_dim
+    strides = (S * H * D, sl.pages_per_layer * sl.num_kv_heads * 16 * D, S * sl.max_pages,
+               S * H * D, S * H)
+    cfg = pkv.make_config(H, sl.num_kv_heads, D, sl.pages_per_layer, S, sl.max_pages,
+                          scale=sl.scale, persistent=1, num_layers=sl.layers, timeout_ms=20000)
+    G = H // sl.num_kv_heads
+
+    def one_run(n):
+        stream = torch.cuda.Stream()
+        dec = pkv.PagedDecoder(cfg, stream=stream)
+        lat, plan = [], []
+        try:
+            for t in range(n):
+                a = time.perf_counter()
+                info = dec.build_queue(sl.ctx_lens(t))
+                b = time.perf_counter()
+                tens = pkv.make_tensors(q[t], k, v, bt, lens, out[t], lse[t], batch=S,
+                                        block_table_stride=sl.max_pages, layer_strides=strides)
+                pkv.pkv_decode(dec.handle, tens, stream)
+                c = time.perf_counter()
+                plan.append(b - a)
+                lat.append(c - b)
+        finally:
+            dec.close()
+        torch.cuda.synchronize()
+        return np.array(lat) * 1e3, np.array(plan) * 1e3, info
+
+    def check(ts):
+        o = out.float().cpu().numpy()
+        l = lse.cpu().numpy()
+        rng = np.random.default_rng(7)
+        worst = 0.0
+        for t in ts:
+            for _ in range(2):
+                layer, s, hk = int(rng.integers(sl.layers)), int(rng.integers(S)), int(rng.integers(sl.num_kv_heads))
+                L = int(sl.ctx_lens(t)[s])
+                npg = -(-L // 16)
+                pg = sl.block_tables[layer, s, :npg]
+                ks = workloads.bits_u16(sl.slabs("k", layer, pg, hk))[:, None]
+                vs = workloads.bits_u16(sl.slabs("v", layer, pg, hk))[:, None]
+                qg = workloads.bits_u16(sl.query_unit(t, layer, s))[None, hk * G:(hk + 1) * G]
+                ro, rl = pa.range_state(qg, ks, vs, np.arange(npg)[None], 0, 0, 0, L, sl.scale, 16)
+                err = np.abs(o[t, layer, s, hk * G:(hk + 1) * G] - ro)
+                lerr = np.abs(l[t, layer, s, hk * G:(hk + 1) * G] - rl)
+                if not (err.max() <= 2e-2 and err.mean() <= 2e-3 and lerr.max() <= 2e-2):
+                    raise SystemExit(f"loop parity failed at step {t} layer {layer} session {s} "
+                                     f"kv head {hk}: max {err.max():.3e} mean {err.mean():.3e}")
+                worst = max(worst, float(err.max()))
+        return worst
+
+    if gate:                                   # parity gate before timing
+        one_run(3)
+        say(f"loop parity gate passed (steps 0-2, max abs err {check([0, 1, 2]):.2e})")
+    runs_out = []
+    for r in range(runs):
+        lat, plan, info = one_run(steps)
+        runs_out.append(lat)
+        say(f"loop run {r}: p50 {np.median(lat):.3f} ms p99 {np.percentile(lat, 99):.3f} ms "
+            f"max {lat.max():.3f} ms; host planning p50 {np.median(plan):.3f} ms")
+    if gate:
+        say(f"loop parity after timing (steps 0, {steps // 2}, {steps - 1}): max abs err "
+            f"{check([0, steps // 2, steps - 1]):.2e}")
+    allv = np.concatenate(runs_out)
+    kv = np.array([sl.kv_bytes(t) for t in range(steps)])
+    gbs = kv / 1e9 / (np.concatenate([x[None] for x in runs_out]).mean(axis=0) * 1e-3)
+    res = {"sessions": S, "layers": sl.layers, "steps": steps, "runs": runs,
+           "items_per_layer": int(info.n_items), "split": bool(info.split),
+           "p50_ms": round(float(np.median(allv)), 4),
+           "p99_ms": round(float(np.percentile(allv, 99)), 4),
+           "max_ms": round(float(allv.max()), 4),
+           "p99_per_run_ms": [round(float(np.percentile(x, 99)), 4) for x in runs_out],
+           "kv_gb_per_step_mean": round(float(kv.mean() / 1e9), 3),
+           "kv_gbs_median": round(float(np.median(gbs)), 1),
+           "pct_of_hbm_peak_median": round(float(np.median(gbs)) / HBM_PEAK_GBS * 100, 2),
+           "launches_per_step": 0}
+    del k, v, q, out, lse
+    torch.cuda.empty_cache()
+    return res
 
 
 def measured_traffic(root):
@@ -264,6 +367,10 @@ def main():
                                           "items", "split", "kv_bytes", "launches_per_step")}
         others[name]["pct_of_hbm_peak"] = 100.0 * r["gbs"] / HBM_PEAK_GBS
         say(f"{name}: {r['gbs']:.1f} GB/s per step, decode {r['decode_gbs']:.1f} GB/s")
+    loop = None
+    if args.loop_steps > 0:
+        loop = measure_loop(torch, pkv, workloads, args.loop_steps, args.loop_runs,
+                            not args.no_gate, say)
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(workloads, wl, args.cpu_seconds, say)
@@ -297,6 +404,8 @@ def main():
                      "kernel": "decode_kernel<128,4>",
                      "decode_us_mean": round(main_res["decode_ms_mean"] * 1e3, 3)},
         "cpu_baseline": cpu,
+        "session_loop_p99_ms": loop["p99_ms"] if loop else None,
+        "session_loop": loop,
         "other_workloads": others,
         "host_wall_ms_per_step": round(main_res["host_wall_ms_per_step"], 4),
     }
