@@ -95,12 +95,20 @@ struct LoopGlobal {
 };
 
 // Device-memory counters of one slot of the resident loop.
+// A slot serves steps e, e + 2, ...; it is re-armed only after every
+// workgroup has checked out of step e (finished popping from it), and
+// workgroup 0 opens it for step e + 2 only after that re-arm.
 struct LoopSlotCtr {
     uint32_t head;              // pop counter
+    uint32_t pad0[31];
     uint32_t step_done;         // completed work units of the step
-    uint32_t pad[62];
+    uint32_t pad1[31];
+    uint32_t checkout;          // workgroups done with the step
+    uint32_t retired;           // last step whose use of the slot has ended
+    uint32_t pad2[62];
     // followed by uint32 done[max_batch]: completed items per row
 };
+static_assert(sizeof(LoopSlotCtr) == 512, "LoopSlotCtr layout");
 
 // Resolved configuration: defaults filled in, checked.
 struct Resolved {

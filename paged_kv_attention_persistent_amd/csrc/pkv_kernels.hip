@@ -782,11 +782,14 @@ __global__ __launch_bounds__(kThreads) void resident_kernel(LoopParams L) {
                     if (x == 2) st_sys(&L.lctrl->exit_reason, 2u);
                 }
             } else {
+                // steps are taken strictly in order: a workgroup that lags
+                // still serves (and checks out of) every step
                 for (;;) {
                     x = __hip_atomic_load(&L.lglobal->dev_exit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     if (x) break;
-                    e = __hip_atomic_load(&L.lglobal->dev_epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    if (e != seen) break;
+                    const uint32_t d = __hip_atomic_load(&L.lglobal->dev_epoch, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+                    if ((int32_t)(d - seen) >= 1) { e = seen + 1; break; }
                     if (wall_clock64() - t0 > L.timeout_ticks + L.timeout_ticks / 4) { x = 2; break; }
                     __builtin_amdgcn_s_sleep(16);
                 }
@@ -798,6 +801,19 @@ __global__ __launch_bounds__(kThreads) void resident_kernel(LoopParams L) {
         if (s_exit) break;
         const uint32_t e = s_epoch;
         seen = e;
+        LoopSlotCtr* ctr = reinterpret_cast<LoopSlotCtr*>(L.counters + (uint64_t)(e & 1u) * L.counter_bytes);
+        uint32_t* done = reinterpret_cast<uint32_t*>(ctr + 1);
+        if (blockIdx.x == 0 && e > 2u) {
+            // the slot last served step e - 2: every workgroup must have
+            // checked out of it (and the slot been re-armed) before reuse
+            if (tid == 0)
+                s_exit = wait_at_least(&ctr->retired, e - 2u, L) ? 0u : 3u;
+            __syncthreads();
+            if (s_exit) {
+                if (tid == 0) st_sys(&L.lctrl->exit_reason, 3u);
+                break;
+            }
+        }
         if (blockIdx.x == 0) {
             // Workgroup 0 copies the step's slot (descriptor, queue header,
             // row tables, items) from host memory into the device mirror with
@@ -849,8 +865,6 @@ __global__ __launch_bounds__(kThreads) void resident_kernel(LoopParams L) {
         P.items = reinterpret_cast<const Item*>(slot + L.q_items_off);
         const uint32_t n_items = uni((uint32_t)s_desc[13]);
         const uint32_t n_mrows = uni((uint32_t)(s_desc[13] >> 32));
-        LoopSlotCtr* ctr = reinterpret_cast<LoopSlotCtr*>(L.counters + (uint64_t)(e & 1u) * L.counter_bytes);
-        uint32_t* done = reinterpret_cast<uint32_t*>(ctr + 1);
         P.head = &ctr->head;
         const uint32_t total = n_items * (uint32_t)n_layers;
         const uint32_t units = total + 1;        // + one unit: rows with no tokens
@@ -938,10 +952,7 @@ __global__ __launch_bounds__(kThreads) void resident_kernel(LoopParams L) {
             if (tid == 0) {
                 if (row >= 0) atomicAdd(done + row, 1u);
                 const uint32_t old = atomicAdd(&ctr->step_done, 1u);
-                if (old + 1 == units) {              // last unit of the step: re-arm, publish
-                    atomicExch(&ctr->head, 0u);
-                    atomicExch(&ctr->step_done, 0u);
-                    for (int b = 0; b < P.batch && b < L.max_batch; ++b) atomicExch(done + b, 0u);
+                if (old + 1 == units) {              // last unit of the step: publish
                     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
                     st_sys(&L.lctrl->out_epoch, e);
                 }
@@ -953,6 +964,20 @@ __global__ __launch_bounds__(kThreads) void resident_kernel(LoopParams L) {
         if (!ok) {
             if (tid == 0) st_sys(&L.lctrl->exit_reason, 3u);
             break;
+        }
+        // Check out of the step: this workgroup pops from the slot no more.
+        // The last workgroup to check out re-arms the slot's counters, then
+        // marks the slot retired for step e.
+        if (tid == 0) {
+            const uint32_t old = atomicAdd(&ctr->checkout, 1u);
+            if (old + 1 == gridDim.x) {
+                atomicExch(&ctr->head, 0u);
+                atomicExch(&ctr->step_done, 0u);
+                for (int b = 0; b < P.batch && b < L.max_batch; ++b) atomicExch(done + b, 0u);
+                atomicExch(&ctr->checkout, 0u);
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                __hip_atomic_store(&ctr->retired, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
         if (blockIdx.x == 0 && tid == 0) st_sys(&L.lctrl->heartbeat, e);
     }

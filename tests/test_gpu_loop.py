@@ -106,7 +106,7 @@ def check_all(lp, units=None):
     assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS and lerr.max() <= MAX_ABS
 
 
-@pytest.mark.parametrize("variant", ["nosplit_d128", "split_d128", "nosplit_d64_g8"])
+@pytest.mark.parametrize("variant", ["nosplit_d128", "split_d128", "nosplit_d64_g8", "many_steps"])
 def test_small_loop_every_output(variant):
     say("variant", variant)
     if variant == "nosplit_d128":
@@ -118,10 +118,16 @@ def test_small_loop_every_output(variant):
         sl = workloads.session_loop(seed=12, sessions=4, layers=3, steps=3, lo=30, hi=200,
                                     num_q_heads=8, num_kv_heads=2, name="loop_split")
         kw = dict(policy=pkv.PKV_POLICY_SPLIT, kv_chunk_tokens=32)
-    else:
+    elif variant == "nosplit_d64_g8":
         sl = workloads.session_loop(seed=13, sessions=6, layers=2, steps=3, lo=1, hi=90,
                                     num_q_heads=16, num_kv_heads=2, head_dim=64, name="loop_d64")
         kw = dict(policy=pkv.PKV_POLICY_NO_SPLIT)
+    else:
+        # many short steps: each counter slot is reused 24 times, so a
+        # workgroup that lags a step behind meets a slot in every state
+        sl = workloads.session_loop(seed=17, sessions=3, layers=2, steps=48, lo=1, hi=70,
+                                    num_q_heads=4, num_kv_heads=1, name="loop_many")
+        kw = dict(policy=pkv.PKV_POLICY_AUTO, kv_chunk_tokens=32)
     lp = Loop(sl, **kw)
     try:
         for t in range(sl.steps):
