@@ -66,6 +66,36 @@ __device__ __forceinline__ float sum8(float v) {
     return v;
 }
 
+// Reductions over lane bits 3..5 (the eight 8-lane groups of a wave) without
+// going through LDS: bit 3 by a DPP rotate of each 16-lane row by 8, bits 4
+// and 5 by gfx950's row-swap permutes, which exchange 16-lane rows (bit 4)
+// and 32-lane halves (bit 5) between two registers.  Every lane ends with the
+// same value, combined in the same order.
+__device__ __forceinline__ float swap16_sum(float v) {
+    const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+__device__ __forceinline__ float swap32_sum(float v) {
+    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+__device__ __forceinline__ float swap16_max(float v) {
+    const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float swap32_max(float v) {
+    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float groups_sum(float v) {
+    v += dpp_f<0x128>(v);   // row_ror:8 (lane bit 3)
+    return swap32_sum(swap16_sum(v));
+}
+__device__ __forceinline__ float groups_max(float v) {
+    v = fmaxf(v, dpp_f<0x128>(v));
+    return swap32_max(swap16_max(v));
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
 
@@ -432,9 +462,13 @@ __device__ __forceinline__ ItemRef read_item(const DecodeParams& P, uint32_t idx
     it.nch = 1;
     it.base = 0;
     if (it.ok) {
-        it.nch = __builtin_amdgcn_readfirstlane(P.n_chunks[it.b]);
+        // both row words in one round trip (part_off has batch + 1 entries)
+        const int nch = P.n_chunks[it.b];
+        const int base = P.part_off[it.b];
+        it.nch = __builtin_amdgcn_readfirstlane(nch);
+        const int base_u = __builtin_amdgcn_readfirstlane(base);
         if (it.nch > 1) {
-            it.base = __builtin_amdgcn_readfirstlane(P.part_off[it.b]);
+            it.base = base_u;
             const int slot = (it.base + it.chunk) * P.hkv + it.hk;
             it.ok = it.chunk < it.nch && slot >= 0 && (it.base + it.nch) * P.hkv <= P.max_items;
         } else {
@@ -512,29 +546,28 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, const ItemRe
     }
     // Claim the next item only now, near the end of this one: a claim made
     // earlier would hold an item this workgroup cannot start while another
-    // workgroup runs dry.  Its latency hides behind the combine below.
-    if (tid == 0) nxt = pop_next(P);
+    // workgroup runs dry.  The claim's result is first used after the
+    // barrier below, so its round trip overlaps the reductions and the wait
+    // for the other waves.
+    uint32_t popped = 0;
+    if (tid == 0) {
+        // A lane-private copy of the address keeps the compiler from turning
+        // this one-lane atomic into its wave-wide form, which reads the
+        // result at once.
+        __attribute__((address_space(1))) uint32_t* head =
+            (__attribute__((address_space(1))) uint32_t*)P.head;
+        __asm__ volatile("" : "+v"(head));
+        popped = __hip_atomic_fetch_add(head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 
     // Combine the 8 token groups of this wave (lanes r = 0..7 with equal p).
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        float M = st.m[g];
-        M = fmaxf(M, __shfl_xor(M, 8));
-        M = fmaxf(M, __shfl_xor(M, 16));
-        M = fmaxf(M, __shfl_xor(M, 32));
+        const float M = groups_max(st.m[g]);
         const float a = __builtin_amdgcn_exp2f(st.m[g] - M);
-        float l = st.l[g] * a;
-        l += __shfl_xor(l, 8);
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
+        const float l = groups_sum(st.l[g] * a);
 #pragma unroll
-        for (int e = 0; e < D / 8; ++e) {
-            float x = st.acc[g][e] * a;
-            x += __shfl_xor(x, 8);
-            x += __shfl_xor(x, 16);
-            x += __shfl_xor(x, 32);
-            st.acc[g][e] = x;
-        }
+        for (int e = 0; e < D / 8; ++e) st.acc[g][e] = groups_sum(st.acc[g][e] * a);
         st.m[g] = M;
         st.l[g] = l;
     }
@@ -549,6 +582,10 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, const ItemRe
         }
     }
     __syncthreads();
+    if (tid == 0) {
+        __asm__ volatile("" : "+v"(popped));     // the claim's first use: after the barrier
+        nxt = (P.static_first ? gridDim.x : 0u) + popped;
+    }
 
     // Combine the 8 waves; each thread finishes two adjacent dims of one head.
     const bool split = it.nch > 1;
@@ -730,9 +767,11 @@ __device__ __forceinline__ ItemRef read_item_mirror(const DecodeParams& P, uint3
     it.nch = 1;
     it.base = 0;
     if (it.ok) {
-        it.nch = __builtin_amdgcn_readfirstlane((int)ld_agt(P.n_chunks + it.b));
+        const uint32_t nch = ld_agt(P.n_chunks + it.b), base = ld_agt(P.part_off + it.b);
+        it.nch = __builtin_amdgcn_readfirstlane((int)nch);
+        const int base_u = __builtin_amdgcn_readfirstlane((int)base);
         if (it.nch > 1) {
-            it.base = __builtin_amdgcn_readfirstlane((int)ld_agt(P.part_off + it.b));
+            it.base = base_u;
             const int slot = (it.base + it.chunk) * P.hkv + it.hk;
             it.ok = it.chunk < it.nch && slot >= 0 && (it.base + it.nch) * P.hkv <= P.max_items;
         } else {
