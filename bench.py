@@ -133,6 +133,7 @@ def measure(torch, pkv, workloads, name, steps, warmup, order, wg_per_cu, copies
     ms_step = total_ms / steps
     res = {
         "workload": name, "kv_bytes": info.kv_bytes, "items": info.n_items,
+        "chunk_tokens": info.chunk_tokens,
         "split": bool(info.split), "launches_per_step": info.launches_per_step,
         "partial_bytes": info.partial_bytes, "ms_per_step": ms_step,
         "gbs": info.kv_bytes / (ms_step * 1e-3) / 1e9,
@@ -367,7 +368,8 @@ def main():
         r, _ = measure(torch, pkv, workloads, name, max(args.steps // 2, 10), args.warmup,
                        args.order, args.wg_per_cu, args.copies, not args.no_gate, say, args.merge)
         others[name] = {k: r[k] for k in ("gbs", "decode_gbs", "ms_per_step", "decode_ms_mean",
-                                          "items", "split", "kv_bytes", "launches_per_step")}
+                                          "items", "split", "chunk_tokens", "kv_bytes",
+                                          "launches_per_step")}
         others[name]["pct_of_hbm_peak"] = 100.0 * r["gbs"] / HBM_PEAK_GBS
         say(f"{name}: {r['gbs']:.1f} GB/s per step, decode {r['decode_gbs']:.1f} GB/s")
     loop = None
@@ -394,7 +396,7 @@ def main():
         "pct_of_hbm_peak": round(100.0 * main_res["gbs"] / HBM_PEAK_GBS, 2),
         "config": {"workload": "single long context", "batch": 1, "context_tokens": 131072,
                    "q_heads": 32, "kv_heads": 8, "head_dim": 128, "page_size": 16,
-                   "kv_chunk_tokens": 4096, "items": main_res["items"],
+                   "kv_chunk_tokens": main_res["chunk_tokens"], "items": main_res["items"],
                    "launches_per_step": main_res["launches_per_step"],
                    "kv_bytes_per_step": main_res["kv_bytes"], "grid": main_res["grid"],
                    "order": args.order, "merge": args.merge} if args.workload == "long" else

@@ -71,8 +71,13 @@ enum {
 };
 
 /* Split policy (PersistentKV page, Methodology 2).  AUTO: cut rows into
- * kv_chunk_tokens-token ranges iff B * Hkv < num_cus and some L_b exceeds
- * kv_chunk_tokens; otherwise one item per (row, KV head). */
+ * C-token ranges iff B * Hkv < num_cus and some L_b exceeds C; otherwise one
+ * item per (row, KV head).  C is kv_chunk_tokens, or with kv_chunk_tokens = 0
+ * ("fit", the default) it is chosen per call as P * T with T the smallest
+ * page count for which sum_b ceil(ceil(L_b / P) / T) <= max(1, num_cus / Hkv):
+ * the shortest ranges that still give at most one item per workgroup (the
+ * longest row's page count if the rows alone exceed that bound), and never
+ * shorter than 64 pages. */
 enum { PKV_POLICY_AUTO = 0, PKV_POLICY_NO_SPLIT = 1, PKV_POLICY_SPLIT = 2 };
 
 /* Queue order: CANONICAL = (seq, kv_head, chunk) ascending; LPT = stable sort
@@ -104,7 +109,7 @@ typedef struct pkv_config {
     float scale;                /* 0 -> 1 / sqrt(D) */
     int32_t policy;             /* PKV_POLICY_* */
     int32_t order;              /* PKV_ORDER_* */
-    int32_t kv_chunk_tokens;    /* split range length; 0 -> 4096; multiple of P */
+    int32_t kv_chunk_tokens;    /* split range length, a multiple of P; 0 -> fitted per call */
     int32_t num_cus;            /* policy input; 0 -> the device's CU count */
     int32_t max_items;          /* queue capacity; 0 -> bound from the shape */
     int32_t wg_per_cu;          /* persistent grid = CUs * wg_per_cu; 0 -> 1 */
@@ -134,7 +139,7 @@ typedef struct pkv_tensors {
 
 typedef struct pkv_queue_info {
     int32_t n_items;            /* items in the compact queue */
-    int32_t split;              /* policy decision: 1 = ranges of kv_chunk_tokens */
+    int32_t split;              /* policy decision: 1 = ranges of chunk_tokens */
     int32_t chunk_tokens;       /* range length used */
     int32_t n_split_rows;       /* rows with more than one range */
     int32_t n_merge_rows;       /* rows finished by the merge kernel (split or empty) */

@@ -21,6 +21,17 @@ Readings taken where the page is silent:
 * Split rule (AUTO): split into ``chunk_tokens``-token ranges iff
   B * Hkv < num_cus and some L_b > chunk_tokens; otherwise one item per
   (row, KV head).  ``chunk_tokens`` is a multiple of the page size.
+* Range length (the page says only that ranges are disjoint): either a
+  fixed ``chunk_tokens``, or, with ``chunk_tokens = 0`` ("fit"), the
+  shortest whole number of pages T for which the split queue still has at
+  most one range per workgroup: sum_b ceil(pages_b / T) <= K with
+  K = max(1, num_cus // Hkv) and pages_b = ceil(L_b / P).  This extends the
+  page's own count for one sequence (as many ranges as it takes to fill the
+  GPU) to a batch, keeping the longest range as short as one round allows.
+  If no T reaches the bound (more non-empty rows than K), T is the longest
+  row's page count.  T is never below 64 pages (1024 tokens, eight pages
+  per wave of a workgroup): shorter ranges cost more in per-range start and
+  merge than they gain in balance.
 * Ranges are fixed chunks from token 0: chunk c covers
   [c * C, min(L_b, (c + 1) * C)).
 * Item encoding, 16 bytes little-endian:
@@ -52,6 +63,25 @@ ITEM_DTYPE = np.dtype([("seq", "<u4"), ("kv_head", "<u2"), ("chunk", "<u2"),
 assert ITEM_DTYPE.itemsize == 16
 
 
+FIT_MIN_PAGES = 64
+
+
+def fit_chunk(ctx_lens, num_kv_heads: int, num_cus: int, page_size: int = 16,
+              min_pages: int = FIT_MIN_PAGES) -> int:
+    """Range length in tokens for chunk mode "fit" (reading in the header):
+    the smallest T pages with sum_b ceil(pages_b / T) <= max(1, num_cus // Hkv),
+    found by trying T = 1, 2, ... in turn, and then at least ``min_pages``."""
+    pages = [-(-int(L) // page_size) for L in ctx_lens]
+    longest = max(pages, default=0)
+    budget = max(1, num_cus // num_kv_heads)
+    T = max(longest, 1)
+    for t in range(1, longest + 1):
+        if sum(-(-n // t) for n in pages) <= budget:
+            T = t
+            break
+    return max(T, min_pages) * page_size
+
+
 def decide_split(ctx_lens, num_kv_heads: int, num_cus: int, chunk_tokens: int,
                  policy: int = POLICY_AUTO) -> bool:
     """The adaptive split decision (PersistentKV page, Methodology 2)."""
@@ -71,8 +101,11 @@ def build_queue(ctx_lens, num_kv_heads: int, num_cus: int, chunk_tokens: int,
                 policy: int = POLICY_AUTO, order: int = ORDER_CANONICAL):
     """Compact work queue for one decode call.
 
+    ``chunk_tokens = 0`` selects chunk mode "fit" (see ``fit_chunk``).
+
     Returns a dict with
       split      bool, the policy decision
+      chunk_tokens  the range length used
       items      ITEM_DTYPE array, one entry per non-empty interval
       n_chunks   int32 [B]
       part_off   int32 [B + 1]
@@ -82,6 +115,8 @@ def build_queue(ctx_lens, num_kv_heads: int, num_cus: int, chunk_tokens: int,
     for L in lens:
         if L < 0:
             raise ValueError("negative context length")
+    if chunk_tokens == 0:                                 # chunk mode "fit"
+        chunk_tokens = fit_chunk(lens, num_kv_heads, num_cus)
     split = decide_split(lens, num_kv_heads, num_cus, chunk_tokens, policy)
     bsz = len(lens)
 
@@ -122,7 +157,7 @@ def build_queue(ctx_lens, num_kv_heads: int, num_cus: int, chunk_tokens: int,
 
     merge_rows = np.array([b for b in range(bsz) if n_chunks[b] != 1], dtype=np.int32)
     return {"split": split, "items": items, "n_chunks": n_chunks,
-            "part_off": part_off, "merge_rows": merge_rows}
+            "part_off": part_off, "merge_rows": merge_rows, "chunk_tokens": chunk_tokens}
 
 
 def partial_slot(item, part_off, num_kv_heads: int) -> int:

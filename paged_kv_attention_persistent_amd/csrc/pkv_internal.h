@@ -13,7 +13,7 @@ namespace pkv {
 constexpr int kPageSize = 16;          // tokens per page (the only size built)
 constexpr int kThreads = 512;          // 8 waves of 64 lanes per workgroup
 constexpr int kWaves = kThreads / 64;
-constexpr int kDefaultChunk = 4096;
+constexpr int kFitMinPages = 64;       // chunk mode "fit": ranges of at least 64 pages
 
 // One queue item: a non-empty token range [tok_begin, tok_end) of one
 // (sequence, KV head).  16 bytes, little-endian.

@@ -1078,14 +1078,50 @@ __global__ __launch_bounds__(kBuildThreads) void build_queue_kernel(BuildParams 
     }
     atomicMax(&s_max, lmax);
     __syncthreads();
+    // Chunk mode "fit" (chunk 0): the smallest T pages with
+    // sum_b ceil(pages_b / T) <= K = max(1, CUs / Hkv), by bisection over T
+    // with a block-wide sum per step (clamped at K + 1, which is all the
+    // comparison needs); the longest row's pages when no T reaches K; never
+    // below kFitMinPages.
+    int chunk = P.chunk;
+    if (chunk == 0) {
+        __shared__ unsigned long long s_cnt;
+        const unsigned long long budget = (unsigned long long)(P.num_cus / P.hkv > 1 ? P.num_cus / P.hkv : 1);
+        const int longest = (s_max + kPageSize - 1) / kPageSize;
+        auto ranges = [&](int T) -> unsigned long long {
+            unsigned long long local = 0;
+            for (int b = r0; b < r1; ++b) {
+                const int L = P.ctx_lens[b];
+                const int pages = L > 0 ? (L + kPageSize - 1) / kPageSize : 0;
+                local += (unsigned long long)((pages + T - 1) / T);
+            }
+            if (local > budget + 1) local = budget + 1;
+            __syncthreads();
+            if (t == 0) s_cnt = 0;
+            __syncthreads();
+            atomicAdd(&s_cnt, local);
+            __syncthreads();
+            return s_cnt;
+        };
+        int T = longest > 0 ? longest : 1;
+        if (longest > 0 && ranges(longest) <= budget) {
+            int lo = 1, hi = longest;
+            while (lo < hi) {
+                const int mid = lo + (hi - lo) / 2;
+                if (ranges(mid) <= budget) hi = mid; else lo = mid + 1;
+            }
+            T = lo;
+        }
+        chunk = (T > kFitMinPages ? T : kFitMinPages) * kPageSize;
+    }
     bool split;
     if (P.policy == PKV_POLICY_NO_SPLIT) split = false;
     else if (P.policy == PKV_POLICY_SPLIT) split = true;
-    else split = B > 0 && (long long)B * P.hkv < P.num_cus && s_max > P.chunk;
+    else split = B > 0 && (long long)B * P.hkv < P.num_cus && s_max > chunk;
 
     auto nchunks = [&](int L) -> int {
         if (L <= 0) return 0;
-        return split ? (L + P.chunk - 1) / P.chunk : 1;
+        return split ? (L + chunk - 1) / chunk : 1;
     };
     int c_items = 0, c_parts = 0, c_merge = 0;
     for (int b = r0; b < r1; ++b) {
@@ -1126,7 +1162,7 @@ __global__ __launch_bounds__(kBuildThreads) void build_queue_kernel(BuildParams 
         if (t == 0) val = ok ? total : 0;
         else if (t == 1) val = s_total[2];
         else if (t == 2) val = split ? 1 : 0;
-        else if (t == 3) val = P.chunk;
+        else if (t == 3) val = chunk;
         else if (t == 4) val = B;
         hw[t] = val;
     }
@@ -1147,8 +1183,8 @@ __global__ __launch_bounds__(kBuildThreads) void build_queue_kernel(BuildParams 
         it.seq = (uint32_t)b;
         it.kv_head = (uint16_t)h;
         it.chunk = (uint16_t)c;
-        it.tok_begin = split ? (uint32_t)(c * P.chunk) : 0u;
-        const long long e = split ? (long long)(c + 1) * P.chunk : (long long)L;
+        it.tok_begin = split ? (uint32_t)(c * chunk) : 0u;
+        const long long e = split ? (long long)(c + 1) * chunk : (long long)L;
         it.tok_end = (uint32_t)(e < L ? e : L);
         P.items[i] = it;
     }

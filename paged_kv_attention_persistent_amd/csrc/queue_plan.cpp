@@ -52,13 +52,17 @@ pkv_status resolve_config(const pkv_config* cfg, int device_cus, Resolved* r, co
     r->policy = cfg->policy;
     if (cfg->order != PKV_ORDER_CANONICAL && cfg->order != PKV_ORDER_LPT) { *why = "unknown order"; return PKV_ERR_INVALID_ARG; }
     r->order = cfg->order;
-    r->chunk = cfg->kv_chunk_tokens == 0 ? kDefaultChunk : cfg->kv_chunk_tokens;
-    if (r->chunk <= 0 || r->chunk % kPageSize) { *why = "kv_chunk_tokens must be a positive multiple of 16"; return PKV_ERR_INVALID_ARG; }
-    const int64_t max_tokens = (int64_t)r->max_pages_per_seq * kPageSize;
-    const int64_t max_chunks = (max_tokens + r->chunk - 1) / r->chunk;
-    if (max_chunks > 65535) { *why = "more than 65535 ranges per row"; return PKV_ERR_CAPACITY; }
+    r->chunk = cfg->kv_chunk_tokens;                  // 0: chunk mode "fit", chosen per call
+    if (r->chunk < 0 || r->chunk % kPageSize) { *why = "kv_chunk_tokens must be 0 or a positive multiple of 16"; return PKV_ERR_INVALID_ARG; }
     r->num_cus = cfg->num_cus > 0 ? cfg->num_cus : device_cus;
     if (r->num_cus <= 0) { *why = "num_cus unknown (set it in the config)"; return PKV_ERR_INVALID_ARG; }
+    const int64_t max_tokens = (int64_t)r->max_pages_per_seq * kPageSize;
+    // ranges per row: ceil(max_tokens / C) for fixed chunks; for "fit" the
+    // range floor bounds it by ceil(max_pages_per_seq / kFitMinPages), which,
+    // like the whole layout, does not depend on the CU count
+    const int64_t max_chunks = r->chunk ? (max_tokens + r->chunk - 1) / r->chunk
+                                        : ((int64_t)r->max_pages_per_seq + kFitMinPages - 1) / kFitMinPages;
+    if (max_chunks > 65535) { *why = "more than 65535 ranges per row"; return PKV_ERR_CAPACITY; }
     if (cfg->max_items < 0) { *why = "max_items must be >= 0"; return PKV_ERR_INVALID_ARG; }
     if (cfg->max_items > 0) {
         r->max_items = cfg->max_items;
@@ -125,6 +129,34 @@ void compute_layout(const Resolved& r, pkv_layout* lay) {
     lay->max_items = r.max_items;
 }
 
+// Chunk mode "fit": the smallest T pages with sum_b ceil(pages_b / T) <= K,
+// K = max(1, CUs / Hkv), so that the split queue still has at most one range
+// per workgroup; the longest row's page count when no T reaches K; and never
+// below kFitMinPages.  The count falls as T grows, so a bisection finds the
+// smallest T.
+int fit_chunk(const Resolved& r, const int32_t* ctx_lens, int batch, int64_t max_len) {
+    const int64_t budget = std::max(1, r.num_cus / r.hkv);
+    const int64_t longest = (max_len + r.page - 1) / r.page;
+    auto ranges = [&](int64_t T) {
+        int64_t n = 0;
+        for (int b = 0; b < batch; ++b) {
+            const int64_t pages = ((int64_t)ctx_lens[b] + r.page - 1) / r.page;
+            n += (pages + T - 1) / T;
+        }
+        return n;
+    };
+    int64_t T = std::max<int64_t>(longest, 1);
+    if (longest > 0 && ranges(longest) <= budget) {
+        int64_t lo = 1, hi = longest;                // ranges(hi) <= budget holds
+        while (lo < hi) {
+            const int64_t mid = lo + (hi - lo) / 2;
+            if (ranges(mid) <= budget) hi = mid; else lo = mid + 1;
+        }
+        T = lo;
+    }
+    return (int)(std::max<int64_t>(T, kFitMinPages) * r.page);
+}
+
 pkv_status plan_queue(const Resolved& r, const int32_t* ctx_lens, int32_t batch, QHdr* qh,
                       int32_t* n_chunks, int32_t* part_off, int32_t* merge_rows, Item* items,
                       int32_t items_cap, pkv_queue_info* info, const char** why) {
@@ -140,17 +172,18 @@ pkv_status plan_queue(const Resolved& r, const int32_t* ctx_lens, int32_t batch,
         max_len = std::max(max_len, L);
         sum_len += L;
     }
+    const int chunk = r.chunk ? r.chunk : fit_chunk(r, ctx_lens, batch, max_len);
     bool split;
     if (r.policy == PKV_POLICY_NO_SPLIT) split = false;
     else if (r.policy == PKV_POLICY_SPLIT) split = true;
-    else split = batch > 0 && (int64_t)batch * r.hkv < r.num_cus && max_len > r.chunk;
+    else split = batch > 0 && (int64_t)batch * r.hkv < r.num_cus && max_len > chunk;
 
     int64_t n_items = 0;
     int n_split_rows = 0, n_merge = 0;
     part_off[0] = 0;
     for (int b = 0; b < batch; ++b) {
         const int64_t L = ctx_lens[b];
-        const int32_t nc = L == 0 ? 0 : (split ? (int32_t)((L + r.chunk - 1) / r.chunk) : 1);
+        const int32_t nc = L == 0 ? 0 : (split ? (int32_t)((L + chunk - 1) / chunk) : 1);
         n_chunks[b] = nc;
         part_off[b + 1] = part_off[b] + (nc > 1 ? nc : 0);
         n_items += (int64_t)nc * r.hkv;
@@ -168,8 +201,8 @@ pkv_status plan_queue(const Resolved& r, const int32_t* ctx_lens, int32_t batch,
                 it.seq = (uint32_t)b;
                 it.kv_head = (uint16_t)h;
                 it.chunk = (uint16_t)c;
-                it.tok_begin = split ? (uint32_t)((int64_t)c * r.chunk) : 0u;
-                it.tok_end = split ? (uint32_t)std::min<int64_t>(L, (int64_t)(c + 1) * r.chunk) : (uint32_t)L;
+                it.tok_begin = split ? (uint32_t)((int64_t)c * chunk) : 0u;
+                it.tok_end = split ? (uint32_t)std::min<int64_t>(L, (int64_t)(c + 1) * chunk) : (uint32_t)L;
                 items[k++] = it;
             }
         }
@@ -183,13 +216,13 @@ pkv_status plan_queue(const Resolved& r, const int32_t* ctx_lens, int32_t batch,
     qh->n_items = (int32_t)n_items;
     qh->n_merge_rows = n_merge;
     qh->split = split ? 1 : 0;
-    qh->chunk_tokens = r.chunk;
+    qh->chunk_tokens = chunk;
     qh->batch = batch;
     if (info) {
         memset(info, 0, sizeof(*info));
         info->n_items = (int32_t)n_items;
         info->split = split ? 1 : 0;
-        info->chunk_tokens = r.chunk;
+        info->chunk_tokens = chunk;
         info->n_split_rows = n_split_rows;
         info->n_merge_rows = n_merge;
         info->n_partial_slots = part_off[batch] * r.hkv;

@@ -76,6 +76,7 @@ def compare_with_oracle(cfg, lens, hkv, num_cus, chunk, policy, order):
     assert np.array_equal(part_off, ref["part_off"])
     assert np.array_equal(merge_rows, ref["merge_rows"])
     assert bool(info.split) == ref["split"]
+    assert info.chunk_tokens == ref["chunk_tokens"]
     assert info.n_items == len(ref["items"])
     sep = cfg.merge_mode == pkv.PKV_MERGE_SEPARATE
     assert info.launches_per_step == 1 + (sep and len(ref["merge_rows"]) > 0)
@@ -88,9 +89,11 @@ def test_host_queue_matches_oracle_on_workloads(name, order):
     for seed in (workloads.MEASURE_SEED, workloads.CALIBRATION_SEED):
         wl = workloads.CONFIGS[name](seed)
         cfg = cfg_for(wl, order=order)
-        info = compare_with_oracle(cfg, wl.ctx_lens, wl.num_kv_heads, 256, 4096,
+        info = compare_with_oracle(cfg, wl.ctx_lens, wl.num_kv_heads, 256, 0,
                                    wq.POLICY_AUTO, order)
         assert info.kv_bytes == wl.kv_bytes
+        fixed = cfg_for(wl, order=order, kv_chunk_tokens=4096)
+        compare_with_oracle(fixed, wl.ctx_lens, wl.num_kv_heads, 256, 4096, wq.POLICY_AUTO, order)
 
 
 def test_host_queue_matches_oracle_random():
@@ -98,7 +101,7 @@ def test_host_queue_matches_oracle_random():
     for trial in range(300):
         bsz = int(rng.integers(0, 20))
         hkv = int(rng.choice([1, 2, 8]))
-        chunk = int(rng.choice([16, 64, 4096]))
+        chunk = int(rng.choice([0, 16, 64, 4096]))
         maxp = int(rng.integers(1, 40))
         lens = rng.integers(0, maxp * 16 + 1, size=bsz)
         if bsz and rng.random() < 0.3:
@@ -112,10 +115,26 @@ def test_host_queue_matches_oracle_random():
         compare_with_oracle(cfg, lens.tolist(), hkv, cus, chunk, policy, order)
 
 
+def test_host_fit_chunk_matches_oracle_on_long_random_rows():
+    # lengths of thousands of pages, so the bisection lands above the 64-page floor
+    rng = np.random.default_rng(23)
+    for trial in range(200):
+        bsz = int(rng.integers(1, 300))
+        hkv = int(rng.choice([1, 2, 8]))
+        cus = int(rng.choice([8, 64, 256, 1024]))
+        maxp = int(rng.integers(1, 6000))
+        lens = rng.integers(0, maxp * 16 + 1, size=bsz)
+        lens[rng.random(bsz) < 0.2] = 0
+        policy = int(rng.integers(0, 3))
+        cfg = pkv.make_config(hkv * 4, hkv, 128, 1000, bsz, maxp, policy=policy, num_cus=cus)
+        compare_with_oracle(cfg, lens.tolist(), hkv, cus, 0, policy, pkv.PKV_ORDER_CANONICAL)
+
+
 def test_config_validation():
     good = pkv.make_config(32, 8, 128, 100, 4, 10, num_cus=256)
     assert pkv.pkv_workspace_size(good) > 0
     bad = [dict(num_q_heads=30), dict(head_dim=96), dict(page_size=32), dict(kv_chunk_tokens=100),
+           dict(kv_chunk_tokens=-16),
            dict(num_pages=0), dict(wg_per_cu=9), dict(policy=7), dict(num_q_heads=64),
            dict(merge_mode=2)]
     base = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, num_pages=100, max_batch=4,
@@ -151,8 +170,12 @@ def test_plan_rejects_bad_lengths_and_capacity():
 def test_layout_regions_are_ordered_and_aligned():
     cfg = pkv.make_config(32, 8, 128, 8192, 1, 8192, num_cus=256)
     lay = pkv.pkv_workspace_layout(cfg)
+    # the layout does not depend on the CU count (create must accept it on any device)
+    for cus in (1, 80, 256, 304):
+        other = pkv.pkv_workspace_layout(pkv.make_config(32, 8, 128, 8192, 1, 8192, num_cus=cus))
+        assert other.total_bytes == lay.total_bytes and other.max_items == lay.max_items
     offs = [lay.ctrl_off, lay.queue_off, lay.n_chunks_off, lay.part_off_off, lay.merge_rows_off,
             lay.items_off, lay.partial_o_off, lay.partial_lse_off, lay.arrive_off, lay.total_bytes]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
-    assert lay.max_items == 8 * 32
+    assert lay.max_items == 8 * (8192 // 64)      # ranges of at least 64 pages
     assert lay.partial_lse_off - lay.partial_o_off >= lay.max_items * 4 * 128 * 4

@@ -185,7 +185,7 @@ def test_full_size_sampled_units(name, merge):
     run = Run(wl, poison=True, merge_mode=merge)
     o, l = run.decode()
     info = run.info
-    ref = wq.build_queue(wl.ctx_lens, wl.num_kv_heads, run.dec.query()["num_cus"], 4096)
+    ref = wq.build_queue(wl.ctx_lens, wl.num_kv_heads, run.dec.query()["num_cus"], 0)
     assert info.n_items == len(ref["items"]) and bool(info.split) == ref["split"]
     qb = workloads.bits_u16(run.q)
     G = wl.num_q_heads // wl.num_kv_heads
@@ -239,7 +239,7 @@ def test_queue_bytes_on_device_match_oracle(name):
     wl = workloads.CONFIGS[name]()
     run = Run(wl, poison=False)
     cus = run.dec.query()["num_cus"]
-    ref = wq.build_queue(wl.ctx_lens, wl.num_kv_heads, cus, 4096)
+    ref = wq.build_queue(wl.ctx_lens, wl.num_kv_heads, cus, 0)      # chunk mode "fit"
     for device_queue in (False, True):
         if device_queue:
             run.dec.build_queue_device(run.lens)
@@ -251,8 +251,45 @@ def test_queue_bytes_on_device_match_oracle(name):
         assert np.array_equal(got["part_off"], ref["part_off"])
         assert np.array_equal(got["merge_rows"], ref["merge_rows"])
         assert list(got["hdr"]) == [len(ref["items"]), len(ref["merge_rows"]), int(ref["split"]),
-                                    4096, wl.batch]
+                                    ref["chunk_tokens"], wl.batch]
     run.close()
+
+
+def test_device_queue_random_lengths_match_oracle():
+    # the device builder's bisection for chunk mode "fit", and fixed chunks,
+    # against the oracle on random batches (queue only; no K/V is read)
+    rng = np.random.default_rng(11)
+    for trial in range(40):
+        B = int(rng.integers(1, 300))
+        hkv = int(rng.choice([1, 2, 8]))
+        cus = int(rng.choice([8, 64, 256]))
+        chunk = int(rng.choice([0, 0, 512, 4096]))
+        policy = int(rng.integers(0, 3))
+        maxp = int(rng.integers(1, 3000))
+        lens = rng.integers(0, maxp * 16 + 1, size=B)
+        lens[rng.random(B) < 0.2] = 0
+        cfg = pkv.make_config(4 * hkv, hkv, 128, 64, B, maxp, policy=policy, kv_chunk_tokens=chunk,
+                              num_cus=cus)
+        dec = pkv.PagedDecoder(cfg)
+        try:
+            ref = wq.build_queue(lens.tolist(), hkv, cus, chunk, policy)
+            if len(ref["items"]) > dec.layout.max_items:
+                continue
+            dev_lens = torch.as_tensor(lens.astype(np.int32)).cuda()
+            dec.build_queue_device(dev_lens)
+            torch.cuda.synchronize()
+            lay, ws = dec.layout, dec.workspace
+            hdr = ws[lay.queue_off:lay.queue_off + 20].cpu().view(torch.int32).numpy()
+            n = int(hdr[0])
+            where = f"trial {trial}: B={B} hkv={hkv} cus={cus} chunk={chunk} policy={policy}"
+            assert list(hdr) == [len(ref["items"]), len(ref["merge_rows"]), int(ref["split"]),
+                                 ref["chunk_tokens"], B], where
+            items = ws[lay.items_off:lay.items_off + 16 * n].cpu().numpy().tobytes()
+            assert items == ref["items"].tobytes(), where
+            nch = ws[lay.n_chunks_off:lay.n_chunks_off + 4 * B].cpu().view(torch.int32).numpy()
+            assert np.array_equal(nch, ref["n_chunks"]), where
+        finally:
+            dec.close()
 
 
 def test_device_queue_decode_matches():

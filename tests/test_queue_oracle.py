@@ -120,3 +120,68 @@ def test_item_bytes_little_endian():
     assert int.from_bytes(raw[off + 6:off + 8], "little") == 17
     assert int.from_bytes(raw[off + 8:off + 12], "little") == 17 * 4096
     assert int.from_bytes(raw[off + 12:off + 16], "little") == min(70000, 18 * 4096)
+
+
+# Chunk mode "fit": pins by closed forms, independent of the search.
+
+def test_fit_chunk_one_row_is_the_ceiling_of_pages_over_the_budget():
+    # one row of n pages and a budget of K ranges: T = ceil(n / K) (floor 1 here)
+    for n, hkv, cus in [(8192, 8, 256), (8191, 8, 256), (100, 1, 7), (1, 4, 256), (33, 2, 8)]:
+        K = max(1, cus // hkv)
+        assert wq.fit_chunk([16 * n], hkv, cus, min_pages=1) == 16 * (-(-n // K))
+        assert wq.fit_chunk([16 * n - 5], hkv, cus, min_pages=1) == 16 * (-(-n // K))
+        assert wq.fit_chunk([16 * n], hkv, cus) == 16 * max(64, -(-n // K))
+
+
+def test_fit_chunk_equal_rows():
+    # B equal rows of n pages: each row gets floor(K / B) ranges, T = ceil(n / floor(K / B))
+    for B, n in [(2, 1000), (3, 64), (5, 17), (16, 4096)]:
+        K = 256 // 8
+        assert wq.fit_chunk([16 * n] * B, 8, 256, min_pages=1) == 16 * (-(-n // (K // B)))
+        assert wq.fit_chunk([16 * n] * B, 8, 256) == 16 * max(64, -(-n // (K // B)))
+
+
+def test_fit_chunk_fallback_and_edges():
+    assert wq.fit_chunk([], 8, 256, min_pages=1) == 16
+    assert wq.fit_chunk([0, 0], 8, 256, min_pages=1) == 16
+    assert wq.fit_chunk([], 8, 256) == 16 * 64
+    # more non-empty rows than the budget: no T fits, T = longest row
+    assert wq.fit_chunk([16 * 5] * 40, 8, 256, min_pages=1) == 16 * 5
+    assert wq.fit_chunk([16 * 500] * 40, 8, 256) == 16 * 500
+
+
+def test_fit_mode_on_the_workloads():
+    cus = 256
+    t = workloads.tiny()
+    q = wq.build_queue(t.ctx_lens, 1, cus, 0)
+    assert not q["split"] and len(q["items"]) == 1 and q["chunk_tokens"] == 1024
+    lc = workloads.long_context()
+    q = wq.build_queue(lc.ctx_lens, 8, cus, 0)
+    assert q["chunk_tokens"] == 4096 and len(q["items"]) == 256       # same as the fixed 4096
+    for seed in (workloads.MEASURE_SEED, workloads.CALIBRATION_SEED):
+        mx = workloads.mixed(seed)
+        q = wq.build_queue(mx.ctx_lens, 8, cus, 0)
+        C = q["chunk_tokens"]
+        assert q["split"] and len(q["items"]) <= cus                  # one round
+        check_invariants(q, list(mx.ctx_lens), 8, C)
+        # a range one page shorter would need a second round
+        pages = [-(-int(L) // 16) for L in mx.ctx_lens]
+        assert sum(-(-n // (C // 16 - 1)) for n in pages) * 8 > cus
+    sh = workloads.many_short()
+    q = wq.build_queue(sh.ctx_lens, 8, cus, 0)
+    assert not q["split"] and len(q["items"]) == 512
+
+
+def test_fit_mode_brute_force_small_grids():
+    # the fitted queue equals the fixed-chunk queue at the chunk it reports
+    for lens in itertools.product([0, 1, 16, 17, 1500, 5000], repeat=3):
+        for hkv, cus in [(1, 4), (2, 8), (1, 2)]:
+            q = wq.build_queue(list(lens), hkv, cus, 0, wq.POLICY_SPLIT)
+            C = q["chunk_tokens"]
+            got = [tuple(int(x) for x in it) for it in q["items"]]
+            assert got == brute_force(list(lens), hkv, C, True)
+            fits = sum(1 for L in lens if L) <= max(1, cus // hkv)
+            if fits:         # at most one range per workgroup
+                assert len(got) <= max(max(1, cus // hkv) * hkv, sum(1 for L in lens if L) * hkv)
+                if C > 1024:  # chosen by the bound, not the floor: one page less would not fit
+                    assert sum(-(-(-(-L // 16)) // (C // 16 - 1)) for L in lens) > max(1, cus // hkv)
