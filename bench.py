@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--loop-steps", type=int, default=200,
                     help="steps per run of the 56-session resident loop (0 skips the loop)")
     ap.add_argument("--loop-runs", type=int, default=3)
+    ap.add_argument("--ablations", action="store_true",
+                    help="also time the scheduling ablations: static vs atomic item assignment, "
+                         "and exact-length bucketed launches vs the compact queue")
     ap.add_argument("--profile-pass", action="store_true",
                     help="for hardware-counter runs: a few untimed decode steps of the workload, "
                          "then a 1 GiB copy probe of known size (the counter reference)")
@@ -56,7 +59,7 @@ def parse():
 
 
 def measure(torch, pkv, workloads, name, steps, warmup, order, wg_per_cu, copies, gate, say,
-            merge="fused"):
+            merge="fused", schedule=0):
     wl = workloads.CONFIGS[name]()
     dev = "cuda"
     q = wl.q(dev)
@@ -70,7 +73,7 @@ def measure(torch, pkv, workloads, name, steps, warmup, order, wg_per_cu, copies
     cfg = pkv.make_config(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages, wl.batch,
                           wl.max_pages_per_seq, scale=wl.scale,
                           order=pkv.PKV_ORDER_LPT if order == "lpt" else pkv.PKV_ORDER_CANONICAL,
-                          wg_per_cu=wg_per_cu,
+                          wg_per_cu=wg_per_cu, schedule=schedule,
                           merge_mode=pkv.PKV_MERGE_SEPARATE if merge == "separate" else pkv.PKV_MERGE_FUSED)
     stream = torch.cuda.current_stream()
     dec = pkv.PagedDecoder(cfg, stream=stream)
@@ -267,6 +270,113 @@ def measured_traffic(root):
     return int(rec["traffic_bytes_per_launch"])
 
 
+def measure_bucketed(torch, pkv, workloads, name, steps, warmup, say):
+    """Exact-length bucketed launches (the baseline the compact queue replaces):
+    rows sorted by length, one handle and one launch per distinct length, each
+    with its own queue built once; a step is every bucket's launch in turn on
+    one stream.  Returns the step rate and the launches and partial-state bytes
+    per step."""
+    from oracle import paged_attention as pa
+    wl = workloads.CONFIGS[name]()
+    dev = "cuda"
+    lens = np.asarray(wl.ctx_lens)
+    order = np.argsort(lens, kind="stable")
+    idx = torch.as_tensor(order, device=dev)
+    q = wl.q(dev)[idx].contiguous()
+    bt = wl.block_table_t(dev)[idx].contiguous()
+    k, v = wl.pool("k", dev, False), wl.pool("v", dev, False)
+    slens = lens[order]
+    lens_dev = torch.as_tensor(slens.astype(np.int32), device=dev)
+    out = torch.empty(wl.batch, wl.num_q_heads, wl.head_dim, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(wl.batch, wl.num_q_heads, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    buckets, b0 = [], 0
+    for b in range(1, wl.batch + 1):
+        if b == wl.batch or slens[b] != slens[b0]:
+            buckets.append((b0, b))
+            b0 = b
+    decs, tens, launches, partial = [], [], 0, 0
+    for (a, b) in buckets:
+        cfg = pkv.make_config(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages, b - a,
+                              wl.max_pages_per_seq, scale=wl.scale)
+        dec = pkv.PagedDecoder(cfg, stream=stream)
+        info = dec.build_queue(slens[a:b].tolist())
+        launches += info.launches_per_step
+        partial += info.partial_bytes
+        decs.append(dec)
+        tens.append(pkv.make_tensors(q[a:b], k, v, bt[a:b], lens_dev[a:b], out[a:b], lse[a:b],
+                                     batch=b - a, block_table_stride=bt.shape[1]))
+
+    def step():
+        for dec, t in zip(decs, tens):
+            pkv.pkv_decode(dec.handle, t, stream)
+
+    step()
+    torch.cuda.synchronize()
+    for dec in decs:
+        dec.query()
+    # parity gate on the first and the last row of the original order
+    o = out.float().cpu().numpy()
+    l = lse.cpu().numpy()
+    qb = workloads.bits_u16(wl.q("cpu"))
+    G = wl.num_q_heads // wl.num_kv_heads
+    pos = {int(r): i for i, r in enumerate(order)}
+    for b, hk in [(0, 0), (wl.batch - 1, wl.num_kv_heads - 1)]:
+        L = int(wl.ctx_lens[b])
+        npg = -(-L // 16)
+        pg = wl.block_table[b, :npg]
+        ks = workloads.bits_u16(wl.pool_slabs("k", pg, hk))[:, None]
+        vs = workloads.bits_u16(wl.pool_slabs("v", pg, hk))[:, None]
+        ro, rl = pa.range_state(qb[b:b + 1, hk * G:(hk + 1) * G], ks, vs, np.arange(npg)[None], 0, 0, 0,
+                                L, wl.scale, 16)
+        i = pos[b]
+        err = np.abs(o[i, hk * G:(hk + 1) * G] - ro).max()
+        lerr = np.abs(l[i, hk * G:(hk + 1) * G] - rl).max()
+        if not (err <= 2e-2 and lerr <= 2e-2):
+            raise SystemExit(f"bucketed parity gate failed on {name} unit {(b, hk)}: {err:.3e} {lerr:.3e}")
+    for _ in range(warmup):
+        step()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    for dec in decs:
+        dec.close()
+    return {"buckets": len(buckets), "launches_per_step": launches, "partial_bytes": partial,
+            "ms_per_step": ms, "gbs": wl.kv_bytes / (ms * 1e-3) / 1e9}
+
+
+def ablations(torch, pkv, workloads, args, say):
+    """Scheduling ablations (static vs atomic item assignment; exact-length
+    bucketed launches vs the compact queue) on the one-shot workloads."""
+    res = {"schedule": {}, "bucketed": {}}
+    steps = max(args.steps // 2, 10)
+    for name in ("long", "mixed", "short"):
+        row = {}
+        for label, sched in (("atomic", pkv.PKV_SCHEDULE_ATOMIC), ("static", pkv.PKV_SCHEDULE_STATIC)):
+            r, _ = measure(torch, pkv, workloads, name, steps, args.warmup, args.order, args.wg_per_cu,
+                           args.copies, not args.no_gate, say, args.merge, sched)
+            row[label] = {"gbs": round(r["gbs"], 1), "decode_us": round(r["decode_ms_mean"] * 1e3, 2)}
+        res["schedule"][name] = row
+        say(f"ablation {name}: atomic {row['atomic']['gbs']} GB/s, static {row['static']['gbs']} GB/s")
+    for name in ("mixed", "short"):
+        r, _ = measure(torch, pkv, workloads, name, steps, args.warmup, args.order, args.wg_per_cu,
+                       args.copies, False, say, args.merge)
+        bk = measure_bucketed(torch, pkv, workloads, name, steps, args.warmup, say)
+        res["bucketed"][name] = {
+            "compact": {"launches_per_step": r["launches_per_step"], "partial_bytes": r["partial_bytes"],
+                        "gbs": round(r["gbs"], 1), "ms_per_step": round(r["ms_per_step"], 4)},
+            "bucketed": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in bk.items()}}
+        say(f"ablation {name}: compact queue {r['gbs']:.1f} GB/s in {r['launches_per_step']} launch(es); "
+            f"bucketed {bk['gbs']:.1f} GB/s in {bk['launches_per_step']} launches ({bk['buckets']} lengths)")
+    return res
+
+
 def cpu_baseline(workloads, wl, seconds, say):
     """The oracle as it stands, on whole (sequence, KV head) units of the same
     workload, repeated pass after pass for about `seconds` of CPU time."""
@@ -376,6 +486,7 @@ def main():
     if args.loop_steps > 0:
         loop = measure_loop(torch, pkv, workloads, args.loop_steps, args.loop_runs,
                             not args.no_gate, say)
+    abl = ablations(torch, pkv, workloads, args, say) if args.ablations else None
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(workloads, wl, args.cpu_seconds, say)
@@ -412,6 +523,7 @@ def main():
         "session_loop_p99_ms": loop["p99_ms"] if loop else None,
         "session_loop": loop,
         "other_workloads": others,
+        "ablations": abl,
         "host_wall_ms_per_step": round(main_res["host_wall_ms_per_step"], 4),
     }
     print(json.dumps(line), flush=True)

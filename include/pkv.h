@@ -84,6 +84,15 @@ enum { PKV_POLICY_AUTO = 0, PKV_POLICY_NO_SPLIT = 1, PKV_POLICY_SPLIT = 2 };
  * of the canonical list by item length, longest first. */
 enum { PKV_ORDER_CANONICAL = 0, PKV_ORDER_LPT = 1 };
 
+/* Item-to-workgroup assignment in one-shot launches.  ATOMIC (default): the
+ * PersistentKV page's work queue -- workgroup g runs item g first, then claims
+ * further items with an atomic counter as it finishes.  STATIC: the WPK note's
+ * compiled schedule -- workgroup g runs items g, g + grid, g + 2 grid, ...
+ * with no claims.  Every item is computed the same way in both, so outputs
+ * are identical; only the time differs (a scheduling ablation).  The resident
+ * loop always claims. */
+enum { PKV_SCHEDULE_ATOMIC = 0, PKV_SCHEDULE_STATIC = 1 };
+
 /* How split rows are merged.  FUSED: inside the decode kernel, the last
  * workgroup to finish a split (row, KV head) merges its partial states (one
  * launch per step).  SEPARATE: a second kernel merges every split row (the
@@ -117,7 +126,8 @@ typedef struct pkv_config {
     int32_t persistent;         /* 0: one launch per pkv_decode; 1: resident loop (below) */
     int32_t num_layers;         /* resident loop: layers per step (0 -> 1) */
     int32_t timeout_ms;         /* resident loop: wait limit, device and host (0 -> 10000) */
-    int32_t reserved[5];        /* must be zero */
+    int32_t schedule;           /* PKV_SCHEDULE_* (one-shot launches) */
+    int32_t reserved[4];        /* must be zero */
 } pkv_config;
 
 typedef struct pkv_tensors {

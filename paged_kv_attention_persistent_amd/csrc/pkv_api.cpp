@@ -92,6 +92,7 @@ DecodeParams make_params(const pkv_handle* h, const pkv_tensors* t) {
     p.head_dim = h->r.d;
     p.coherent_out = 0;
     p.static_first = 1;
+    p.static_sched = h->r.schedule == PKV_SCHEDULE_STATIC ? 1 : 0;
     p.coherent_in = 0;
     p.host_error = h->host_err_dev;
     p.batch = t ? t->batch : 0;

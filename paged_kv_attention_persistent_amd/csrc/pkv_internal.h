@@ -115,7 +115,7 @@ struct Resolved {
     int hq, hkv, g, d, page, num_pages, max_batch, max_pages_per_seq;
     float scale;
     int policy, order, chunk, num_cus, max_items, wg_per_cu, merge_mode;
-    int persistent, num_layers, timeout_ms;
+    int persistent, num_layers, timeout_ms, schedule;
 };
 
 pkv_status resolve_config(const pkv_config* cfg, int device_cus, Resolved* r, const char** why);
@@ -162,6 +162,7 @@ struct DecodeParams {
     int32_t max_tokens;         // max_pages_per_seq * page size
     int32_t max_items;          // capacity of items and partial slots
     int32_t fused_merge;        // 1: last arriver merges inside the decode kernel
+    int32_t static_sched;       // 1: workgroup g runs items g, g + grid, ... (no claims)
     float scale_log2;           // scale * log2(e)
 };
 

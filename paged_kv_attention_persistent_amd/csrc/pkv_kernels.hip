@@ -435,7 +435,9 @@ __device__ void merge_row(const DecodeParams& P, int b, int hk, int nc, int base
 // Claim the next item for this workgroup.  One-shot launches run a static
 // first round (workgroup i runs item i) and pop later items past it; the
 // resident loop pops every item (a workgroup claims work only while it runs).
-__device__ __forceinline__ uint32_t pop_next(const DecodeParams& P) {
+// Under the static schedule the next item is simply idx + grid.
+__device__ __forceinline__ uint32_t pop_next(const DecodeParams& P, uint32_t idx) {
+    if (P.static_sched) return idx + gridDim.x;
     return (P.static_first ? gridDim.x : 0u) + atomicAdd(P.head, 1u);
 }
 
@@ -491,7 +493,7 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, const ItemRe
     if (!it.ok) {                                  // uniform over the workgroup
         if (tid == 0) {
             report(P.ctrl, P.host_error, PKV_DEVERR_BAD_ITEM, it.idx);
-            nxt = pop_next(P);
+            nxt = pop_next(P, it.idx);
         }
         return;
     }
@@ -550,7 +552,7 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, const ItemRe
     // barrier below, so its round trip overlaps the reductions and the wait
     // for the other waves.
     uint32_t popped = 0;
-    if (tid == 0) {
+    if (tid == 0 && !P.static_sched) {
         // A lane-private copy of the address keeps the compiler from turning
         // this one-lane atomic into its wave-wide form, which reads the
         // result at once.
@@ -584,7 +586,7 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, const ItemRe
     __syncthreads();
     if (tid == 0) {
         __asm__ volatile("" : "+v"(popped));     // the claim's first use: after the barrier
-        nxt = (P.static_first ? gridDim.x : 0u) + popped;
+        nxt = P.static_sched ? it.idx + gridDim.x : (P.static_first ? gridDim.x : 0u) + popped;
     }
 
     // Combine the 8 waves; each thread finishes two adjacent dims of one head.
@@ -908,7 +910,7 @@ __global__ __launch_bounds__(kThreads) void resident_kernel(LoopParams L) {
         const uint32_t total = n_items * (uint32_t)n_layers;
         const uint32_t units = total + 1;        // + one unit: rows with no tokens
         bool ok = true;
-        if (tid == 0) sm.next = pop_next(P);     // every unit is popped
+        if (tid == 0) sm.next = pop_next(P, 0);  // every unit is popped
         __syncthreads();
         uint32_t idx = __builtin_amdgcn_readfirstlane(sm.next);
         while (idx < units) {
@@ -983,7 +985,7 @@ __global__ __launch_bounds__(kThreads) void resident_kernel(LoopParams L) {
                     }
                     __syncthreads();
                 }
-                if (tid == 0) nxt = pop_next(P);
+                if (tid == 0) nxt = pop_next(P, idx);
             }
             // publish completion: this unit's outputs are stored, then count it
             __builtin_amdgcn_s_waitcnt(0x0F70);

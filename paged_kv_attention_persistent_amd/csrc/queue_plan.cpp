@@ -24,7 +24,7 @@ pkv_status resolve_config(const pkv_config* cfg, int device_cus, Resolved* r, co
     *why = "";
     if (!cfg || !r) { *why = "null config"; return PKV_ERR_INVALID_ARG; }
     if (cfg->struct_size != sizeof(pkv_config)) { *why = "pkv_config.struct_size mismatch"; return PKV_ERR_INVALID_ARG; }
-    for (int i = 0; i < 5; ++i)
+    for (int i = 0; i < 4; ++i)
         if (cfg->reserved[i]) { *why = "reserved config fields must be zero"; return PKV_ERR_INVALID_ARG; }
     if (cfg->num_q_heads <= 0 || cfg->num_kv_heads <= 0 || cfg->num_q_heads % cfg->num_kv_heads) {
         *why = "num_q_heads must be a positive multiple of num_kv_heads"; return PKV_ERR_INVALID_ARG;
@@ -85,6 +85,11 @@ pkv_status resolve_config(const pkv_config* cfg, int device_cus, Resolved* r, co
     r->timeout_ms = cfg->timeout_ms == 0 ? 10000 : cfg->timeout_ms;
     if (r->timeout_ms < 1 || r->timeout_ms > 3600000) { *why = "timeout_ms must be 1..3600000"; return PKV_ERR_INVALID_ARG; }
     if (r->persistent && r->wg_per_cu != 1) { *why = "the resident loop runs one workgroup per CU"; return PKV_ERR_INVALID_ARG; }
+    if (cfg->schedule != PKV_SCHEDULE_ATOMIC && cfg->schedule != PKV_SCHEDULE_STATIC) {
+        *why = "unknown schedule"; return PKV_ERR_INVALID_ARG;
+    }
+    if (r->persistent && cfg->schedule != PKV_SCHEDULE_ATOMIC) { *why = "the resident loop claims items atomically"; return PKV_ERR_INVALID_ARG; }
+    r->schedule = cfg->schedule;
     if ((int64_t)r->max_items * r->num_layers > ((int64_t)1 << 31) / (4 * r->g * r->d)) {
         *why = "partial-state storage too large"; return PKV_ERR_CAPACITY;
     }

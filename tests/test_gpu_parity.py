@@ -402,3 +402,19 @@ def test_fused_merge_bitwise_equals_separate_merge_over_repeats():
     assert a.dec.query()["error_code"] == 0
     a.close()
     b.close()
+
+
+@pytest.mark.parametrize("name", ["long", "mixed", "short"])
+def test_static_schedule_equals_atomic_bitwise(name):
+    # the schedule only moves items between workgroups; each item is computed
+    # the same way, so every output bit must agree
+    wl = workloads.CONFIGS[name]()
+    outs = []
+    for schedule in (pkv.PKV_SCHEDULE_ATOMIC, pkv.PKV_SCHEDULE_STATIC):
+        run = Run(wl, poison=True, schedule=schedule)
+        o, l = run.decode()
+        outs.append((o, l))
+        assert run.dec.query()["items_done"] >= run.info.n_items
+        run.close()
+    say(f"{name}: static vs atomic schedule, {outs[0][0].size} outputs compared")
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
