@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--loop-steps", type=int, default=200,
                     help="steps per run of the 56-session resident loop (0 skips the loop)")
     ap.add_argument("--loop-runs", type=int, default=3)
+    ap.add_argument("--no-loop-append", action="store_true",
+                    help="skip the second loop measurement, with the KV append inside each step")
     ap.add_argument("--ablations", action="store_true",
                     help="also time the scheduling ablations: static vs atomic item assignment, "
                          "and exact-length bucketed launches vs the compact queue")
@@ -152,14 +154,18 @@ def measure(torch, pkv, workloads, name, steps, warmup, order, wg_per_cu, copies
     return res, wl
 
 
-def measure_loop(torch, pkv, workloads, steps, runs, gate, say):
+def measure_loop(torch, pkv, workloads, steps, runs, gate, say, append=False):
     """The 56-session resident loop: 32 layers of 32/8-head, head_dim 128
     decode attention per session, contexts U[2048, 16384] growing one token
     per step.  The resident kernel is launched once per run; per step the host
     plans the queue, publishes the step and waits for its completion.  Step
-    latency = pkv_decode wall time (publish -> completion observed)."""
+    latency = pkv_decode wall time (publish -> completion observed).  With
+    append, each step also writes every session's newest token into the
+    cache inside the same kernel (pages from a free list), and the cache
+    starts with the tokens before step 0 only."""
     from oracle import paged_attention as pa
-    sl = workloads.session_loop(steps=max(steps, 3))
+    sl = workloads.session_loop(steps=max(steps, 3), append=append)
+    tag = "loop+append" if append else "loop"
     dev = "cuda"
     t0 = time.perf_counter()
     k, v, q = sl.pools("k", dev), sl.pools("v", dev), sl.queries(dev)
@@ -169,27 +175,36 @@ def measure_loop(torch, pkv, workloads, steps, runs, gate, say):
     lse = torch.empty((sl.steps, sl.layers, sl.sessions, sl.num_q_heads), dtype=torch.float32,
                       device=dev)
     lens = torch.zeros(sl.sessions, dtype=torch.int32, device=dev)
+    new_k = sl.new_kv("k", dev) if append else None
+    new_v = sl.new_kv("v", dev) if append else None
     torch.cuda.synchronize()
-    say(f"loop inputs generated in {time.perf_counter() - t0:.1f} s "
+    say(f"{tag} inputs generated in {time.perf_counter() - t0:.1f} s "
         f"({2 * k.numel() * 2 / 1e9:.1f} GB of K/V)")
     S, H, D = sl.sessions, sl.num_q_heads, sl.head_dim
     strides = (S * H * D, sl.pages_per_layer * sl.num_kv_heads * 16 * D, S * sl.max_pages,
                S * H * D, S * H)
     cfg = pkv.make_config(H, sl.num_kv_heads, D, sl.pages_per_layer, S, sl.max_pages,
-                          scale=sl.scale, persistent=1, num_layers=sl.layers, timeout_ms=20000)
+                          scale=sl.scale, persistent=1, num_layers=sl.layers, timeout_ms=20000,
+                          append=1 if append else 0)
     G = H // sl.num_kv_heads
 
     def one_run(n):
+        # every run starts from the same cache: a run rewrites the rows and
+        # block-table entries the previous run appended with the same values
         stream = torch.cuda.Stream()
         dec = pkv.PagedDecoder(cfg, stream=stream)
+        if append:
+            pkv.pkv_loop_set_free_pages(dec.handle, sl.free_pages)
         lat, plan = [], []
         try:
             for t in range(n):
                 a = time.perf_counter()
                 info = dec.build_queue(sl.ctx_lens(t))
                 b = time.perf_counter()
+                extra = dict(new_k=new_k[t], new_v=new_v[t], layer_stride_new=S * sl.num_kv_heads * D) \
+                    if append else {}
                 tens = pkv.make_tensors(q[t], k, v, bt, lens, out[t], lse[t], batch=S,
-                                        block_table_stride=sl.max_pages, layer_strides=strides)
+                                        block_table_stride=sl.max_pages, layer_strides=strides, **extra)
                 pkv.pkv_decode(dec.handle, tens, stream)
                 c = time.perf_counter()
                 plan.append(b - a)
@@ -209,9 +224,14 @@ def measure_loop(torch, pkv, workloads, steps, runs, gate, say):
                 layer, s, hk = int(rng.integers(sl.layers)), int(rng.integers(S)), int(rng.integers(sl.num_kv_heads))
                 L = int(sl.ctx_lens(t)[s])
                 npg = -(-L // 16)
-                pg = sl.block_tables[layer, s, :npg]
-                ks = workloads.bits_u16(sl.slabs("k", layer, pg, hk))[:, None]
-                vs = workloads.bits_u16(sl.slabs("v", layer, pg, hk))[:, None]
+
+                def paged(which):
+                    rows = workloads.bits_u16(sl.token_rows(which, t, layer, s, hk))
+                    full = np.zeros((npg * 16, D), dtype=rows.dtype)
+                    full[:L] = rows
+                    return full.reshape(npg, 1, 16, D)
+
+                ks, vs = paged("k"), paged("v")
                 qg = workloads.bits_u16(sl.query_unit(t, layer, s))[None, hk * G:(hk + 1) * G]
                 ro, rl = pa.range_state(qg, ks, vs, np.arange(npg)[None], 0, 0, 0, L, sl.scale, 16)
                 err = np.abs(o[t, layer, s, hk * G:(hk + 1) * G] - ro)
@@ -224,15 +244,15 @@ def measure_loop(torch, pkv, workloads, steps, runs, gate, say):
 
     if gate:                                   # parity gate before timing
         one_run(3)
-        say(f"loop parity gate passed (steps 0-2, max abs err {check([0, 1, 2]):.2e})")
+        say(f"{tag} parity gate passed (steps 0-2, max abs err {check([0, 1, 2]):.2e})")
     runs_out = []
     for r in range(runs):
         lat, plan, info = one_run(steps)
         runs_out.append(lat)
-        say(f"loop run {r}: p50 {np.median(lat):.3f} ms p99 {np.percentile(lat, 99):.3f} ms "
+        say(f"{tag} run {r}: p50 {np.median(lat):.3f} ms p99 {np.percentile(lat, 99):.3f} ms "
             f"max {lat.max():.3f} ms; host planning p50 {np.median(plan):.3f} ms")
     if gate:
-        say(f"loop parity after timing (steps 0, {steps // 2}, {steps - 1}): max abs err "
+        say(f"{tag} parity after timing (steps 0, {steps // 2}, {steps - 1}): max abs err "
             f"{check([0, steps // 2, steps - 1]):.2e}")
     allv = np.concatenate(runs_out)
     kv = np.array([sl.kv_bytes(t) for t in range(steps)])
@@ -246,8 +266,8 @@ def measure_loop(torch, pkv, workloads, steps, runs, gate, say):
            "kv_gb_per_step_mean": round(float(kv.mean() / 1e9), 3),
            "kv_gbs_median": round(float(np.median(gbs)), 1),
            "pct_of_hbm_peak_median": round(float(np.median(gbs)) / HBM_PEAK_GBS * 100, 2),
-           "launches_per_step": 0}
-    del k, v, q, out, lse
+           "launches_per_step": 0, "append": bool(append)}
+    del k, v, q, out, lse, new_k, new_v
     torch.cuda.empty_cache()
     return res
 
@@ -482,10 +502,13 @@ def main():
                                           "launches_per_step")}
         others[name]["pct_of_hbm_peak"] = 100.0 * r["gbs"] / HBM_PEAK_GBS
         say(f"{name}: {r['gbs']:.1f} GB/s per step, decode {r['decode_gbs']:.1f} GB/s")
-    loop = None
+    loop = loop_append = None
     if args.loop_steps > 0:
         loop = measure_loop(torch, pkv, workloads, args.loop_steps, args.loop_runs,
                             not args.no_gate, say)
+        if not args.no_loop_append:
+            loop_append = measure_loop(torch, pkv, workloads, args.loop_steps, args.loop_runs,
+                                       not args.no_gate, say, append=True)
     abl = ablations(torch, pkv, workloads, args, say) if args.ablations else None
     cpu = None
     if args.cpu_seconds > 0:
@@ -522,6 +545,7 @@ def main():
         "cpu_baseline": cpu,
         "session_loop_p99_ms": loop["p99_ms"] if loop else None,
         "session_loop": loop,
+        "session_loop_append": loop_append,
         "other_workloads": others,
         "ablations": abl,
         "host_wall_ms_per_step": round(main_res["host_wall_ms_per_step"], 4),

@@ -127,7 +127,11 @@ typedef struct pkv_config {
     int32_t num_layers;         /* resident loop: layers per step (0 -> 1) */
     int32_t timeout_ms;         /* resident loop: wait limit, device and host (0 -> 10000) */
     int32_t schedule;           /* PKV_SCHEDULE_* (one-shot launches) */
-    int32_t reserved[4];        /* must be zero */
+    int32_t append;             /* resident loop: 1 -> each step first writes every session's
+                                   newest token (K/V from pkv_tensors.new_k / new_v) into the
+                                   cache, taking a page from the free list when the token
+                                   opens a page (see pkv_loop_set_free_pages) */
+    int32_t reserved[3];        /* must be zero */
 } pkv_config;
 
 typedef struct pkv_tensors {
@@ -145,6 +149,12 @@ typedef struct pkv_tensors {
      * l + 1 of q, of each pool, of the block table, of out and of lse (the
      * same queue serves every layer).  Ignored when num_layers is 1. */
     int64_t layer_stride_q, layer_stride_kv, layer_stride_bt, layer_stride_out, layer_stride_lse;
+    /* Resident loop with append = 1: the K and V of each session's newest token
+     * (token ctx_lens[b] - 1), bf16 [B][Hkv][D] per layer, layer l at
+     * new_k + l * layer_stride_new elements (likewise new_v).  Null otherwise. */
+    const void* new_k;
+    const void* new_v;
+    int64_t layer_stride_new;
 } pkv_tensors;
 
 typedef struct pkv_queue_info {
@@ -250,6 +260,25 @@ PKV_API pkv_status pkv_decode(pkv_handle* h, const pkv_tensors* t, void* stream)
  * before and right after the persistent decode kernel (not the merge).  Pass
  * nulls to stop recording. */
 PKV_API pkv_status pkv_set_decode_events(pkv_handle* h, void* before, void* after);
+
+/* KV append in the resident loop (config append = 1; the next step after
+ * the paged attention itself in a decode step, GPUOS page, the key-value cache
+ * updates its persistent workers serve).  At every step the session's newest
+ * token, index ctx_lens[b] - 1 of the queue built for the step, is written
+ * into the cache before attention reads it: row (token mod P) of page
+ * block_table[b][token / P] of every layer's pools, from new_k / new_v.  When
+ * the token opens a new page (token mod P == 0) the step takes the next page
+ * id from the free list and also writes it into block_table[b][token / P] of
+ * every layer (a page id indexes every layer's pool alike).  The library owns
+ * the free list: pkv_loop_set_free_pages replaces it with a copy of
+ * pages[0..n) (ids in [0, num_pages), taken in that order); call it before
+ * the first step or between steps.  A step that needs more pages than are
+ * left fails with PKV_ERR_CAPACITY before anything is published.
+ * PKV_ERR_STATE unless the handle runs the loop with append = 1. */
+PKV_API pkv_status pkv_loop_set_free_pages(pkv_handle* h, const int32_t* pages, int32_t n);
+
+/* Pages left on the append free list (into *n). */
+PKV_API pkv_status pkv_loop_free_pages(const pkv_handle* h, int32_t* n);
 
 /* Optional per-item trace (diagnostics): when buf (device memory, 32 bytes x
  * capacity) is set, every decode launch writes, for each item it runs,

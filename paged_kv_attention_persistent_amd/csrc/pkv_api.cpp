@@ -13,6 +13,7 @@
 #include <chrono>
 #include <string>
 #include <thread>
+#include <vector>
 
 #include "pkv_internal.h"
 
@@ -52,6 +53,11 @@ struct pkv_handle {
     uint64_t slot_bytes = 0;
     uint32_t epoch = 0;                 // last published step
     bool loop_running = false;
+    // append: the free list (taken in order from free_head) and the lengths of
+    // the queue built for the next step
+    std::vector<int32_t> free_pages;
+    size_t free_head = 0;
+    std::vector<int32_t> lens;
     std::string last_error;
 };
 
@@ -107,11 +113,11 @@ DecodeParams make_params(const pkv_handle* h, const pkv_tensors* t) {
     return p;
 }
 
-// Offset of the queue region inside a host slot (after the step descriptor).
-constexpr uint64_t kSlotQueue = sizeof(LoopDesc);
+// A host slot: the step descriptor, the append page grants, then the queue.
+uint64_t slot_queue_off(const pkv_handle* h) { return sizeof(LoopDesc) + loop_grant_bytes(h->r); }
 
 unsigned char* slot_queue(pkv_handle* h, uint32_t epoch) {
-    return h->slots + (uint64_t)(epoch & 1u) * h->slot_bytes + kSlotQueue;
+    return h->slots + (uint64_t)(epoch & 1u) * h->slot_bytes + slot_queue_off(h);
 }
 
 pkv_status start_loop(pkv_handle* h) {
@@ -134,11 +140,14 @@ pkv_status start_loop(pkv_handle* h) {
     lp.lctrl = h->lctrl_dev;
     lp.slots = h->slots_dev;
     lp.slot_bytes = h->slot_bytes;
-    lp.q_hdr_off = kSlotQueue;
-    lp.q_nch_off = kSlotQueue + (h->lay.n_chunks_off - h->lay.queue_off);
-    lp.q_poff_off = kSlotQueue + (h->lay.part_off_off - h->lay.queue_off);
-    lp.q_mrows_off = kSlotQueue + (h->lay.merge_rows_off - h->lay.queue_off);
-    lp.q_items_off = kSlotQueue + (h->lay.items_off - h->lay.queue_off);
+    const uint64_t q0 = slot_queue_off(h);
+    lp.q_hdr_off = q0;
+    lp.q_nch_off = q0 + (h->lay.n_chunks_off - h->lay.queue_off);
+    lp.q_poff_off = q0 + (h->lay.part_off_off - h->lay.queue_off);
+    lp.q_mrows_off = q0 + (h->lay.merge_rows_off - h->lay.queue_off);
+    lp.q_items_off = q0 + (h->lay.items_off - h->lay.queue_off);
+    lp.grant_off = sizeof(LoopDesc);
+    lp.append = h->r.append;
     lp.lglobal = reinterpret_cast<LoopGlobal*>(h->ws + h->lay.loop_off);
     lp.mirror = h->ws + h->lay.loop_mirror_off;
     lp.counters = h->ws + h->lay.loop_off + sizeof(LoopGlobal);
@@ -176,7 +185,31 @@ pkv_status decode_loop(pkv_handle* h, const pkv_tensors* t) {
         __atomic_load_n(&h->lctrl->exit_reason, __ATOMIC_ACQUIRE) != 0)
         return fail(h, PKV_ERR_TIMEOUT, "resident kernel has exited (idle or wait limit)");
     const uint32_t e = h->epoch + 1;
-    LoopDesc* d = reinterpret_cast<LoopDesc*>(h->slots + (uint64_t)(e & 1u) * h->slot_bytes);
+    unsigned char* slot = h->slots + (uint64_t)(e & 1u) * h->slot_bytes;
+    LoopDesc* d = reinterpret_cast<LoopDesc*>(slot);
+    if (h->r.append) {
+        // page grants for the rows whose newest token opens a page, taken
+        // from the free list in order; nothing is published if it runs out
+        if (!t->new_k || !t->new_v || !aligned(t->new_k, 4) || !aligned(t->new_v, 4))
+            return fail(h, PKV_ERR_INVALID_ARG, "append needs new_k and new_v (4-byte aligned)");
+        if ((int)h->lens.size() != t->batch) return fail(h, PKV_ERR_STATE, "batch differs from the built queue");
+        int32_t* grant = reinterpret_cast<int32_t*>(slot + sizeof(LoopDesc));
+        size_t need = 0;
+        for (int b = 0; b < t->batch; ++b)
+            need += (h->lens[b] >= 1 && (h->lens[b] - 1) % h->r.page == 0) ? 1 : 0;
+        if (h->free_head + need > h->free_pages.size())
+            return fail(h, PKV_ERR_CAPACITY, "append free list exhausted");
+        for (int b = 0; b < t->batch; ++b) {
+            const bool opens = h->lens[b] >= 1 && (h->lens[b] - 1) % h->r.page == 0;
+            grant[b] = opens ? h->free_pages[h->free_head++] : -1;
+        }
+        d->new_k = static_cast<const uint16_t*>(t->new_k);
+        d->new_v = static_cast<const uint16_t*>(t->new_v);
+        d->ls_new = h->r.num_layers > 1 ? t->layer_stride_new : 0;
+    } else {
+        d->new_k = d->new_v = nullptr;
+        d->ls_new = 0;
+    }
     d->q = static_cast<const uint16_t*>(t->q);
     d->k_pool = static_cast<const uint16_t*>(t->k_pool);
     d->v_pool = static_cast<const uint16_t*>(t->v_pool);
@@ -356,6 +389,7 @@ PKV_API pkv_status pkv_build_queue(pkv_handle* h, const int32_t* ctx_lens_host, 
                                   reinterpret_cast<Item*>(st + (h->lay.items_off - q0)), h->r.max_items, &qi, &why);
         if (s != PKV_OK) return fail(h, s, why);
         qi.launches_per_step = 0;             // nothing is launched per step
+        h->lens.assign(ctx_lens_host, ctx_lens_host + batch);
         h->built = true;
         h->built_on_device = false;
         h->batch = batch;
@@ -473,6 +507,23 @@ PKV_API pkv_status pkv_set_decode_events(pkv_handle* h, void* before, void* afte
     if ((before == nullptr) != (after == nullptr)) return fail(h, PKV_ERR_INVALID_ARG, "set both events or neither");
     h->ev_before = static_cast<hipEvent_t>(before);
     h->ev_after = static_cast<hipEvent_t>(after);
+    return PKV_OK;
+}
+
+PKV_API pkv_status pkv_loop_set_free_pages(pkv_handle* h, const int32_t* pages, int32_t n) {
+    if (!h) return PKV_ERR_INVALID_ARG;
+    if (!h->r.persistent || !h->r.append) return fail(h, PKV_ERR_STATE, "free pages need a loop with append = 1");
+    if (n < 0 || (n > 0 && !pages)) return fail(h, PKV_ERR_INVALID_ARG, "bad free page list");
+    for (int32_t i = 0; i < n; ++i)
+        if (pages[i] < 0 || pages[i] >= h->r.num_pages) return fail(h, PKV_ERR_INVALID_ARG, "free page outside the pool");
+    h->free_pages.assign(pages, pages + n);
+    h->free_head = 0;
+    return PKV_OK;
+}
+
+PKV_API pkv_status pkv_loop_free_pages(const pkv_handle* h, int32_t* n) {
+    if (!h || !n) return PKV_ERR_INVALID_ARG;
+    *n = (int32_t)(h->free_pages.size() - h->free_head);
     return PKV_OK;
 }
 

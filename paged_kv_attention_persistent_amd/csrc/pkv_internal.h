@@ -79,11 +79,15 @@ struct LoopDesc {
     int32_t bt_stride;
     int32_t n_layers;
     uint32_t epoch;
-    int32_t pad[38];
+    const uint16_t* new_k;      // append: newest token's K / V, [B][Hkv][D] per layer
+    const uint16_t* new_v;
+    int64_t ls_new;
+    int32_t pad[32];
 };
 static_assert(sizeof(LoopDesc) == 256, "loop descriptor is 256 bytes");
 static_assert(offsetof(LoopDesc, batch) == 88 && offsetof(LoopDesc, bt_stride) == 92 &&
-              offsetof(LoopDesc, n_layers) == 96, "loop descriptor words read as 64-bit pairs");
+              offsetof(LoopDesc, n_layers) == 96 && offsetof(LoopDesc, new_k) == 104 &&
+              offsetof(LoopDesc, ls_new) == 120, "loop descriptor words read as 64-bit pairs");
 static_assert(offsetof(QHdr, n_merge_rows) == 4, "queue header words read as one 64-bit pair");
 
 // Device-memory mirror of the host control words, written by workgroup 0
@@ -115,13 +119,14 @@ struct Resolved {
     int hq, hkv, g, d, page, num_pages, max_batch, max_pages_per_seq;
     float scale;
     int policy, order, chunk, num_cus, max_items, wg_per_cu, merge_mode;
-    int persistent, num_layers, timeout_ms, schedule;
+    int persistent, num_layers, timeout_ms, schedule, append;
 };
 
 pkv_status resolve_config(const pkv_config* cfg, int device_cus, Resolved* r, const char** why);
 void compute_layout(const Resolved& r, pkv_layout* lay);
 uint64_t loop_counter_bytes(const Resolved& r);
 uint64_t loop_slot_bytes(const Resolved& r, const pkv_layout& lay);
+uint64_t loop_grant_bytes(const Resolved& r);      // append page grants in a slot, after LoopDesc
 
 // Host queue planner.  Writes the queue header, n_chunks, part_off, merge_rows
 // and items into the caller's arrays.  Returns PKV_OK or an error.
@@ -175,6 +180,8 @@ struct LoopParams {
     unsigned char* slots;       // device view of the two host queue slots
     uint64_t slot_bytes;
     uint64_t q_hdr_off, q_nch_off, q_poff_off, q_mrows_off, q_items_off;  // within a slot
+    uint64_t grant_off;         // append: int32 [max_batch] page grants within a slot
+    int32_t append;             // 1: write each row's newest token before attention
     LoopGlobal* lglobal;        // device mirror of the control words
     unsigned char* mirror;      // device copies of the two host slots (same layout)
     unsigned char* counters;    // LoopSlotCtr + done[max_batch], two slots

@@ -783,6 +783,45 @@ __device__ __forceinline__ ItemRef read_item_mirror(const DecodeParams& P, uint3
     return it;
 }
 
+__device__ __forceinline__ void st_agt(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// KV append (resident loop, append = 1): the item that ends at its row's
+// newest token j = te - 1 first writes that token's K and V for its head into
+// the cache, so no other workgroup depends on the write (a page lies inside
+// one range, ranges being whole pages).  When j opens a page the step's grant
+// for the row is the page id, and every head's item writes it into the block
+// table (the same value).  Stores are agent-coherent: later steps read the
+// row and the entry from other XCDs.  All threads of the workgroup call this.
+template <int D>
+__device__ void append_token(const DecodeParams& Q, const int32_t* grants, const ItemRef& it,
+                             const uint16_t* new_k, const uint16_t* new_v, int tid) {
+    const uint32_t j = it.te - 1;
+    const int pj = (int)(j / kPageSize), off = (int)(j % kPageSize);
+    uint32_t* btw = reinterpret_cast<uint32_t*>(const_cast<int32_t*>(Q.block_table) + (size_t)it.b * Q.bt_stride + pj);
+    int32_t page = off == 0 ? (int32_t)ld_agt(reinterpret_cast<const uint32_t*>(grants) + it.b)
+                            : (int32_t)ld_sys(btw);
+    page = __builtin_amdgcn_readfirstlane(page);
+    if ((uint32_t)page >= (uint32_t)Q.num_pages) {             // never write outside the pool
+        if (tid == 0) report(Q.ctrl, Q.host_error, PKV_DEVERR_PAGE_OOB, (uint32_t)page);
+        return;
+    }
+    if (off == 0 && tid == 0) st_agt(btw, (uint32_t)page);
+    const size_t row = (((size_t)page * Q.hkv + it.hk) * kPageSize + off) * D;
+    const size_t src = ((size_t)it.b * Q.hkv + it.hk) * D;
+    uint32_t* dk = reinterpret_cast<uint32_t*>(const_cast<uint16_t*>(Q.k_pool) + row);
+    uint32_t* dv = reinterpret_cast<uint32_t*>(const_cast<uint16_t*>(Q.v_pool) + row);
+    const uint32_t* sk = reinterpret_cast<const uint32_t*>(new_k + src);
+    const uint32_t* sv = reinterpret_cast<const uint32_t*>(new_v + src);
+    for (int t = tid; t < D / 2; t += kThreads) {
+        st_agt(dk + t, ld_sys(sk + t));
+        st_agt(dv + t, ld_sys(sv + t));
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);        // the writes are done before any wave reads the page
+    __syncthreads();
+}
+
 // Spin (thread 0) until *p >= target, the exit flag rises, or the limit.
 __device__ __forceinline__ bool wait_at_least(const uint32_t* p, uint32_t target, const LoopParams& L) {
     const uint64_t t0 = wall_clock64();
@@ -877,9 +916,9 @@ __global__ __launch_bounds__(kThreads) void resident_kernel(LoopParams L) {
         // shared through LDS.
         const unsigned char* slot = L.mirror + (uint64_t)(e & 1u) * L.slot_bytes;
         const LoopDesc* dsc = reinterpret_cast<const LoopDesc*>(slot);
-        __shared__ uint64_t s_desc[16];
-        if (tid < 14) {                           // 13 descriptor words + n_items | n_merge_rows << 32
-            const uint64_t* d64 = tid < 13 ? reinterpret_cast<const uint64_t*>(dsc) + tid
+        __shared__ uint64_t s_desc[17];
+        if (tid < 17) {                           // 16 descriptor words + n_items | n_merge_rows << 32
+            const uint64_t* d64 = tid < 16 ? reinterpret_cast<const uint64_t*>(dsc) + tid
                                            : reinterpret_cast<const uint64_t*>(slot + L.q_hdr_off);
             s_desc[tid] = ld_agt64(d64);
         }
@@ -899,13 +938,17 @@ __global__ __launch_bounds__(kThreads) void resident_kernel(LoopParams L) {
         P.batch = (int32_t)uni((uint32_t)s_desc[11]);
         P.bt_stride = (int32_t)uni((uint32_t)(s_desc[11] >> 32));
         const int n_layers = (int)uni((uint32_t)s_desc[12]);
+        const uint16_t* new_k = reinterpret_cast<const uint16_t*>(uni64(s_desc[13]));
+        const uint16_t* new_v = reinterpret_cast<const uint16_t*>(uni64(s_desc[14]));
+        const int64_t ls_new = (int64_t)uni64(s_desc[15]);
+        const int32_t* grants = reinterpret_cast<const int32_t*>(slot + L.grant_off);
         P.qhdr = reinterpret_cast<const QHdr*>(slot + L.q_hdr_off);
         P.n_chunks = reinterpret_cast<const int32_t*>(slot + L.q_nch_off);
         P.part_off = reinterpret_cast<const int32_t*>(slot + L.q_poff_off);
         P.merge_rows = reinterpret_cast<const int32_t*>(slot + L.q_mrows_off);
         P.items = reinterpret_cast<const Item*>(slot + L.q_items_off);
-        const uint32_t n_items = uni((uint32_t)s_desc[13]);
-        const uint32_t n_mrows = uni((uint32_t)(s_desc[13] >> 32));
+        const uint32_t n_items = uni((uint32_t)s_desc[16]);
+        const uint32_t n_mrows = uni((uint32_t)(s_desc[16] >> 32));
         P.head = &ctr->head;
         const uint32_t total = n_items * (uint32_t)n_layers;
         const uint32_t units = total + 1;        // + one unit: rows with no tokens
@@ -952,6 +995,8 @@ __global__ __launch_bounds__(kThreads) void resident_kernel(LoopParams L) {
                     __syncthreads();
                     if (s_exit) { ok = false; break; }
                 }
+                if (L.append && it.ok && it.chunk == it.nch - 1)
+                    append_token<D>(Q, grants, it, new_k + layer * ls_new, new_v + layer * ls_new, tid);
                 process_item<D, G>(Q, sm, it, nxt);
             } else {
                 // rows with no tokens take the neutral state, in every layer;

@@ -24,7 +24,7 @@ pkv_status resolve_config(const pkv_config* cfg, int device_cus, Resolved* r, co
     *why = "";
     if (!cfg || !r) { *why = "null config"; return PKV_ERR_INVALID_ARG; }
     if (cfg->struct_size != sizeof(pkv_config)) { *why = "pkv_config.struct_size mismatch"; return PKV_ERR_INVALID_ARG; }
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 3; ++i)
         if (cfg->reserved[i]) { *why = "reserved config fields must be zero"; return PKV_ERR_INVALID_ARG; }
     if (cfg->num_q_heads <= 0 || cfg->num_kv_heads <= 0 || cfg->num_q_heads % cfg->num_kv_heads) {
         *why = "num_q_heads must be a positive multiple of num_kv_heads"; return PKV_ERR_INVALID_ARG;
@@ -90,14 +90,20 @@ pkv_status resolve_config(const pkv_config* cfg, int device_cus, Resolved* r, co
     }
     if (r->persistent && cfg->schedule != PKV_SCHEDULE_ATOMIC) { *why = "the resident loop claims items atomically"; return PKV_ERR_INVALID_ARG; }
     r->schedule = cfg->schedule;
+    if (cfg->append != 0 && cfg->append != 1) { *why = "append must be 0 or 1"; return PKV_ERR_INVALID_ARG; }
+    if (cfg->append && !r->persistent) { *why = "append needs the resident loop"; return PKV_ERR_INVALID_ARG; }
+    r->append = cfg->append;
     if ((int64_t)r->max_items * r->num_layers > ((int64_t)1 << 31) / (4 * r->g * r->d)) {
         *why = "partial-state storage too large"; return PKV_ERR_CAPACITY;
     }
     return PKV_OK;
 }
 
+uint64_t loop_grant_bytes(const Resolved& r) { return align256(4ull * r.max_batch); }
+
 uint64_t loop_slot_bytes(const Resolved& r, const pkv_layout& lay) {
-    return align256(sizeof(LoopDesc) + (lay.items_off - lay.queue_off) + 16ull * r.max_items);
+    return align256(sizeof(LoopDesc) + loop_grant_bytes(r) + (lay.items_off - lay.queue_off) +
+                    16ull * r.max_items);
 }
 
 uint64_t loop_counter_bytes(const Resolved& r) {

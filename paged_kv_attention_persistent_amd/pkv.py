@@ -44,7 +44,8 @@ class pkv_config(C.Structure):
                 ("kv_chunk_tokens", C.c_int32), ("num_cus", C.c_int32),
                 ("max_items", C.c_int32), ("wg_per_cu", C.c_int32),
                 ("merge_mode", C.c_int32), ("persistent", C.c_int32), ("num_layers", C.c_int32),
-                ("timeout_ms", C.c_int32), ("schedule", C.c_int32), ("reserved", C.c_int32 * 4)]
+                ("timeout_ms", C.c_int32), ("schedule", C.c_int32), ("append", C.c_int32),
+                ("reserved", C.c_int32 * 3)]
 
 
 class pkv_tensors(C.Structure):
@@ -53,7 +54,8 @@ class pkv_tensors(C.Structure):
                 ("out", C.c_void_p), ("lse", C.c_void_p), ("batch", C.c_int32),
                 ("block_table_stride", C.c_int32), ("layer_stride_q", C.c_int64),
                 ("layer_stride_kv", C.c_int64), ("layer_stride_bt", C.c_int64),
-                ("layer_stride_out", C.c_int64), ("layer_stride_lse", C.c_int64)]
+                ("layer_stride_out", C.c_int64), ("layer_stride_lse", C.c_int64),
+                ("new_k", C.c_void_p), ("new_v", C.c_void_p), ("layer_stride_new", C.c_int64)]
 
 
 class pkv_queue_info(C.Structure):
@@ -113,6 +115,8 @@ SIGNATURES = {
     "pkv_debug_gather": (C.c_int32, [C.c_void_p, C.POINTER(pkv_tensors), C.c_int32,
                                      C.c_void_p, C.c_void_p, C.c_void_p]),
     "pkv_set_trace": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_int32]),
+    "pkv_loop_set_free_pages": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_int32]),
+    "pkv_loop_free_pages": (C.c_int32, [C.c_void_p, C.POINTER(C.c_int32)]),
     "pkv_copy_probe": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int32, C.c_void_p]),
     "pkv_read_probe": (C.c_int32, [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int32, C.c_void_p]),
 }
@@ -153,7 +157,7 @@ def make_config(num_q_heads, num_kv_heads, head_dim, num_pages, max_batch, max_p
                 page_size=16, scale=0.0, policy=PKV_POLICY_AUTO, order=PKV_ORDER_CANONICAL,
                 kv_chunk_tokens=0, num_cus=0, max_items=0, wg_per_cu=0,
                 merge_mode=PKV_MERGE_FUSED, persistent=0, num_layers=0,
-                timeout_ms=0, schedule=0) -> pkv_config:
+                timeout_ms=0, schedule=0, append=0) -> pkv_config:
     cfg = pkv_config()
     cfg.struct_size = C.sizeof(pkv_config)
     cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim = num_q_heads, num_kv_heads, head_dim
@@ -165,6 +169,7 @@ def make_config(num_q_heads, num_kv_heads, head_dim, num_pages, max_batch, max_p
     cfg.merge_mode = merge_mode
     cfg.persistent, cfg.num_layers, cfg.timeout_ms = persistent, num_layers, timeout_ms
     cfg.schedule = schedule
+    cfg.append = append
     return cfg
 
 
@@ -213,8 +218,10 @@ def pkv_build_queue_device(handle: int, ctx_lens_dev, stream=None) -> None:
 
 
 def make_tensors(q, k_pool, v_pool, block_table, ctx_lens, out, lse, batch=None,
-                 block_table_stride=0, layer_strides=None) -> pkv_tensors:
-    """layer_strides: (q, kv, bt, out, lse) element strides for layered tensors."""
+                 block_table_stride=0, layer_strides=None, new_k=None, new_v=None,
+                 layer_stride_new=0) -> pkv_tensors:
+    """layer_strides: (q, kv, bt, out, lse) element strides for layered tensors;
+    new_k / new_v: the newest token's K / V for a loop with append."""
     t = pkv_tensors()
     t.q, t.k_pool, t.v_pool = q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr()
     t.block_table = block_table.data_ptr()
@@ -225,6 +232,9 @@ def make_tensors(q, k_pool, v_pool, block_table, ctx_lens, out, lse, batch=None,
     if layer_strides is not None:
         (t.layer_stride_q, t.layer_stride_kv, t.layer_stride_bt, t.layer_stride_out,
          t.layer_stride_lse) = [int(x) for x in layer_strides]
+    if new_k is not None:
+        t.new_k, t.new_v = new_k.data_ptr(), new_v.data_ptr()
+        t.layer_stride_new = int(layer_stride_new)
     return t
 
 
@@ -289,6 +299,19 @@ def pkv_debug_gather(handle: int, tensors: pkv_tensors, item_index: int, k_out, 
                                   C.c_void_p(k_out.data_ptr()), C.c_void_p(v_out.data_ptr()),
                                   C.c_void_p(_stream_ptr(stream))),
            "pkv_debug_gather", C.c_void_p(handle))
+
+
+def pkv_loop_set_free_pages(handle: int, pages) -> None:
+    arr = np.ascontiguousarray(np.asarray(pages, dtype=np.int32))
+    _check(lib().pkv_loop_set_free_pages(C.c_void_p(handle), arr.ctypes.data_as(C.c_void_p), int(arr.size)),
+           "pkv_loop_set_free_pages", C.c_void_p(handle))
+
+
+def pkv_loop_free_pages(handle: int) -> int:
+    n = C.c_int32(0)
+    _check(lib().pkv_loop_free_pages(C.c_void_p(handle), C.byref(n)), "pkv_loop_free_pages",
+           C.c_void_p(handle))
+    return int(n.value)
 
 
 def pkv_set_trace(handle: int, buf=None) -> None:

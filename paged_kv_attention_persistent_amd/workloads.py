@@ -288,7 +288,12 @@ class SessionLoop:
     context is L0_s + t.  Pages for L0_s + steps tokens are allocated up front
     in every layer; each layer has its own randomly permuted pool.  K/V of the
     tokens a later step adds are generated with the rest (the append of new
-    tokens is not part of the step)."""
+    tokens is not part of the step).
+
+    With append=True the cache starts with the L0_s - 1 tokens before step 0
+    only (pages for them in every layer, every other row NaN) and step t
+    appends token L0_s - 1 + t from new_kv(); a token that opens a page takes
+    the next id of free_pages, in session order, the same id in every layer."""
     name: str
     sessions: int
     layers: int
@@ -302,6 +307,8 @@ class SessionLoop:
     seed: int
     page_size: int = 16
     scale: float = 0.0
+    append: bool = False
+    free_pages: np.ndarray = None     # append: page ids not in use before step 0
 
     def __post_init__(self):
         if self.scale == 0.0:
@@ -319,10 +326,67 @@ class SessionLoop:
             * self.head_dim * 2 * 2
 
     def pools(self, which: str, device) -> torch.Tensor:
-        """[layers][pages][Hkv][P][D] bf16 (one stream per tensor name)."""
+        """[layers][pages][Hkv][P][D] bf16 (one stream per tensor name).  With
+        append, rows that hold no token before step 0 are NaN."""
         t = torch.empty(self.layers, self.pages_per_layer, self.num_kv_heads, self.page_size,
                         self.head_dim, dtype=torch.bfloat16, device=device)
-        return fill_normal_bf16(t, self.seed, self.name + "/" + which)
+        t = fill_normal_bf16(t, self.seed, self.name + "/" + which)
+        if self.append:
+            P = self.page_size
+            valid = np.zeros((self.layers, self.pages_per_layer, P), dtype=bool)
+            lay = np.arange(self.layers)[:, None]
+            for s, L in enumerate(self.l0 - 1):
+                n = -(-int(L) // P)
+                if n == 0:
+                    continue
+                valid[lay, self.block_tables[:, s, :n - 1]] = True          # full pages
+                valid[np.arange(self.layers), self.block_tables[:, s, n - 1], :int(L) - (n - 1) * P] = True
+            bad = torch.as_tensor(~valid).to(device)[:, :, None, :, None].expand_as(t)
+            t.view(torch.int16)[bad] = 0x7FC0
+        return t
+
+    def new_kv(self, which: str, device) -> torch.Tensor:
+        """Append: K or V of each step's new token, [steps][layers][sessions][Hkv][D] bf16."""
+        t = torch.empty(self.steps, self.layers, self.sessions, self.num_kv_heads, self.head_dim,
+                        dtype=torch.bfloat16, device=device)
+        return fill_normal_bf16(t, self.seed, self.name + "/new_" + which)
+
+    def new_kv_unit(self, which: str, t: int, layer: int, s: int, kv_head: int) -> torch.Tensor:
+        """CPU regeneration of new_kv(which)[t][layer][s][kv_head] ([D])."""
+        D = self.head_dim
+        off = (((t * self.layers + layer) * self.sessions + s) * self.num_kv_heads + kv_head) * D
+        idx = torch.arange(off, off + D, dtype=torch.int64)
+        return _to_bf16(normal_bf16_bits(self.seed, self.name + "/new_" + which, idx))
+
+    def token_rows(self, which: str, t: int, layer: int, s: int, kv_head: int) -> torch.Tensor:
+        """The L_s(t) tokens of (layer, session, KV head) at step t in order, [L][D]
+        bf16: the cache's tokens before step 0, then with append the tokens of
+        steps 0..t."""
+        L = int(self.ctx_lens(t)[s])
+        P = self.page_size
+        if not self.append:
+            pages = self.block_tables[layer, s, :-(-L // P)]
+            return self.slabs(which, layer, pages, kv_head).reshape(-1, self.head_dim)[:L]
+        L0 = int(self.l0[s]) - 1
+        rows = []
+        if L0 > 0:
+            pages = self.block_tables[layer, s, :-(-L0 // P)]
+            rows.append(self.slabs(which, layer, pages, kv_head).reshape(-1, self.head_dim)[:L0])
+        rows += [self.new_kv_unit(which, u, layer, s, kv_head)[None] for u in range(t + 1)]
+        return torch.cat(rows)
+
+    def appended_block_tables(self, steps: int) -> np.ndarray:
+        """Append: block tables after `steps` steps (free pages taken in step,
+        then session, order)."""
+        bt = self.block_tables.copy()
+        k = 0
+        for t in range(steps):
+            for s in range(self.sessions):
+                j = int(self.l0[s]) - 1 + t
+                if j % self.page_size == 0:
+                    bt[:, s, j // self.page_size] = self.free_pages[k]
+                    k += 1
+        return bt
 
     def queries(self, device) -> torch.Tensor:
         """[steps][layers][sessions][Hq][D] bf16."""
@@ -352,11 +416,29 @@ class SessionLoop:
 
 def session_loop(seed: int = MEASURE_SEED, sessions: int = 56, layers: int = 32,
                  steps: int = 200, lo: int = 2048, hi: int = 16384, num_q_heads: int = 32,
-                 num_kv_heads: int = 8, head_dim: int = 128, name: str = "loop") -> SessionLoop:
+                 num_kv_heads: int = 8, head_dim: int = 128, name: str = "loop",
+                 append: bool = False) -> SessionLoop:
     """56 sessions x 32 layers, contexts U[2048, 16384] growing one token per
-    step for 200 steps, 32/8 heads, head_dim 128."""
+    step for 200 steps, 32/8 heads, head_dim 128.  append=True: see SessionLoop."""
     rng = np.random.default_rng([seed, 5, zlib.crc32(name.encode())])
     l0 = rng.integers(lo, hi + 1, size=sessions).astype(np.int32)
+    if append:
+        l0 = np.maximum(l0, 1)
+        init = [-(-int(L - 1) // 16) for L in l0]
+        final = [-(-int(L - 1 + steps) // 16) for L in l0]
+        n_init = int(sum(init))
+        n_grow = int(sum(f - i for f, i in zip(final, init)))
+        maxp = max(max(final), 1)
+        bts = np.full((layers, sessions, maxp), -1, dtype=np.int32)
+        for layer in range(layers):
+            perm = rng.permutation(n_init).astype(np.int32)
+            pos = 0
+            for s, n in enumerate(init):
+                bts[layer, s, :n] = perm[pos:pos + n]
+                pos += n
+        free = np.arange(n_init, n_init + n_grow, dtype=np.int32)
+        return SessionLoop(name, sessions, layers, steps, num_q_heads, num_kv_heads, head_dim,
+                           l0, bts, max(n_init + n_grow, 1), seed, append=True, free_pages=free)
     need = [-(-int(L + steps) // 16) for L in l0]
     npg = int(sum(need))
     maxp = max(need)

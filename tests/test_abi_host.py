@@ -136,7 +136,8 @@ def test_config_validation():
     bad = [dict(num_q_heads=30), dict(head_dim=96), dict(page_size=32), dict(kv_chunk_tokens=100),
            dict(kv_chunk_tokens=-16),
            dict(num_pages=0), dict(wg_per_cu=9), dict(policy=7), dict(num_q_heads=64),
-           dict(merge_mode=2), dict(schedule=2), dict(persistent=1, schedule=1)]
+           dict(merge_mode=2), dict(schedule=2), dict(persistent=1, schedule=1), dict(append=2),
+           dict(append=1)]
     base = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, num_pages=100, max_batch=4,
                 max_pages_per_seq=10, num_cus=256)
     for b in bad:

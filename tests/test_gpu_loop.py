@@ -35,6 +35,10 @@ class Loop:
         self.k = sl.pools("k", dev)
         self.v = sl.pools("v", dev)
         self.q = sl.queries(dev)
+        if sl.append:
+            self.new_k = sl.new_kv("k", dev)
+            self.new_v = sl.new_kv("v", dev)
+            cfgkw["append"] = 1
         self.bt = torch.as_tensor(sl.block_tables).to(dev)
         self.out = torch.full((sl.steps, sl.layers, sl.sessions, sl.num_q_heads, sl.head_dim),
                               float("nan"), dtype=torch.bfloat16, device=dev)
@@ -48,15 +52,21 @@ class Loop:
                                    num_layers=sl.layers, timeout_ms=timeout_ms, **cfgkw)
         self.stream = torch.cuda.Stream()
         self.dec = pkv.PagedDecoder(self.cfg, stream=self.stream)
+        if sl.append:
+            pkv.pkv_loop_set_free_pages(self.dec.handle, sl.free_pages)
         S, H, D = sl.sessions, sl.num_q_heads, sl.head_dim
         self.strides = (S * H * D, sl.pages_per_layer * sl.num_kv_heads * 16 * D,
                         S * sl.max_pages, S * H * D, S * H)
 
     def tensors(self, t):
         sl = self.sl
+        extra = {}
+        if sl.append:
+            extra = dict(new_k=self.new_k[t], new_v=self.new_v[t],
+                         layer_stride_new=sl.sessions * sl.num_kv_heads * sl.head_dim)
         return pkv.make_tensors(self.q[t], self.k, self.v, self.bt, self.lens, self.out[t],
                                 self.lse[t], batch=sl.sessions, block_table_stride=sl.max_pages,
-                                layer_strides=self.strides)
+                                layer_strides=self.strides, **extra)
 
     def step(self, t):
         info = self.dec.build_queue(self.sl.ctx_lens(t))
@@ -70,16 +80,22 @@ class Loop:
 
 
 def oracle_unit(sl, t, layer, s, hk):
+    """The oracle over the logical token sequence of (step, layer, session, KV
+    head): the cache's tokens, and with append the tokens steps 0..t wrote."""
     L = int(sl.ctx_lens(t)[s])
     G = sl.num_q_heads // sl.num_kv_heads
     if L == 0:
         return np.zeros((G, sl.head_dim)), np.full(G, -np.inf)
     npg = -(-L // 16)
-    pages = sl.block_tables[layer, s, :npg]
-    ks = workloads.bits_u16(sl.slabs("k", layer, pages, hk))[:, None]
-    vs = workloads.bits_u16(sl.slabs("v", layer, pages, hk))[:, None]
+
+    def paged(which):
+        rows = workloads.bits_u16(sl.token_rows(which, t, layer, s, hk))
+        full = np.zeros((npg * 16, sl.head_dim), dtype=rows.dtype)
+        full[:L] = rows
+        return full.reshape(npg, 1, 16, sl.head_dim)
+
     qg = workloads.bits_u16(sl.query_unit(t, layer, s))[None, hk * G:(hk + 1) * G]
-    return pa.range_state(qg, ks, vs, np.arange(npg)[None], 0, 0, 0, L, sl.scale, 16)
+    return pa.range_state(qg, paged("k"), paged("v"), np.arange(npg)[None], 0, 0, 0, L, sl.scale, 16)
 
 
 def check_all(lp, units=None):
@@ -178,5 +194,68 @@ def test_loop_rejects_one_shot_only_calls():
         with pytest.raises(pkv.PkvError) as e:
             pkv.pkv_decode(lp.dec.handle, t, lp.stream)
         assert e.value.status == pkv.PKV_ERR_INVALID_ARG
+    finally:
+        lp.close()
+
+
+@pytest.mark.parametrize("variant", ["nosplit", "split"])
+def test_loop_append_writes_tokens_and_grows_block_tables(variant):
+    # each step appends every session's newest token and takes a page from the
+    # free list when it opens one; outputs match the oracle over the logical
+    # token sequence, and the cache and block tables end up bit-exact
+    say("append", variant)
+    sl = workloads.session_loop(seed=21, sessions=5, layers=2, steps=40, lo=1, hi=40,
+                                num_q_heads=8, num_kv_heads=2, name="loop_append", append=True)
+    kw = dict(policy=pkv.PKV_POLICY_NO_SPLIT) if variant == "nosplit" else \
+        dict(policy=pkv.PKV_POLICY_SPLIT, kv_chunk_tokens=32)
+    lp = Loop(sl, **kw)
+    try:
+        for t in range(sl.steps):
+            lp.step(t)
+        assert pkv.pkv_loop_free_pages(lp.dec.handle) == 0      # every free page used once
+    finally:
+        lp.close()
+    check_all(lp)
+    want_bt = sl.appended_block_tables(sl.steps)
+    assert np.array_equal(lp.bt.cpu().numpy(), want_bt)
+    kb, vb = workloads.bits_u16(lp.k.cpu()), workloads.bits_u16(lp.v.cpu())
+    for layer in range(sl.layers):
+        for s in range(sl.sessions):
+            for hk in range(sl.num_kv_heads):
+                for t in range(sl.steps):
+                    j = int(sl.l0[s]) - 1 + t
+                    pg = want_bt[layer, s, j // 16]
+                    assert np.array_equal(kb[layer, pg, hk, j % 16],
+                                          workloads.bits_u16(sl.new_kv_unit("k", t, layer, s, hk)))
+                    assert np.array_equal(vb[layer, pg, hk, j % 16],
+                                          workloads.bits_u16(sl.new_kv_unit("v", t, layer, s, hk)))
+
+
+def test_loop_append_errors():
+    sl = workloads.session_loop(seed=22, sessions=3, layers=1, steps=3, lo=1, hi=20,
+                                num_q_heads=4, num_kv_heads=1, name="loop_append_err", append=True)
+    lp = Loop(sl)
+    try:
+        pkv.pkv_loop_set_free_pages(lp.dec.handle, [])            # nothing to take
+        opens = [t for t in range(sl.steps) if any((int(L) - 1 + t) % 16 == 0 for L in sl.l0)]
+        for t in range(sl.steps):
+            if t in opens:
+                with pytest.raises(pkv.PkvError) as e:
+                    lp.step(t)
+                assert e.value.status == pkv.PKV_ERR_CAPACITY
+                break
+            lp.step(t)
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.pkv_loop_set_free_pages(lp.dec.handle, [sl.pages_per_layer])   # outside the pool
+        assert e.value.status == pkv.PKV_ERR_INVALID_ARG
+    finally:
+        lp.close()
+    plain = workloads.session_loop(seed=23, sessions=2, layers=1, steps=1, lo=5, hi=40,
+                                   num_q_heads=4, num_kv_heads=1, name="loop_plain")
+    lp = Loop(plain)
+    try:
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.pkv_loop_set_free_pages(lp.dec.handle, [0])
+        assert e.value.status == pkv.PKV_ERR_STATE
     finally:
         lp.close()
