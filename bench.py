@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--loop-steps", type=int, default=200,
                     help="steps per run of the 56-session resident loop (0 skips the loop)")
     ap.add_argument("--loop-runs", type=int, default=3)
+    ap.add_argument("--density", action="store_true",
+                    help="cadenced loop with session churn: most sessions with no late step "
+                         "at periods of 10 and 20 ms (bisection, 3 runs each)")
     ap.add_argument("--no-loop-append", action="store_true",
                     help="skip the second loop measurement, with the KV append inside each step")
     ap.add_argument("--ablations", action="store_true",
@@ -268,6 +271,119 @@ def measure_loop(torch, pkv, workloads, steps, runs, gate, say, append=False):
            "pct_of_hbm_peak_median": round(float(np.median(gbs)) / HBM_PEAK_GBS * 100, 2),
            "launches_per_step": 0, "append": bool(append)}
     del k, v, q, out, lse, new_k, new_v
+    torch.cuda.empty_cache()
+    return res
+
+
+def density_search(torch, pkv, workloads, periods_ms, max_sessions, steps, runs, say):
+    """Cadenced session loop (WPK note: sessions served on a fixed beat, late
+    beats counted, density = most sessions with none late).  Steps are
+    published on a clock of period T; a step is late if it completes after its
+    next tick.  Sessions come and go: each slot hosts a sequence of sessions
+    (lifetimes U[40, 120] steps); when one leaves, the next joins the slot at a
+    step boundary with a fresh context (drawn so that it fits the slot's
+    pages).  For each T the largest session count with no late step over
+    `runs` runs is found by bisection."""
+    from oracle import paged_attention as pa
+    dev = "cuda"
+    sl = workloads.session_loop(sessions=max_sessions, steps=steps, name="loop_density")
+    t0 = time.perf_counter()
+    k, v, q = sl.pools("k", dev), sl.pools("v", dev), sl.queries(dev)
+    bt = torch.as_tensor(sl.block_tables).to(dev)
+    out = torch.empty((sl.steps, sl.layers, sl.sessions, sl.num_q_heads, sl.head_dim),
+                      dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((sl.steps, sl.layers, sl.sessions, sl.num_q_heads), dtype=torch.float32,
+                      device=dev)
+    lens_dev = torch.zeros(sl.sessions, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    say(f"density inputs: {max_sessions} session slots, {2 * k.numel() * 2 / 1e9:.1f} GB of K/V, "
+        f"{time.perf_counter() - t0:.1f} s")
+    # per-slot session schedule: lengths at every step with joins and leaves
+    rng = np.random.default_rng([workloads.MEASURE_SEED, 9])
+    lens = np.zeros((steps, max_sessions), dtype=np.int32)
+    joins = 0
+    for s in range(max_sessions):
+        cap = int(sl.l0[s])                      # the slot's pages hold cap + steps tokens
+        t, L0 = 0, cap
+        while t < steps:
+            life = int(rng.integers(40, 121))
+            for u in range(t, min(steps, t + life)):
+                lens[u, s] = L0 + (u - t)
+            t += life
+            if t < steps:
+                L0 = int(rng.integers(min(2048, cap), cap + 1))
+                joins += 1
+    S_all, H, D = sl.sessions, sl.num_q_heads, sl.head_dim
+    strides = (S_all * H * D, sl.pages_per_layer * sl.num_kv_heads * 16 * D, S_all * sl.max_pages,
+               S_all * H * D, S_all * H)
+    cfg = pkv.make_config(H, sl.num_kv_heads, D, sl.pages_per_layer, S_all, sl.max_pages,
+                          scale=sl.scale, persistent=1, num_layers=sl.layers, timeout_ms=20000)
+
+    def run(S, period_s):
+        stream = torch.cuda.Stream()
+        dec = pkv.PagedDecoder(cfg, stream=stream)
+        late, lat = 0, []
+        try:
+            start = time.perf_counter()
+            for t in range(steps):
+                tick = start + t * period_s
+                while time.perf_counter() < tick:
+                    pass
+                dec.build_queue(lens[t, :S])
+                tens = pkv.make_tensors(q[t], k, v, bt, lens_dev, out[t], lse[t], batch=S,
+                                        block_table_stride=sl.max_pages, layer_strides=strides)
+                a = time.perf_counter()
+                pkv.pkv_decode(dec.handle, tens, stream)
+                done = time.perf_counter()
+                lat.append(done - a)
+                late += done > tick + period_s
+        finally:
+            dec.close()
+        torch.cuda.synchronize()
+        return late, np.array(lat) * 1e3
+
+    # parity of a churned step: a slot after a join reads its new, shorter context
+    _, _ = run(min(8, max_sessions), 0.0)
+    o = out.float().cpu().numpy()
+    l = lse.cpu().numpy()
+    G = H // sl.num_kv_heads
+    t_chk = steps - 1
+    for s in range(min(8, max_sessions)):
+        L = int(lens[t_chk, s])
+        npg = -(-L // 16)
+        pg = sl.block_tables[0, s, :npg]
+        ks = workloads.bits_u16(sl.slabs("k", 0, pg, 0))[:, None]
+        vs = workloads.bits_u16(sl.slabs("v", 0, pg, 0))[:, None]
+        qg = workloads.bits_u16(sl.query_unit(t_chk, 0, s))[None, :G]
+        ro, rl = pa.range_state(qg, ks, vs, np.arange(npg)[None], 0, 0, 0, L, sl.scale, 16)
+        err = np.abs(o[t_chk, 0, s, :G] - ro).max()
+        if not err <= 2e-2:
+            raise SystemExit(f"density loop parity failed for slot {s}: {err:.3e}")
+    say(f"density loop parity passed ({joins} joins in the schedule)")
+    res = {"max_sessions_tried": max_sessions, "steps_per_run": steps, "runs": runs,
+           "session_lifetime_steps": [40, 120], "joins_per_run": joins, "periods": {}}
+    for T in periods_ms:
+        lo, hi, best = 1, max_sessions, 0
+        best_p99 = None
+        while lo <= hi:
+            S = (lo + hi) // 2
+            lates, p99s = [], []
+            for _ in range(runs):
+                late, lat = run(S, T / 1e3)
+                lates.append(late)
+                p99s.append(float(np.percentile(lat, 99)))
+                if late:
+                    break
+            ok = sum(lates) == 0
+            say(f"density T={T} ms: {S} sessions -> {sum(lates)} late steps, p99 {max(p99s):.2f} ms")
+            if ok:
+                best, best_p99 = S, max(p99s)
+                lo = S + 1
+            else:
+                hi = S - 1
+        res["periods"][str(T)] = {"sessions": best, "p99_ms_at_density": best_p99}
+        say(f"density at T={T} ms: {best} sessions with no late step over {runs} runs")
+    del k, v, q, out, lse
     torch.cuda.empty_cache()
     return res
 
@@ -510,6 +626,7 @@ def main():
             loop_append = measure_loop(torch, pkv, workloads, args.loop_steps, args.loop_runs,
                                        not args.no_gate, say, append=True)
     abl = ablations(torch, pkv, workloads, args, say) if args.ablations else None
+    density = density_search(torch, pkv, workloads, (10, 20), 160, 100, 3, say) if args.density else None
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(workloads, wl, args.cpu_seconds, say)
@@ -546,6 +663,7 @@ def main():
         "session_loop_p99_ms": loop["p99_ms"] if loop else None,
         "session_loop": loop,
         "session_loop_append": loop_append,
+        "session_density": density,
         "other_workloads": others,
         "ablations": abl,
         "host_wall_ms_per_step": round(main_res["host_wall_ms_per_step"], 4),
