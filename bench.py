@@ -57,6 +57,10 @@ def parse():
     ap.add_argument("--ablations", action="store_true",
                     help="also time the scheduling ablations: static vs atomic item assignment, "
                          "and exact-length bucketed launches vs the compact queue")
+    ap.add_argument("--kv", default="bf16", choices=["bf16", "f32"],
+                    help="KV-cache element type of the main workload (and of --profile-pass)")
+    ap.add_argument("--no-f32", action="store_true",
+                    help="skip the fp32 KV-cache measurements of the long, mixed and short workloads")
     ap.add_argument("--profile-pass", action="store_true",
                     help="for hardware-counter runs: a few untimed decode steps of the workload, "
                          "then a 1 GiB copy probe of known size (the counter reference)")
@@ -64,8 +68,8 @@ def parse():
 
 
 def measure(torch, pkv, workloads, name, steps, warmup, order, wg_per_cu, copies, gate, say,
-            merge="fused", schedule=0):
-    wl = workloads.CONFIGS[name]()
+            merge="fused", schedule=0, kv="bf16"):
+    wl = workloads.CONFIGS[name]().with_kv_dtype(kv)
     dev = "cuda"
     q = wl.q(dev)
     pools = []
@@ -79,6 +83,7 @@ def measure(torch, pkv, workloads, name, steps, warmup, order, wg_per_cu, copies
                           wl.max_pages_per_seq, scale=wl.scale,
                           order=pkv.PKV_ORDER_LPT if order == "lpt" else pkv.PKV_ORDER_CANONICAL,
                           wg_per_cu=wg_per_cu, schedule=schedule,
+                          kv_dtype=pkv.PKV_KV_F32 if kv == "f32" else pkv.PKV_KV_BF16,
                           merge_mode=pkv.PKV_MERGE_SEPARATE if merge == "separate" else pkv.PKV_MERGE_FUSED)
     stream = torch.cuda.current_stream()
     dec = pkv.PagedDecoder(cfg, stream=stream)
@@ -98,16 +103,16 @@ def measure(torch, pkv, workloads, name, steps, warmup, order, wg_per_cu, copies
             L = int(wl.ctx_lens[b])
             npg = -(-L // 16)
             pg = wl.block_table[b, :npg]
-            ks = workloads.bits_u16(wl.pool_slabs("k", pg, hk))[:, None]
-            vs = workloads.bits_u16(wl.pool_slabs("v", pg, hk))[:, None]
+            ks = workloads.kv_host(wl.pool_slabs("k", pg, hk))[:, None]
+            vs = workloads.kv_host(wl.pool_slabs("v", pg, hk))[:, None]
             ro, rl = pa.range_state(qb[b:b + 1, hk * G:(hk + 1) * G], ks, vs,
                                     np.arange(npg)[None], 0, 0, 0, L, wl.scale, 16)
             err = np.abs(o[b, hk * G:(hk + 1) * G] - ro)
             lerr = np.abs(l[b, hk * G:(hk + 1) * G] - rl)
             if not (err.max() <= 2e-2 and err.mean() <= 2e-3 and lerr.max() <= 2e-2):
-                raise SystemExit(f"parity gate failed on {name} unit {(b, hk)}: "
+                raise SystemExit(f"parity gate failed on {name} ({kv}) unit {(b, hk)}: "
                                  f"max {err.max():.3e} mean {err.mean():.3e} lse {lerr.max():.3e}")
-        say(f"parity gate passed ({name})")
+        say(f"parity gate passed ({name}, {kv} cache)")
 
     for i in range(warmup):
         pkv.pkv_decode(dec.handle, tens[i % copies], stream)
@@ -140,7 +145,7 @@ def measure(torch, pkv, workloads, name, steps, warmup, order, wg_per_cu, copies
     kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
     ms_step = total_ms / steps
     res = {
-        "workload": name, "kv_bytes": info.kv_bytes, "items": info.n_items,
+        "workload": name, "kv_dtype": kv, "kv_bytes": info.kv_bytes, "items": info.n_items,
         "chunk_tokens": info.chunk_tokens,
         "split": bool(info.split), "launches_per_step": info.launches_per_step,
         "partial_bytes": info.partial_bytes, "ms_per_step": ms_step,
@@ -533,14 +538,14 @@ def cpu_baseline(workloads, wl, seconds, say):
         npg = -(-L // 16)
         if (b, hk) not in cache:
             pg = wl.block_table[b, :npg]
-            cache[(b, hk)] = (workloads.bits_u16(wl.pool_slabs("k", pg, hk))[:, None],
-                              workloads.bits_u16(wl.pool_slabs("v", pg, hk))[:, None])
+            cache[(b, hk)] = (workloads.kv_host(wl.pool_slabs("k", pg, hk))[:, None],
+                              workloads.kv_host(wl.pool_slabs("v", pg, hk))[:, None])
         ks, vs = cache[(b, hk)]
         t0 = time.perf_counter()
         pa.range_state(qb[b:b + 1, hk * G:(hk + 1) * G], ks, vs, np.arange(npg)[None], 0, 0, 0, L,
                        wl.scale, 16)
         spent += time.perf_counter() - t0
-        done_bytes += L * wl.head_dim * 2 * 2
+        done_bytes += L * wl.head_dim * wl.kv_elem_bytes * 2
         n += 1
     passes = n / len(units)
     say(f"cpu baseline: {n} units ({passes:.2f} passes), {spent:.1f} s")
@@ -556,7 +561,7 @@ def profile_pass(torch, pkv, workloads, args, say):
     workload (alternating two pool copies), then one copy probe moving
     exactly 1 GiB (read 1 GiB, write 1 GiB), whose counter readings give the
     scale from counter units to bytes."""
-    wl = workloads.CONFIGS[args.workload]()
+    wl = workloads.CONFIGS[args.workload]().with_kv_dtype(args.kv)
     dev = "cuda"
     q = wl.q(dev)
     pools = [(wl.pool("k", dev, False), wl.pool("v", dev, False)) for _ in range(2)]
@@ -565,6 +570,7 @@ def profile_pass(torch, pkv, workloads, args, say):
     lse = torch.empty(wl.batch, wl.num_q_heads, dtype=torch.float32, device=dev)
     cfg = pkv.make_config(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages, wl.batch,
                           wl.max_pages_per_seq, scale=wl.scale,
+                          kv_dtype=pkv.PKV_KV_F32 if args.kv == "f32" else pkv.PKV_KV_BF16,
                           merge_mode=pkv.PKV_MERGE_SEPARATE if args.merge == "separate" else pkv.PKV_MERGE_FUSED)
     dec = pkv.PagedDecoder(cfg)
     info = dec.build_queue(wl.ctx_lens)
@@ -582,7 +588,7 @@ def profile_pass(torch, pkv, workloads, args, say):
     dst = torch.empty(n, dtype=torch.uint8, device=dev)
     pkv.pkv_copy_probe(dst, src, n)
     torch.cuda.synchronize()
-    print(json.dumps({"profile_pass": args.workload, "decode_steps": steps,
+    print(json.dumps({"profile_pass": args.workload, "kv_dtype": args.kv, "decode_steps": steps,
                       "kv_bytes_per_step": info.kv_bytes, "copy_probe_bytes": n}), flush=True)
 
 
@@ -606,7 +612,8 @@ def main():
         profile_pass(torch, pkv, workloads, args, say)
         return
     main_res, wl = measure(torch, pkv, workloads, args.workload, args.steps, args.warmup,
-                           args.order, args.wg_per_cu, args.copies, not args.no_gate, say, args.merge)
+                           args.order, args.wg_per_cu, args.copies, not args.no_gate, say, args.merge,
+                           kv=args.kv)
     say(f"{args.workload}: {main_res['gbs']:.1f} GB/s per step, decode kernel "
         f"{main_res['decode_gbs']:.1f} GB/s ({main_res['decode_ms_mean'] * 1e3:.1f} us)")
     others = {}
@@ -618,6 +625,20 @@ def main():
                                           "launches_per_step")}
         others[name]["pct_of_hbm_peak"] = 100.0 * r["gbs"] / HBM_PEAK_GBS
         say(f"{name}: {r['gbs']:.1f} GB/s per step, decode {r['decode_gbs']:.1f} GB/s")
+    f32 = {}
+    if not args.no_f32:
+        for name in ("long", "mixed", "short"):
+            if name == args.workload and args.kv == "f32":
+                continue
+            r, _ = measure(torch, pkv, workloads, name, max(args.steps // 2, 10), args.warmup,
+                           args.order, args.wg_per_cu, args.copies, not args.no_gate, say, args.merge,
+                           kv="f32")
+            f32[name] = {k: r[k] for k in ("gbs", "decode_gbs", "ms_per_step", "decode_ms_mean",
+                                           "items", "chunk_tokens", "kv_bytes")}
+            f32[name]["pct_of_hbm_peak"] = 100.0 * r["gbs"] / HBM_PEAK_GBS
+            f32[name]["decode_frac"] = r["decode_gbs"] / HBM_PEAK_GBS
+            say(f"{name} (fp32 cache): {r['gbs']:.1f} GB/s per step, decode {r['decode_gbs']:.1f} GB/s "
+                f"({r['decode_ms_mean'] * 1e3:.1f} us)")
     loop = loop_append = None
     if args.loop_steps > 0:
         loop = measure_loop(torch, pkv, workloads, args.loop_steps, args.loop_runs,
@@ -642,22 +663,23 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded counter-based N(0,1) bf16; permuted page pool)",
+        "dtype": args.kv,
+        "data": f"synthetic (seeded counter-based N(0,1) {args.kv}; permuted page pool)",
         "pct_of_hbm_peak": round(100.0 * main_res["gbs"] / HBM_PEAK_GBS, 2),
         "config": {"workload": "single long context", "batch": 1, "context_tokens": 131072,
                    "q_heads": 32, "kv_heads": 8, "head_dim": 128, "page_size": 16,
                    "kv_chunk_tokens": main_res["chunk_tokens"], "items": main_res["items"],
                    "launches_per_step": main_res["launches_per_step"],
                    "kv_bytes_per_step": main_res["kv_bytes"], "grid": main_res["grid"],
-                   "order": args.order, "merge": args.merge} if args.workload == "long" else
-                  {"workload": args.workload, "items": main_res["items"],
+                   "order": args.order, "merge": args.merge, "kv_dtype": args.kv}
+                  if args.workload == "long" else
+                  {"workload": args.workload, "items": main_res["items"], "kv_dtype": args.kv,
                    "kv_bytes_per_step": main_res["kv_bytes"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__)))
-                     if args.workload == "long" else None,
-                     "kernel": "decode_kernel<128,4>",
+                     if args.workload == "long" and args.kv == "bf16" else None,
+                     "kernel": f"decode_kernel<128,4,{'KvF32' if args.kv == 'f32' else 'KvBf16'}>",
                      "decode_us_mean": round(main_res["decode_ms_mean"] * 1e3, 3)},
         "cpu_baseline": cpu,
         "session_loop_p99_ms": loop["p99_ms"] if loop else None,
@@ -665,6 +687,7 @@ def main():
         "session_loop_append": loop_append,
         "session_density": density,
         "other_workloads": others,
+        "kv_f32": f32 or None,
         "ablations": abl,
         "host_wall_ms_per_step": round(main_res["host_wall_ms_per_step"], 4),
     }

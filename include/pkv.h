@@ -23,8 +23,9 @@
  *
  * Data layout (all row-major, contiguous, 16-byte aligned device memory):
  *   q          bf16  [B][Hq][D]
- *   k_pool     bf16  [num_pages][Hkv][P][D]      (one (page, head) slab of
- *   v_pool     bf16  [num_pages][Hkv][P][D]       P*D values is contiguous)
+ *   k_pool     bf16 or fp32 (pkv_config.kv_dtype) [num_pages][Hkv][P][D]
+ *   v_pool     the same                    (one (page, head) slab of P*D
+ *                                           values is contiguous)
  *   block_table int32 [B][block_table_stride]    entries past ceil(L_b/P)
  *                                                are ignored (may be -1)
  *   ctx_lens   int32 [B]
@@ -93,6 +94,14 @@ enum { PKV_ORDER_CANONICAL = 0, PKV_ORDER_LPT = 1 };
  * loop always claims. */
 enum { PKV_SCHEDULE_ATOMIC = 0, PKV_SCHEDULE_STATIC = 1 };
 
+/* Element type of the KV cache.  BF16: 2-byte values.  F32: 4-byte values,
+ * as in the fp32 attention cache of the text-to-speech model on the WPK note
+ * ("Same precision" list); the same kernels read twice the bytes per token,
+ * q.K and P.V run in fp32 on the full-precision values (q stays bf16, widened
+ * exactly).  q, out and lse keep their types.  The resident loop takes BF16
+ * only. */
+enum { PKV_KV_BF16 = 0, PKV_KV_F32 = 1 };
+
 /* How split rows are merged.  FUSED: inside the decode kernel, the last
  * workgroup to finish a split (row, KV head) merges its partial states (one
  * launch per step).  SEPARATE: a second kernel merges every split row (the
@@ -131,13 +140,14 @@ typedef struct pkv_config {
                                    newest token (K/V from pkv_tensors.new_k / new_v) into the
                                    cache, taking a page from the free list when the token
                                    opens a page (see pkv_loop_set_free_pages) */
-    int32_t reserved[3];        /* must be zero */
+    int32_t kv_dtype;           /* PKV_KV_*: element type of k_pool / v_pool */
+    int32_t reserved[2];        /* must be zero */
 } pkv_config;
 
 typedef struct pkv_tensors {
     const void* q;              /* bf16 [B][Hq][D] */
-    const void* k_pool;         /* bf16 [num_pages][Hkv][P][D] */
-    const void* v_pool;         /* bf16 [num_pages][Hkv][P][D] */
+    const void* k_pool;         /* kv_dtype [num_pages][Hkv][P][D] */
+    const void* v_pool;         /* kv_dtype [num_pages][Hkv][P][D] */
     const int32_t* block_table; /* int32 [B][block_table_stride] */
     const int32_t* ctx_lens;    /* int32 [B] (device copy; used by the device
                                    queue builder) */
@@ -323,9 +333,10 @@ PKV_API pkv_status pkv_plan_queue(const pkv_config* cfg, const int32_t* ctx_lens
                                   void* items, int32_t items_cap, int32_t* n_chunks,
                                   int32_t* part_off, int32_t* merge_rows, pkv_queue_info* info);
 
-/* Test hook: write the bf16 K and V rows that the decode kernel's own gather
+/* Test hook: write the K and V rows that the decode kernel's own gather
  * reads for queue item item_index, in token order, to device buffers k_out and
- * v_out (bf16 [Hkv-local: 1][tok_end - tok_begin][D]).  Enqueued on stream. */
+ * v_out ([tok_end - tok_begin][D] of the cache's element type, kv_dtype).
+ * Enqueued on stream. */
 PKV_API pkv_status pkv_debug_gather(pkv_handle* h, const pkv_tensors* t, int32_t item_index,
                                     void* k_out, void* v_out, void* stream);
 

@@ -12,8 +12,8 @@ Summary, Methodology section 1 "Native Block-Table Decode Engine"):
   reading taken).
 * Layout: attention runs directly over the paged cache through the block
   table, with no repacking into contiguous K/V.  Pool layout (the page is
-  silent; reading taken): K and V pools are separate arrays of bf16 bit
-  patterns shaped [num_pages][Hkv][page_size][D]; ``block_table[b][j]`` is the
+  silent; reading taken): K and V pools are separate arrays shaped
+  [num_pages][Hkv][page_size][D]; ``block_table[b][j]`` is the
   physical page holding logical tokens j*page_size .. j*page_size+page_size-1
   of sequence b.
 * Row-local bounds: only the true length L_b of each row is read; tokens at or
@@ -23,9 +23,11 @@ Summary, Methodology section 1 "Native Block-Table Decode Engine"):
   merge combines such states exactly.  An empty range yields the neutral state
   (o = 0, lse = -inf), which the merge gives weight zero.
 
-Inputs are numpy arrays of bf16 bit patterns (uint16); every value is widened
-exactly to float64 and all arithmetic below is float64.  Output LSE is the
-natural logarithm.
+Inputs are numpy arrays of bf16 bit patterns (uint16).  The K/V pools may
+instead hold float32 values: the fp32 attention cache that the Wave
+Persistent Kernel note lists for its text-to-speech model ("Same precision"
+list); the query stays bf16 bits.  Every value is widened exactly to float64
+and all arithmetic below is float64.  Output LSE is the natural logarithm.
 
 Because the split-and-merge scheme reaches the plain result exactly (up to
 rounding order), the oracle is that plain definition written out: one softmax
@@ -49,16 +51,28 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
+def kv_to_f64(values: np.ndarray) -> np.ndarray:
+    """Widen cache values exactly to float64: uint16 arrays are bf16 bit
+    patterns, float32 arrays are fp32 values (float64 holds both exactly)."""
+    values = np.asarray(values)
+    if values.dtype == np.uint16:
+        return bf16_bits_to_f64(values)
+    if values.dtype == np.float32:
+        return values.astype(np.float64)
+    raise TypeError(f"cache values must be uint16 (bf16 bits) or float32, not {values.dtype}")
+
+
 def gather_tokens(pool: np.ndarray, block_table: np.ndarray, seq: int, kv_head: int,
                   tok_begin: int, tok_end: int, page_size: int) -> np.ndarray:
-    """Raw bf16 bits of tokens [tok_begin, tok_end) of one (sequence, KV head).
+    """Raw cache values of tokens [tok_begin, tok_end) of one (sequence, KV
+    head).
 
     Token t lives in physical page ``block_table[seq][t // page_size]`` at row
     ``t % page_size`` (PersistentKV page, Methodology 1, "Layout").  Returns
-    a uint16 array [tok_end - tok_begin][D] in token order.
+    an array [tok_end - tok_begin][D] of the pool's dtype in token order.
     """
     if tok_end <= tok_begin:
-        return np.zeros((0, pool.shape[-1]), dtype=np.uint16)
+        return np.zeros((0, pool.shape[-1]), dtype=pool.dtype)
     t = np.arange(tok_begin, tok_end, dtype=np.int64)
     phys = np.asarray(block_table[seq], dtype=np.int64)[t // page_size]
     if phys.min() < 0 or phys.max() >= pool.shape[0]:
@@ -85,10 +99,10 @@ def range_state(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
     d = q.shape[2]
     if tok_end <= tok_begin:
         return np.zeros((g, d)), np.full(g, -np.inf)
-    kk = bf16_bits_to_f64(gather_tokens(k_pool, block_table, seq, kv_head,
-                                        tok_begin, tok_end, page_size))
-    vv = bf16_bits_to_f64(gather_tokens(v_pool, block_table, seq, kv_head,
-                                        tok_begin, tok_end, page_size))
+    kk = kv_to_f64(gather_tokens(k_pool, block_table, seq, kv_head,
+                                 tok_begin, tok_end, page_size))
+    vv = kv_to_f64(gather_tokens(v_pool, block_table, seq, kv_head,
+                                 tok_begin, tok_end, page_size))
     qg = bf16_bits_to_f64(q[seq, kv_head * g:(kv_head + 1) * g, :])   # [G][D]
     s = float(scale) * (qg @ kk.T)                                      # [G][n]
     m = s.max(axis=1, keepdims=True)
@@ -130,7 +144,8 @@ def decode_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
                      page_size: int, units=None):
     """softmax(q K^T * scale) V and its LSE for every (sequence, query head).
 
-    q [B][Hq][D], pools [num_pages][Hkv][page_size][D], all bf16 bits;
+    q [B][Hq][D] bf16 bits, pools [num_pages][Hkv][page_size][D] bf16 bits
+    or float32 values;
     block_table int [B][max_pages]; ctx_lens int [B].  A row with L_b = 0 gets
     O = 0 and LSE = -inf (the neutral state).  ``units`` optionally restricts
     the work to a list of (seq, kv_head) pairs; rows outside it stay neutral.

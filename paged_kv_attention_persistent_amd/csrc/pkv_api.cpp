@@ -491,7 +491,7 @@ PKV_API pkv_status pkv_decode(pkv_handle* h, const pkv_tensors* t, void* stream)
         return hip_fail(h, e, "stream wait");
     const DecodeParams p = make_params(h, t);
     if (h->ev_before && (e = hipEventRecord(h->ev_before, st)) != hipSuccess) return hip_fail(h, e, "event record");
-    int rc = launch_decode(p, h->r.d, h->r.g, h->grid, st);
+    int rc = launch_decode(p, h->r.d, h->r.g, h->r.kv_dtype, h->grid, st);
     if (rc != 0) return hip_fail(h, (hipError_t)rc, "decode launch");
     if (h->ev_after && (e = hipEventRecord(h->ev_after, st)) != hipSuccess) return hip_fail(h, e, "event record");
     const int merge_rows = h->built_on_device ? h->batch : h->qinfo.n_merge_rows;
@@ -626,8 +626,7 @@ PKV_API pkv_status pkv_debug_gather(pkv_handle* h, const pkv_tensors* t, int32_t
     if (st != h->stream && (e = hipStreamWaitEvent(st, h->upload_evt, 0)) != hipSuccess)
         return hip_fail(h, e, "stream wait");
     const DecodeParams p = make_params(h, t);
-    int rc = launch_debug_gather(p, h->r.d, item_index, static_cast<uint16_t*>(k_out),
-                                 static_cast<uint16_t*>(v_out), st);
+    int rc = launch_debug_gather(p, h->r.d, h->r.kv_dtype, item_index, k_out, v_out, st);
     if (rc != 0) return hip_fail(h, (hipError_t)rc, "gather launch");
     return PKV_OK;
 }

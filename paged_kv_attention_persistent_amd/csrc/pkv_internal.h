@@ -119,7 +119,7 @@ struct Resolved {
     int hq, hkv, g, d, page, num_pages, max_batch, max_pages_per_seq;
     float scale;
     int policy, order, chunk, num_cus, max_items, wg_per_cu, merge_mode;
-    int persistent, num_layers, timeout_ms, schedule, append;
+    int persistent, num_layers, timeout_ms, schedule, append, kv_dtype;
 };
 
 pkv_status resolve_config(const pkv_config* cfg, int device_cus, Resolved* r, const char** why);
@@ -214,11 +214,11 @@ struct BuildParams {
 // Launch wrappers (pkv_kernels.hip).  Return a hipError_t as int.
 int launch_init_ctrl(Ctrl* ctrl, uint32_t* arrive, int n_arrive, void* stream);
 int launch_zero(void* p, size_t bytes, void* stream);
-int launch_decode(const DecodeParams& p, int head_dim, int group, int grid, void* stream);
+int launch_decode(const DecodeParams& p, int head_dim, int group, int kv_dtype, int grid, void* stream);
 int launch_merge(const DecodeParams& p, int head_dim, int group, int n_rows, void* stream);
 int launch_build_queue(const BuildParams& p, void* stream);
-int launch_debug_gather(const DecodeParams& p, int head_dim, int item_index, uint16_t* k_out,
-                        uint16_t* v_out, void* stream);
+int launch_debug_gather(const DecodeParams& p, int head_dim, int kv_dtype, int item_index, void* k_out,
+                        void* v_out, void* stream);
 bool supported_shape(int head_dim, int group);
 int launch_copy_probe(void* dst, const void* src, size_t bytes, int grid, void* stream);
 int launch_read_probe(const void* src, size_t bytes, void* sink, int grid, void* stream);

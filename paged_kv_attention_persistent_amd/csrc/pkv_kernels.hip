@@ -113,27 +113,46 @@ __device__ __forceinline__ void report(const Ctrl* c0, uint32_t* host_error, uin
     if (host_error) __hip_atomic_store(host_error, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// Per-lane share of one page of K and V: two token rows (8*j + r, j = 0, 1)
-// times D/64 pieces of 8 dims (piece 8*k + p of the row).
-template <int D>
-struct Tile {
-    static constexpr int NPC = D / 64;
-    u32x4 k[2][NPC];
-    u32x4 v[2][NPC];
+// Element type of the K/V cache.  A tile is the part of one page that a wave
+// loads and consumes at a time: the whole page for bf16 (two token rows per
+// lane, 8*j + r for j = 0, 1), half a page for fp32 (one token row per lane,
+// row 8*h + r of half h); either way 8 KB per wave at D = 128, so both
+// element types keep the same registers per tile and the same pipeline.
+struct KvBf16 {
+    static constexpr int kBytes = 2;
+    static constexpr int kRows = 2;            // token rows per lane in a tile
+    static constexpr int kTilesPerPage = 1;
+};
+struct KvF32 {
+    static constexpr int kBytes = 4;
+    static constexpr int kRows = 1;
+    static constexpr int kTilesPerPage = 2;
 };
 
-// Byte offsets of the lane's two token rows inside a (page, head) slab.  Rows
-// at or beyond `valid` are never read: their lanes re-read row 0 of the same
-// page (always a valid token) and the consumer masks them.
+// Per-lane share of one tile of K and V: kRows token rows times D/64 pieces
+// of 8 dims (piece 8*k + p of the row), each piece QW 16-byte words.
+template <int D, typename KV>
+struct Tile {
+    static constexpr int NPC = D / 64;
+    static constexpr int QW = KV::kBytes / 2;
+    u32x4 k[KV::kRows][NPC * QW];
+    u32x4 v[KV::kRows][NPC * QW];
+};
+
+// Byte offsets of the lane's token rows inside a tile (the tile's first row
+// is the slab address the loads get).  Rows at or beyond `valid` (counted
+// from the tile's first row) are never read: their lanes re-read row 0 of the
+// tile (always a valid token) and the consumer masks them.
 struct LaneOff {
     uint32_t o0, o1;
 };
 
-template <int D>
+template <int D, typename KV>
 __device__ __forceinline__ LaneOff lane_offsets(int r, int p, int valid) {
+    constexpr int RB = D * KV::kBytes;                        // bytes per token row
     const int t0 = r < valid ? r : 0;
     const int t1 = 8 + r < valid ? 8 + r : 0;
-    return {(uint32_t)(t0 * D * 2 + p * 16), (uint32_t)(t1 * D * 2 + p * 16)};
+    return {(uint32_t)(t0 * RB + p * 8 * KV::kBytes), (uint32_t)(t1 * RB + p * 8 * KV::kBytes)};
 }
 
 // Streaming 16-byte load with the non-temporal hint: K/V pages are read
@@ -144,17 +163,22 @@ __device__ __forceinline__ u32x4 ld_stream(const char* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-// The gather of one page: ks / vs are the wave-uniform slab addresses, the
-// lane adds its 32-bit row offset; piece k sits 128 bytes further on.
-template <int D>
-__device__ __forceinline__ void load_tile(Tile<D>& t, const char* ks, const char* vs, LaneOff o) {
+// The gather of one tile: ks / vs are the wave-uniform addresses of the
+// tile's first row, the lane adds its 32-bit row offset; piece k sits
+// 64 * element-size bytes further on, and its QW words are consecutive.
+template <int D, typename KV>
+__device__ __forceinline__ void load_tile(Tile<D, KV>& t, const char* ks, const char* vs, LaneOff o) {
+    constexpr int QW = Tile<D, KV>::QW;
 #pragma unroll
-    for (int k = 0; k < Tile<D>::NPC; ++k) {
-        t.k[0][k] = ld_stream(ks + o.o0 + 128 * k);
-        t.k[1][k] = ld_stream(ks + o.o1 + 128 * k);
-        t.v[0][k] = ld_stream(vs + o.o0 + 128 * k);
-        t.v[1][k] = ld_stream(vs + o.o1 + 128 * k);
-    }
+    for (int k = 0; k < Tile<D, KV>::NPC; ++k)
+#pragma unroll
+        for (int q = 0; q < QW; ++q) {
+            const uint32_t off = 64 * KV::kBytes * k + 16 * q;
+            t.k[0][k * QW + q] = ld_stream(ks + o.o0 + off);
+            if constexpr (KV::kRows == 2) t.k[1][k * QW + q] = ld_stream(ks + o.o1 + off);
+            t.v[0][k * QW + q] = ld_stream(vs + o.o0 + off);
+            if constexpr (KV::kRows == 2) t.v[1][k * QW + q] = ld_stream(vs + o.o1 + off);
+        }
 }
 
 template <int D, int G>
@@ -164,47 +188,72 @@ struct State {
     float acc[G][D / 8];
 };
 
-template <int D, int G, bool MASKED>
-__device__ __forceinline__ void consume_tile(const Tile<D>& t, const u32x4 (&qv)[G][D / 64],
+// q.K, online-softmax update and P.V for one tile.  q stays packed bf16 in
+// registers; for a bf16 cache two K rows meet it in v_dot2 (fp32 accumulate),
+// for an fp32 cache each q pair is widened to fp32 on the fly (exact) and
+// multiplied with full-precision K.  The accumulator is fp32 either way.
+template <int D, int G, typename KV, bool MASKED>
+__device__ __forceinline__ void consume_tile(const Tile<D, KV>& t, const u32x4 (&qv)[G][D / 64],
                                              State<D, G>& st, float c, int r, int valid) {
     constexpr int NPC = D / 64;
-    float s[2][G];
+    constexpr int R = KV::kRows;
+    constexpr int NW = NPC * Tile<D, KV>::QW;    // 16-byte words per row and lane
+    float s[R][G];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < R; ++j) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             float a = 0.0f;
 #pragma unroll
             for (int k = 0; k < NPC; ++k) {
-                a = dot2(t.k[j][k].x, qv[g][k].x, a);
-                a = dot2(t.k[j][k].y, qv[g][k].y, a);
-                a = dot2(t.k[j][k].z, qv[g][k].z, a);
-                a = dot2(t.k[j][k].w, qv[g][k].w, a);
+                if constexpr (KV::kBytes == 2) {
+                    a = dot2(t.k[j][k].x, qv[g][k].x, a);
+                    a = dot2(t.k[j][k].y, qv[g][k].y, a);
+                    a = dot2(t.k[j][k].z, qv[g][k].z, a);
+                    a = dot2(t.k[j][k].w, qv[g][k].w, a);
+                } else {
+                    const u32x4 k0 = t.k[j][2 * k], k1 = t.k[j][2 * k + 1];
+                    u32x4 q = qv[g][k];
+                    // widen q here, tile by tile: hoisted out of the loop the
+                    // widened copy would need D * G / 8 more VGPRs per lane
+                    __asm__ volatile("" : "+v"(q));
+                    a = fmaf(__uint_as_float(k0.x), bf16_lo(q.x), a);
+                    a = fmaf(__uint_as_float(k0.y), bf16_hi(q.x), a);
+                    a = fmaf(__uint_as_float(k0.z), bf16_lo(q.y), a);
+                    a = fmaf(__uint_as_float(k0.w), bf16_hi(q.y), a);
+                    a = fmaf(__uint_as_float(k1.x), bf16_lo(q.z), a);
+                    a = fmaf(__uint_as_float(k1.y), bf16_hi(q.z), a);
+                    a = fmaf(__uint_as_float(k1.z), bf16_lo(q.w), a);
+                    a = fmaf(__uint_as_float(k1.w), bf16_hi(q.w), a);
+                }
             }
             s[j][g] = sum8(a) * c;
         }
     }
-    u32x4 v[2][NPC];
+    u32x4 v[R][NW];
 #pragma unroll
-    for (int k = 0; k < NPC; ++k) { v[0][k] = t.v[0][k]; v[1][k] = t.v[1][k]; }
+    for (int j = 0; j < R; ++j)
+#pragma unroll
+        for (int k = 0; k < NW; ++k) v[j][k] = t.v[j][k];
     if (MASKED) {                                 // the last, partial page of a row
-        const bool ok0 = r < valid, ok1 = 8 + r < valid;
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            if (!ok0) s[0][g] = -INFINITY;
-            if (!ok1) s[1][g] = -INFINITY;
-        }
+        for (int j = 0; j < R; ++j) {
+            const bool ok = 8 * j + r < valid;
 #pragma unroll
-        for (int k = 0; k < NPC; ++k) {
-            if (!ok0) v[0][k] = u32x4{0u, 0u, 0u, 0u};
-            if (!ok1) v[1][k] = u32x4{0u, 0u, 0u, 0u};
+            for (int g = 0; g < G; ++g)
+                if (!ok) s[j][g] = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < NW; ++k)
+                if (!ok) v[j][k] = u32x4{0u, 0u, 0u, 0u};
         }
     }
     float mx[G];
     bool need = false;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        mx[g] = fmaxf(s[0][g], s[1][g]);
+        mx[g] = s[0][g];
+#pragma unroll
+        for (int j = 1; j < R; ++j) mx[g] = fmaxf(mx[g], s[j][g]);
         need |= mx[g] > st.m[g] + kTau;
     }
     if (need) {
@@ -220,19 +269,31 @@ __device__ __forceinline__ void consume_tile(const Tile<D>& t, const u32x4 (&qv)
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        const float p0 = __builtin_amdgcn_exp2f(s[0][g] - st.m[g]);
-        const float p1 = __builtin_amdgcn_exp2f(s[1][g] - st.m[g]);
-        st.l[g] += p0 + p1;
+        if constexpr (KV::kBytes == 2) {
+            const float p0 = __builtin_amdgcn_exp2f(s[0][g] - st.m[g]);
+            const float p1 = __builtin_amdgcn_exp2f(s[1][g] - st.m[g]);
+            st.l[g] += p0 + p1;
 #pragma unroll
-        for (int k = 0; k < NPC; ++k) {
-            const uint32_t a0[4] = {v[0][k].x, v[0][k].y, v[0][k].z, v[0][k].w};
-            const uint32_t a1[4] = {v[1][k].x, v[1][k].y, v[1][k].z, v[1][k].w};
+            for (int k = 0; k < NPC; ++k) {
+                const uint32_t a0[4] = {v[0][k].x, v[0][k].y, v[0][k].z, v[0][k].w};
+                const uint32_t a1[4] = {v[1][k].x, v[1][k].y, v[1][k].z, v[1][k].w};
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                float& lo = st.acc[g][k * 8 + 2 * w];
-                float& hi = st.acc[g][k * 8 + 2 * w + 1];
-                lo = fmaf(p1, bf16_lo(a1[w]), fmaf(p0, bf16_lo(a0[w]), lo));
-                hi = fmaf(p1, bf16_hi(a1[w]), fmaf(p0, bf16_hi(a0[w]), hi));
+                for (int w = 0; w < 4; ++w) {
+                    float& lo = st.acc[g][k * 8 + 2 * w];
+                    float& hi = st.acc[g][k * 8 + 2 * w + 1];
+                    lo = fmaf(p1, bf16_lo(a1[w]), fmaf(p0, bf16_lo(a0[w]), lo));
+                    hi = fmaf(p1, bf16_hi(a1[w]), fmaf(p0, bf16_hi(a0[w]), hi));
+                }
+            }
+        } else {
+            const float p0 = __builtin_amdgcn_exp2f(s[0][g] - st.m[g]);
+            st.l[g] += p0;
+#pragma unroll
+            for (int k = 0; k < NW; ++k) {
+                const float x[4] = {__uint_as_float(v[0][k].x), __uint_as_float(v[0][k].y),
+                                    __uint_as_float(v[0][k].z), __uint_as_float(v[0][k].w)};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st.acc[g][4 * k + e] = fmaf(p0, x[e], st.acc[g][4 * k + e]);
             }
         }
     }
@@ -253,15 +314,19 @@ struct WaveItem {
 };
 
 // One window of up to 64 of this wave's pages: i = wb .. wb + n - 1 of the
-// wave's page list (item page w + 8 i).  Loads run ahead of the page being
-// consumed; past the end the prefetch re-reads the last full page (a cache
+// wave's page list (item page w + 8 i), walked tile by tile (a tile is a
+// page, or half of one for an fp32 cache).  Loads run ahead of the tile being
+// consumed; past the end the prefetch re-reads the last full tile (a cache
 // hit) so that every iteration issues the same loads and the wait counts the
 // compiler derives stay exact.  btv holds the window's validated page ids.
-template <int D, int G>
+template <int D, int G, typename KV>
 __device__ __forceinline__ void run_window(const DecodeParams& P, const u32x4 (&qv)[G][D / 64],
                                            State<D, G>& st, int32_t btv, int n, int wb,
                                            const WaveItem& wi, int r, int p) {
-    constexpr uint64_t kSlabBytes = (uint64_t)kPageSize * D * 2;
+    constexpr int TPP = KV::kTilesPerPage;
+    constexpr int kTileRows = kPageSize / TPP;
+    constexpr uint64_t kSlabBytes = (uint64_t)kPageSize * D * KV::kBytes;
+    constexpr uint64_t kTileBytes = kSlabBytes / TPP;
     const char* kbase = reinterpret_cast<const char*>(P.k_pool);
     const char* vbase = reinterpret_cast<const char*>(P.v_pool);
     const uint64_t head_off = (uint64_t)wi.hk * kSlabBytes;
@@ -276,51 +341,53 @@ __device__ __forceinline__ void run_window(const DecodeParams& P, const u32x4 (&
     };
     const float c = P.scale_log2;
     // Only the item's last page can be partial; keep it out of the pipelined
-    // loop so that the loop issues full-page loads with loop-invariant lane
-    // offsets (no per-page VGPR temporaries competing with in-flight tiles).
+    // loop so that the loop issues full-tile loads with loop-invariant lane
+    // offsets (no per-tile VGPR temporaries competing with in-flight tiles).
     int vlast;
     const uint64_t slast = page_of(n - 1, vlast);
     const int nf = vlast < kPageSize ? n - 1 : n;               // full pages in the window
-    const LaneOff full = lane_offsets<D>(r, p, kPageSize);
-    auto issue = [&](Tile<D>& T, int ii) {
+    const int nt = nf * TPP;                                    // their tiles
+    const LaneOff full = lane_offsets<D, KV>(r, p, kTileRows);
+    auto issue = [&](Tile<D, KV>& T, int ii) {
         int unused;
-        const uint64_t so = page_of(ii < nf ? ii : nf - 1, unused);
+        const int ti = ii < nt ? ii : nt - 1;
+        const uint64_t so = page_of(ti / TPP, unused) + (uint64_t)(ti % TPP) * kTileBytes;
         LaneOff o = full;
         // Keep the lane offset a 32-bit VGPR inside the loop so the loads use
         // the scalar-base + 32-bit-offset form (no 64-bit per-lane address math).
         __asm__ volatile("" : "+v"(o.o0), "+v"(o.o1));
-        load_tile<D>(T, kbase + so, vbase + so, o);
+        load_tile<D, KV>(T, kbase + so, vbase + so, o);
     };
     // The loop is rotated so that every iteration first consumes a tile and
     // then refills the registers it just freed: no instruction at the loop
     // head writes a register that a load may still be filling.
-    if (nf > 0) {
-        if constexpr (PipelineDepth<D, G>::value == 2) {     // three tiles, two pages ahead
-            Tile<D> A, B, C;
+    if (nt > 0) {
+        if constexpr (PipelineDepth<D, G>::value == 2) {     // three tiles, two ahead
+            Tile<D, KV> A, B, C;
             issue(A, 0);
             issue(B, 1);
             issue(C, 2);
             for (int ii = 0;; ii += 3) {
-                consume_tile<D, G, false>(A, qv, st, c, r, kPageSize);
-                if (ii + 1 >= nf) break;
+                consume_tile<D, G, KV, false>(A, qv, st, c, r, kTileRows);
+                if (ii + 1 >= nt) break;
                 issue(A, ii + 3);
-                consume_tile<D, G, false>(B, qv, st, c, r, kPageSize);
-                if (ii + 2 >= nf) break;
+                consume_tile<D, G, KV, false>(B, qv, st, c, r, kTileRows);
+                if (ii + 2 >= nt) break;
                 issue(B, ii + 4);
-                consume_tile<D, G, false>(C, qv, st, c, r, kPageSize);
-                if (ii + 3 >= nf) break;
+                consume_tile<D, G, KV, false>(C, qv, st, c, r, kTileRows);
+                if (ii + 3 >= nt) break;
                 issue(C, ii + 5);
             }
-        } else {                                              // two tiles, one page ahead
-            Tile<D> A, B;
+        } else {                                              // two tiles, one ahead
+            Tile<D, KV> A, B;
             issue(A, 0);
             issue(B, 1);
             for (int ii = 0;; ii += 2) {
-                consume_tile<D, G, false>(A, qv, st, c, r, kPageSize);
-                if (ii + 1 >= nf) break;
+                consume_tile<D, G, KV, false>(A, qv, st, c, r, kTileRows);
+                if (ii + 1 >= nt) break;
                 issue(A, ii + 2);
-                consume_tile<D, G, false>(B, qv, st, c, r, kPageSize);
-                if (ii + 2 >= nf) break;
+                consume_tile<D, G, KV, false>(B, qv, st, c, r, kTileRows);
+                if (ii + 2 >= nt) break;
                 issue(B, ii + 3);
             }
         }
@@ -331,9 +398,15 @@ __device__ __forceinline__ void run_window(const DecodeParams& P, const u32x4 (&
     // other counters left at their maxima (GFX9 encoding).
     __builtin_amdgcn_s_waitcnt(0x0F70);
     if (nf < n) {                                             // the partial last page
-        Tile<D> T;
-        load_tile<D>(T, kbase + slast, vbase + slast, lane_offsets<D>(r, p, vlast));
-        consume_tile<D, G, true>(T, qv, st, c, r, vlast);
+#pragma unroll
+        for (int h = 0; h < TPP; ++h) {
+            const int vh = vlast - h * kTileRows;               // valid rows of this tile
+            if (vh <= 0) break;
+            Tile<D, KV> T;
+            const uint64_t so = slast + (uint64_t)h * kTileBytes;
+            load_tile<D, KV>(T, kbase + so, vbase + so, lane_offsets<D, KV>(r, p, vh));
+            consume_tile<D, G, KV, true>(T, qv, st, c, r, vh);
+        }
     }
 }
 
@@ -480,7 +553,7 @@ __device__ __forceinline__ ItemRef read_item(const DecodeParams& P, uint32_t idx
     return it;
 }
 
-template <int D, int G>
+template <int D, int G, typename KV>
 __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, const ItemRef& it, uint32_t& nxt) {
     constexpr int NPC = D / 64;
     const int tid = threadIdx.x;
@@ -544,7 +617,7 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, const ItemRe
             if (lane == __ffsll(badm) - 1) report(P.ctrl, P.host_error, PKV_DEVERR_PAGE_OOB, (uint32_t)btv);
             btv = badl ? 0 : btv;
         }
-        run_window<D, G>(P, qv, st, btv, n, wb, wi, r, p);
+        run_window<D, G, KV>(P, qv, st, btv, n, wb, wi, r, p);
     }
     // Claim the next item only now, near the end of this one: a claim made
     // earlier would hold an item this workgroup cannot start while another
@@ -645,7 +718,7 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, const ItemRe
     }
 }
 
-template <int D, int G>
+template <int D, int G, typename KV>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     __shared__ Smem<D, G> sm;
     const int tid = threadIdx.x;
@@ -679,7 +752,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
         uint32_t nxt = 0;
         uint64_t t_start = 0;
         if (P.trace) t_start = wall_clock64();
-        process_item<D, G>(P, sm, read_item(P, idx), nxt);
+        process_item<D, G, KV>(P, sm, read_item(P, idx), nxt);
         ++done_here;
         if (P.trace && tid == 0 && idx < (uint32_t)P.trace_cap) {
             const uint64_t t_end = wall_clock64();
@@ -997,7 +1070,7 @@ __global__ __launch_bounds__(kThreads) void resident_kernel(LoopParams L) {
                 }
                 if (L.append && it.ok && it.chunk == it.nch - 1)
                     append_token<D>(Q, grants, it, new_k + layer * ls_new, new_v + layer * ls_new, tid);
-                process_item<D, G>(Q, sm, it, nxt);
+                process_item<D, G, KvBf16>(Q, sm, it, nxt);
             } else {
                 // rows with no tokens take the neutral state, in every layer;
                 // thread 0 finds them (64 merge rows at a time), all threads write
@@ -1237,11 +1310,14 @@ __global__ __launch_bounds__(kBuildThreads) void build_queue_kernel(BuildParams 
     }
 }
 
-// Test hook: one wave runs the decode kernel's own gather over every page of
-// one item, in order, and stores the rows it read.
-template <int D>
+// Test hook: one wave runs the decode kernel's own gather over every tile of
+// one item, in order, and stores the rows it read (k_out / v_out hold the
+// item's tokens as [token][D] rows of the cache's element type).
+template <int D, typename KV>
 __global__ __launch_bounds__(64) void debug_gather_kernel(DecodeParams P, int item_index,
-                                                          uint16_t* k_out, uint16_t* v_out) {
+                                                          char* k_out, char* v_out) {
+    constexpr int TPP = KV::kTilesPerPage, kTileRows = kPageSize / TPP, QW = Tile<D, KV>::QW;
+    constexpr size_t kRowBytes = (size_t)D * KV::kBytes;
     const int lane = threadIdx.x;
     const int r = lane >> 3, p = lane & 7;
     if (item_index < 0 || item_index >= P.qhdr->n_items) return;
@@ -1257,19 +1333,27 @@ __global__ __launch_bounds__(64) void debug_gather_kernel(DecodeParams P, int it
         }
         const int rem = (int)(it.tok_end - it.tok_begin) - j * kPageSize;
         const int valid = rem < kPageSize ? rem : kPageSize;
-        Tile<D> t;
-        const uint64_t slab = ((uint64_t)(uint32_t)pg * P.hkv + it.kv_head) * kPageSize * D * 2;
-        load_tile<D>(t, reinterpret_cast<const char*>(P.k_pool) + slab,
-                     reinterpret_cast<const char*>(P.v_pool) + slab, lane_offsets<D>(r, p, valid));
+        for (int h = 0; h < TPP; ++h) {
+            const int vh = valid - h * kTileRows;
+            if (vh <= 0) break;
+            Tile<D, KV> t;
+            const uint64_t slab = ((uint64_t)(uint32_t)pg * P.hkv + it.kv_head) * kPageSize * kRowBytes +
+                                  (uint64_t)h * kTileRows * kRowBytes;
+            load_tile<D, KV>(t, reinterpret_cast<const char*>(P.k_pool) + slab,
+                             reinterpret_cast<const char*>(P.v_pool) + slab, lane_offsets<D, KV>(r, p, vh));
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int tok = 8 * jj + r;
-            if (tok >= valid) continue;
-            const size_t row = (size_t)(j * kPageSize + tok) * D;
+            for (int jj = 0; jj < KV::kRows; ++jj) {
+                const int tok = 8 * jj + r;
+                if (tok >= vh) continue;
+                const size_t row = (size_t)(j * kPageSize + h * kTileRows + tok) * kRowBytes;
 #pragma unroll
-            for (int k = 0; k < Tile<D>::NPC; ++k) {
-                *reinterpret_cast<u32x4*>(k_out + row + (8 * k + p) * 8) = t.k[jj][k];
-                *reinterpret_cast<u32x4*>(v_out + row + (8 * k + p) * 8) = t.v[jj][k];
+                for (int k = 0; k < Tile<D, KV>::NPC; ++k)
+#pragma unroll
+                    for (int q = 0; q < QW; ++q) {
+                        const size_t off = row + (size_t)(8 * k + p) * 8 * KV::kBytes + 16 * q;
+                        *reinterpret_cast<u32x4*>(k_out + off) = t.k[jj][k * QW + q];
+                        *reinterpret_cast<u32x4*>(v_out + off) = t.v[jj][k * QW + q];
+                    }
             }
         }
     }
@@ -1317,8 +1401,11 @@ __global__ void init_ctrl_kernel(Ctrl* c, uint32_t* arrive, int n_arrive) {
 }
 
 template <int D, int G>
-int launch_decode_t(const DecodeParams& p, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((decode_kernel<D, G>), dim3(grid), dim3(kThreads), 0, s, p);
+int launch_decode_t(const DecodeParams& p, int kv_dtype, int grid, hipStream_t s) {
+    if (kv_dtype == PKV_KV_F32)
+        hipLaunchKernelGGL((decode_kernel<D, G, KvF32>), dim3(grid), dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((decode_kernel<D, G, KvBf16>), dim3(grid), dim3(kThreads), 0, s, p);
     return (int)hipGetLastError();
 }
 
@@ -1389,8 +1476,8 @@ int launch_resident(const LoopParams& lp, int head_dim, int group, int grid, voi
     PKV_DISPATCH(launch_resident_t, head_dim, group, lp, grid, (hipStream_t)stream);
 }
 
-int launch_decode(const DecodeParams& p, int head_dim, int group, int grid, void* stream) {
-    PKV_DISPATCH(launch_decode_t, head_dim, group, p, grid, (hipStream_t)stream);
+int launch_decode(const DecodeParams& p, int head_dim, int group, int kv_dtype, int grid, void* stream) {
+    PKV_DISPATCH(launch_decode_t, head_dim, group, p, kv_dtype, grid, (hipStream_t)stream);
 }
 
 int launch_merge(const DecodeParams& p, int head_dim, int group, int n_rows, void* stream) {
@@ -1403,14 +1490,23 @@ int launch_build_queue(const BuildParams& p, void* stream) {
     return (int)hipGetLastError();
 }
 
-int launch_debug_gather(const DecodeParams& p, int head_dim, int item_index, uint16_t* k_out,
-                        uint16_t* v_out, void* stream) {
+template <int D>
+void launch_debug_gather_t(const DecodeParams& p, int kv_dtype, int item_index, char* k_out, char* v_out,
+                           hipStream_t s) {
+    if (kv_dtype == PKV_KV_F32)
+        hipLaunchKernelGGL((debug_gather_kernel<D, KvF32>), dim3(1), dim3(64), 0, s, p, item_index, k_out, v_out);
+    else
+        hipLaunchKernelGGL((debug_gather_kernel<D, KvBf16>), dim3(1), dim3(64), 0, s, p, item_index, k_out, v_out);
+}
+
+int launch_debug_gather(const DecodeParams& p, int head_dim, int kv_dtype, int item_index, void* k_out,
+                        void* v_out, void* stream) {
+    char* ko = static_cast<char*>(k_out);
+    char* vo = static_cast<char*>(v_out);
     if (head_dim == 128)
-        hipLaunchKernelGGL((debug_gather_kernel<128>), dim3(1), dim3(64), 0, (hipStream_t)stream, p,
-                           item_index, k_out, v_out);
+        launch_debug_gather_t<128>(p, kv_dtype, item_index, ko, vo, (hipStream_t)stream);
     else if (head_dim == 64)
-        hipLaunchKernelGGL((debug_gather_kernel<64>), dim3(1), dim3(64), 0, (hipStream_t)stream, p,
-                           item_index, k_out, v_out);
+        launch_debug_gather_t<64>(p, kv_dtype, item_index, ko, vo, (hipStream_t)stream);
     else
         return (int)hipErrorInvalidValue;
     return (int)hipGetLastError();

@@ -24,7 +24,7 @@ pkv_status resolve_config(const pkv_config* cfg, int device_cus, Resolved* r, co
     *why = "";
     if (!cfg || !r) { *why = "null config"; return PKV_ERR_INVALID_ARG; }
     if (cfg->struct_size != sizeof(pkv_config)) { *why = "pkv_config.struct_size mismatch"; return PKV_ERR_INVALID_ARG; }
-    for (int i = 0; i < 3; ++i)
+    for (int i = 0; i < 2; ++i)
         if (cfg->reserved[i]) { *why = "reserved config fields must be zero"; return PKV_ERR_INVALID_ARG; }
     if (cfg->num_q_heads <= 0 || cfg->num_kv_heads <= 0 || cfg->num_q_heads % cfg->num_kv_heads) {
         *why = "num_q_heads must be a positive multiple of num_kv_heads"; return PKV_ERR_INVALID_ARG;
@@ -93,6 +93,9 @@ pkv_status resolve_config(const pkv_config* cfg, int device_cus, Resolved* r, co
     if (cfg->append != 0 && cfg->append != 1) { *why = "append must be 0 or 1"; return PKV_ERR_INVALID_ARG; }
     if (cfg->append && !r->persistent) { *why = "append needs the resident loop"; return PKV_ERR_INVALID_ARG; }
     r->append = cfg->append;
+    if (cfg->kv_dtype != PKV_KV_BF16 && cfg->kv_dtype != PKV_KV_F32) { *why = "unknown kv_dtype"; return PKV_ERR_INVALID_ARG; }
+    if (cfg->kv_dtype != PKV_KV_BF16 && r->persistent) { *why = "the resident loop reads a bf16 cache"; return PKV_ERR_UNSUPPORTED; }
+    r->kv_dtype = cfg->kv_dtype;
     if ((int64_t)r->max_items * r->num_layers > ((int64_t)1 << 31) / (4 * r->g * r->d)) {
         *why = "partial-state storage too large"; return PKV_ERR_CAPACITY;
     }
@@ -238,7 +241,7 @@ pkv_status plan_queue(const Resolved& r, const int32_t* ctx_lens, int32_t batch,
         info->n_merge_rows = n_merge;
         info->n_partial_slots = part_off[batch] * r.hkv;
         info->launches_per_step = 1 + ((r.merge_mode == PKV_MERGE_SEPARATE && n_merge > 0) ? 1 : 0);
-        info->kv_bytes = (uint64_t)sum_len * r.hkv * r.d * 2ull * 2ull;
+        info->kv_bytes = (uint64_t)sum_len * r.hkv * r.d * (r.kv_dtype == PKV_KV_F32 ? 4ull : 2ull) * 2ull;
         info->partial_bytes = (uint64_t)info->n_partial_slots * r.g * (r.d + 1) * 4ull * 2ull;
     }
     return PKV_OK;

@@ -29,6 +29,7 @@ PKV_POLICY_AUTO, PKV_POLICY_NO_SPLIT, PKV_POLICY_SPLIT = 0, 1, 2
 PKV_ORDER_CANONICAL, PKV_ORDER_LPT = 0, 1
 PKV_SCHEDULE_ATOMIC, PKV_SCHEDULE_STATIC = 0, 1
 PKV_MERGE_FUSED, PKV_MERGE_SEPARATE = 0, 1
+PKV_KV_BF16, PKV_KV_F32 = 0, 1
 PKV_DEVERR_NONE, PKV_DEVERR_PAGE_OOB, PKV_DEVERR_BAD_ITEM = 0, 1, 2
 
 ITEM_DTYPE = np.dtype([("seq", "<u4"), ("kv_head", "<u2"), ("chunk", "<u2"),
@@ -45,7 +46,7 @@ class pkv_config(C.Structure):
                 ("max_items", C.c_int32), ("wg_per_cu", C.c_int32),
                 ("merge_mode", C.c_int32), ("persistent", C.c_int32), ("num_layers", C.c_int32),
                 ("timeout_ms", C.c_int32), ("schedule", C.c_int32), ("append", C.c_int32),
-                ("reserved", C.c_int32 * 3)]
+                ("kv_dtype", C.c_int32), ("reserved", C.c_int32 * 2)]
 
 
 class pkv_tensors(C.Structure):
@@ -157,7 +158,7 @@ def make_config(num_q_heads, num_kv_heads, head_dim, num_pages, max_batch, max_p
                 page_size=16, scale=0.0, policy=PKV_POLICY_AUTO, order=PKV_ORDER_CANONICAL,
                 kv_chunk_tokens=0, num_cus=0, max_items=0, wg_per_cu=0,
                 merge_mode=PKV_MERGE_FUSED, persistent=0, num_layers=0,
-                timeout_ms=0, schedule=0, append=0) -> pkv_config:
+                timeout_ms=0, schedule=0, append=0, kv_dtype=PKV_KV_BF16) -> pkv_config:
     cfg = pkv_config()
     cfg.struct_size = C.sizeof(pkv_config)
     cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim = num_q_heads, num_kv_heads, head_dim
@@ -170,6 +171,7 @@ def make_config(num_q_heads, num_kv_heads, head_dim, num_pages, max_batch, max_p
     cfg.persistent, cfg.num_layers, cfg.timeout_ms = persistent, num_layers, timeout_ms
     cfg.schedule = schedule
     cfg.append = append
+    cfg.kv_dtype = kv_dtype
     return cfg
 
 

@@ -19,9 +19,13 @@ so each element is an N(0, 1) draw quantised to 65536 levels (tails cut at
 about 4.3 sigma).  (k1, k2) come from the seed and the tensor's name.  The
 arithmetic is integer-only, so CPU and GPU produce identical bits.
 
+An fp32 KV cache (``kv_dtype="f32"``) draws from the same counters through
+``NORMAL_TABLE_F32[j]``, the float32 of the same quantile: full 24-bit
+mantissas, and the bf16 cache of the same workload is exactly its rounding.
+
 Parity runs poison what must never be read: pool pages no block table points
 to, and the slots of a sequence's last page at or beyond its length, hold the
-bf16 quiet-NaN pattern 0x7FC0.  Block-table entries past a sequence's last
+quiet-NaN pattern (0x7FC0 in bf16, 0x7FC00000 in fp32).  Block-table entries past a sequence's last
 page are -1.
 
 Workload shapes are those of the decode-attention traces on the PersistentKV
@@ -37,7 +41,7 @@ from __future__ import annotations
 
 import math
 import zlib
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 
 import numpy as np
 import torch
@@ -45,6 +49,8 @@ import torch
 MEASURE_SEED = 20260623
 CALIBRATION_SEED = 20260622
 BF16_NAN = 0x7FC0
+F32_NAN = 0x7FC00000
+KV_DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32}
 _M32 = 0xFFFFFFFF
 
 
@@ -71,16 +77,28 @@ def _mix32(x: torch.Tensor) -> torch.Tensor:
 _TABLE_CACHE: dict = {}
 
 
+def _quantiles_f32() -> np.ndarray:
+    from scipy.special import ndtri
+    p = (np.arange(65536, dtype=np.float64) + 0.5) / 65536.0
+    return ndtri(p).astype(np.float32)
+
+
 def normal_table(device) -> torch.Tensor:
     """int64 tensor [65536] of bf16 bit patterns of N(0,1) quantiles."""
     key = str(device)
     if key not in _TABLE_CACHE:
-        from scipy.special import ndtri
-        p = (np.arange(65536, dtype=np.float64) + 0.5) / 65536.0
-        f32 = ndtri(p).astype(np.float32)
-        u = f32.view(np.uint32).astype(np.uint64)
+        u = _quantiles_f32().view(np.uint32).astype(np.uint64)
         rne = (u + 0x7FFF + ((u >> 16) & 1)) >> 16          # float32 -> bf16 RNE
         _TABLE_CACHE[key] = torch.from_numpy(rne.astype(np.int64)).to(device)
+    return _TABLE_CACHE[key]
+
+
+def normal_table_f32(device) -> torch.Tensor:
+    """int64 tensor [65536] of float32 bit patterns of the same quantiles."""
+    key = "f32/" + str(device)
+    if key not in _TABLE_CACHE:
+        u = _quantiles_f32().view(np.uint32).astype(np.int64)
+        _TABLE_CACHE[key] = torch.from_numpy(u).to(device)
     return _TABLE_CACHE[key]
 
 
@@ -92,12 +110,22 @@ def stream_keys(seed: int, name: str):
     return k1, k2
 
 
-def normal_bf16_bits(seed: int, name: str, index: torch.Tensor) -> torch.Tensor:
-    """bf16 bit patterns (int64 tensor, values 0..65535) for element ``index``."""
+def _table_index(seed: int, name: str, index: torch.Tensor) -> torch.Tensor:
     k1, k2 = stream_keys(seed, name)
     a = _mix32((index & _M32) ^ k1)
     b = _mix32(a ^ (index >> 32) ^ k2)
-    return normal_table(index.device)[b >> 16]
+    return b >> 16
+
+
+def normal_bf16_bits(seed: int, name: str, index: torch.Tensor) -> torch.Tensor:
+    """bf16 bit patterns (int64 tensor, values 0..65535) for element ``index``."""
+    return normal_table(index.device)[_table_index(seed, name, index)]
+
+
+def normal_f32_bits(seed: int, name: str, index: torch.Tensor) -> torch.Tensor:
+    """float32 bit patterns (int64 tensor, values 0..2^32-1) for element
+    ``index``: the values whose bf16 rounding ``normal_bf16_bits`` gives."""
+    return normal_table_f32(index.device)[_table_index(seed, name, index)]
 
 
 def _to_bf16(bits: torch.Tensor) -> torch.Tensor:
@@ -105,22 +133,49 @@ def _to_bf16(bits: torch.Tensor) -> torch.Tensor:
     return (bits - ((bits >> 15) & 1) * 65536).to(torch.int16).view(torch.bfloat16)
 
 
-def fill_normal_bf16(out: torch.Tensor, seed: int, name: str, offset: int = 0,
-                     chunk: int = 1 << 24) -> torch.Tensor:
-    """Fill a contiguous bf16 tensor with the stream ``name`` starting at
-    element ``offset`` (chunked to bound the int64 temporaries)."""
+def _to_f32(bits: torch.Tensor) -> torch.Tensor:
+    """int64 tensor of 32-bit patterns -> torch.float32 with those bits."""
+    return (bits - ((bits >> 31) & 1) * (1 << 32)).to(torch.int32).view(torch.float32)
+
+
+def normal_values(seed: int, name: str, index: torch.Tensor, dtype=torch.bfloat16) -> torch.Tensor:
+    """Elements ``index`` of stream ``name`` as bf16 or float32 values."""
+    if dtype == torch.float32:
+        return _to_f32(normal_f32_bits(seed, name, index))
+    return _to_bf16(normal_bf16_bits(seed, name, index))
+
+
+def fill_normal(out: torch.Tensor, seed: int, name: str, offset: int = 0,
+                chunk: int = 1 << 24) -> torch.Tensor:
+    """Fill a contiguous bf16 or float32 tensor with the stream ``name``
+    starting at element ``offset`` (chunked to bound the int64 temporaries)."""
     flat = out.view(-1)
     n = flat.numel()
     for s in range(0, n, chunk):
         e = min(n, s + chunk)
         idx = torch.arange(offset + s, offset + e, dtype=torch.int64, device=out.device)
-        flat[s:e] = _to_bf16(normal_bf16_bits(seed, name, idx))
+        flat[s:e] = normal_values(seed, name, idx, out.dtype)
     return out
+
+
+def fill_normal_bf16(out: torch.Tensor, seed: int, name: str, offset: int = 0,
+                     chunk: int = 1 << 24) -> torch.Tensor:
+    """Fill a contiguous bf16 tensor with the stream ``name``."""
+    assert out.dtype == torch.bfloat16
+    return fill_normal(out, seed, name, offset, chunk)
 
 
 def bits_u16(t: torch.Tensor) -> np.ndarray:
     """Host numpy uint16 view of a bf16 tensor's bits (copies to CPU)."""
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def kv_host(t: torch.Tensor) -> np.ndarray:
+    """Host numpy copy of a KV tensor in the form the oracle reads: uint16 bf16
+    bit patterns for a bf16 cache, float32 values for an fp32 cache."""
+    if t.dtype == torch.float32:
+        return t.detach().cpu().contiguous().numpy()
+    return bits_u16(t)
 
 
 @dataclass
@@ -137,10 +192,25 @@ class Workload:
     seed: int
     scale: float = 0.0
     extra: dict = field(default_factory=dict)
+    kv_dtype: str = "bf16"            # element type of the K/V pools: "bf16" or "f32"
 
     def __post_init__(self):
         if self.scale == 0.0:
             self.scale = 1.0 / math.sqrt(self.head_dim)
+        if self.kv_dtype not in KV_DTYPES:
+            raise ValueError(f"kv_dtype must be one of {sorted(KV_DTYPES)}")
+
+    @property
+    def kv_torch_dtype(self):
+        return KV_DTYPES[self.kv_dtype]
+
+    @property
+    def kv_elem_bytes(self) -> int:
+        return 4 if self.kv_dtype == "f32" else 2
+
+    def with_kv_dtype(self, kv_dtype: str) -> "Workload":
+        """The same workload (same streams, same tables) with another cache type."""
+        return replace(self, kv_dtype=kv_dtype)
 
     @property
     def batch(self) -> int:
@@ -154,7 +224,7 @@ class Workload:
     def kv_bytes(self) -> int:
         """Bytes of K and V of valid tokens: the algorithmic read volume."""
         return int(self.ctx_lens.astype(np.int64).sum()) * self.num_kv_heads \
-            * self.head_dim * 2 * 2
+            * self.head_dim * self.kv_elem_bytes * 2
 
     def q(self, device="cpu") -> torch.Tensor:
         t = torch.empty(self.batch, self.num_q_heads, self.head_dim,
@@ -162,10 +232,10 @@ class Workload:
         return fill_normal_bf16(t, self.seed, self.name + "/q")
 
     def pool(self, which: str, device="cpu", poison: bool = True) -> torch.Tensor:
-        """K ('k') or V ('v') pool [num_pages][Hkv][P][D] bf16."""
+        """K ('k') or V ('v') pool [num_pages][Hkv][P][D] of kv_dtype."""
         t = torch.empty(self.num_pages, self.num_kv_heads, self.page_size,
-                        self.head_dim, dtype=torch.bfloat16, device=device)
-        fill_normal_bf16(t, self.seed, self.name + "/" + which)
+                        self.head_dim, dtype=self.kv_torch_dtype, device=device)
+        fill_normal(t, self.seed, self.name + "/" + which)
         if poison:
             self.poison(t)
         return t
@@ -176,9 +246,8 @@ class Workload:
         per_page = self.num_kv_heads * self.page_size * self.head_dim
         pages = torch.as_tensor(np.asarray(pages, dtype=np.int64))
         idx = pages[:, None] * per_page + torch.arange(per_page, dtype=torch.int64)[None, :]
-        bits = normal_bf16_bits(self.seed, self.name + "/" + which, idx.reshape(-1))
-        return _to_bf16(bits).view(len(pages), self.num_kv_heads, self.page_size,
-                                   self.head_dim)
+        vals = normal_values(self.seed, self.name + "/" + which, idx.reshape(-1), self.kv_torch_dtype)
+        return vals.view(len(pages), self.num_kv_heads, self.page_size, self.head_dim)
 
     def pool_slabs(self, which: str, pages, kv_head: int) -> torch.Tensor:
         """Regenerate on the CPU only the (page, kv_head) slabs of the given
@@ -188,14 +257,17 @@ class Workload:
         pages = torch.as_tensor(np.asarray(pages, dtype=np.int64))
         idx = (pages[:, None] * per_page + kv_head * slab
                + torch.arange(slab, dtype=torch.int64)[None, :])
-        bits = normal_bf16_bits(self.seed, self.name + "/" + which, idx.reshape(-1))
-        return _to_bf16(bits).view(len(pages), self.page_size, self.head_dim)
+        vals = normal_values(self.seed, self.name + "/" + which, idx.reshape(-1), self.kv_torch_dtype)
+        return vals.view(len(pages), self.page_size, self.head_dim)
 
     def poison(self, pool: torch.Tensor) -> None:
         """Write NaN into unreferenced pages and past-the-end slots."""
         used = np.zeros(self.num_pages, dtype=bool)
         P = self.page_size
-        nan = torch.tensor(BF16_NAN, dtype=torch.int16).view(torch.bfloat16)
+        if pool.dtype == torch.float32:
+            nan = torch.tensor(F32_NAN, dtype=torch.int32).view(torch.float32)
+        else:
+            nan = torch.tensor(BF16_NAN, dtype=torch.int16).view(torch.bfloat16)
         for b in range(self.batch):
             L = int(self.ctx_lens[b])
             npg = -(-L // P)
@@ -265,7 +337,7 @@ def many_short(seed: int = MEASURE_SEED, batch: int = 64, ctx: int = 4096) -> Wo
 
 def custom(name: str, lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
            seed: int = MEASURE_SEED, spare_pages: int = 0, page_size: int = 16,
-           max_pages: int | None = None) -> Workload:
+           max_pages: int | None = None, kv_dtype: str = "bf16") -> Workload:
     """Any shape: lengths given, pool = the pages needed plus ``spare_pages``
     (spare pages are poisoned)."""
     rng = np.random.default_rng([seed, zlib.crc32(name.encode())])
@@ -273,7 +345,7 @@ def custom(name: str, lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
     npg = int(sum(-(-int(L) // page_size) for L in lens)) + spare_pages
     npg = max(npg, 1)
     return Workload(name, num_q_heads, num_kv_heads, head_dim, page_size, lens,
-                    _tables(rng, lens, page_size, npg, max_pages), npg, seed)
+                    _tables(rng, lens, page_size, npg, max_pages), npg, seed, kv_dtype=kv_dtype)
 
 
 CONFIGS = {"tiny": tiny, "long": long_context, "mixed": mixed, "short": many_short}

@@ -137,7 +137,7 @@ def test_config_validation():
            dict(kv_chunk_tokens=-16),
            dict(num_pages=0), dict(wg_per_cu=9), dict(policy=7), dict(num_q_heads=64),
            dict(merge_mode=2), dict(schedule=2), dict(persistent=1, schedule=1), dict(append=2),
-           dict(append=1)]
+           dict(append=1), dict(kv_dtype=2), dict(kv_dtype=-1), dict(persistent=1, kv_dtype=1)]
     base = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, num_pages=100, max_batch=4,
                 max_pages_per_seq=10, num_cus=256)
     for b in bad:
@@ -149,6 +149,29 @@ def test_config_validation():
     c.struct_size = 4
     with pytest.raises(pkv.PkvError):
         pkv.pkv_workspace_size(c)
+    c = pkv.make_config(**base)
+    c.reserved[1] = 1
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_workspace_size(c)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_workspace_size(pkv.make_config(**dict(base, persistent=1, kv_dtype=1)))
+    assert e.value.status == pkv.PKV_ERR_UNSUPPORTED
+
+
+def test_f32_cache_plan_and_layout():
+    # the fp32 cache changes neither the queue nor the workspace, only the
+    # bytes a step reads
+    from paged_kv_attention_persistent_amd import workloads
+    wl = workloads.mixed()
+    kw = dict(num_cus=256)
+    a = pkv.make_config(32, 8, 128, wl.num_pages, wl.batch, wl.max_pages_per_seq, **kw)
+    b = pkv.make_config(32, 8, 128, wl.num_pages, wl.batch, wl.max_pages_per_seq,
+                        kv_dtype=pkv.PKV_KV_F32, **kw)
+    ia, *_, infa = pkv.pkv_plan_queue(a, wl.ctx_lens)
+    ib, *_, infb = pkv.pkv_plan_queue(b, wl.ctx_lens)
+    assert ia.tobytes() == ib.tobytes()
+    assert infb.kv_bytes == 2 * infa.kv_bytes == wl.with_kv_dtype("f32").kv_bytes
+    assert pkv.pkv_workspace_size(a) == pkv.pkv_workspace_size(b)
 
 
 def test_plan_rejects_bad_lengths_and_capacity():
@@ -180,3 +203,22 @@ def test_layout_regions_are_ordered_and_aligned():
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert lay.max_items == 8 * (8192 // 64)      # ranges of at least 64 pages
     assert lay.partial_lse_off - lay.partial_o_off >= lay.max_items * 4 * 128 * 4
+
+
+def test_f32_stream_rounds_to_bf16_stream():
+    # the fp32 cache's values round (RNE) to exactly the bf16 cache's values,
+    # and carry low mantissa bits that bf16 cannot hold
+    import torch
+    from paged_kv_attention_persistent_amd import workloads
+    wl = workloads.custom("f32_stream", [100, 37], 8, 2, 64, spare_pages=2)
+    kb = wl.pool("k", "cpu", poison=True)
+    kf = wl.with_kv_dtype("f32").pool("k", "cpu", poison=True)
+    assert kf.dtype == torch.float32 and kb.dtype == torch.bfloat16
+    fin = torch.isfinite(kf)
+    assert torch.equal(fin, torch.isfinite(kb))            # the same slots poisoned
+    assert torch.equal(kf[fin].to(torch.bfloat16).view(torch.int16), kb[fin].view(torch.int16))
+    assert torch.equal(kf[~fin].view(torch.int32), torch.full_like(kf[~fin].view(torch.int32), 0x7FC00000))
+    assert (kf[fin].view(torch.int32) & 0xFFFF).ne(0).float().mean() > 0.99
+    sl = wl.with_kv_dtype("f32").pool_slabs("v", wl.block_table[0, :3], 1)
+    full = wl.with_kv_dtype("f32").pool("v", "cpu", poison=False)
+    assert torch.equal(sl, full[torch.as_tensor(wl.block_table[0, :3].astype(np.int64)), 1])

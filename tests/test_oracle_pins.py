@@ -11,6 +11,12 @@
 * closed forms (hand-derived fixtures in tests/golden/closed_forms.json);
 * planted mistakes: each plausible bug, planted in the oracle by
   monkeypatching it, must make at least one of the pins above fail.
+
+The library, permutation, LSE-law and closed-form pins run for both cache
+element types: bf16 bit patterns and float32 values (the fp32 attention
+cache of the Wave Persistent Kernel note, "Same precision" list).  For
+float32 the test widens values itself with numpy, independently of the
+oracle's widening.
 """
 
 import json
@@ -32,8 +38,20 @@ def f32_to_bf16_bits(x):
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
 
 
-def random_case(rng, lens, hq, hkv, d, page_size, spare=3, permute=True):
-    """Random bf16 inputs; pool pages scattered; unused slots NaN."""
+def kv_values(rng, shape, kv):
+    """Random N(0,1) cache values: bf16 bits, or float32 with full mantissas."""
+    x = rng.standard_normal(shape)
+    return f32_to_bf16_bits(x) if kv == "bf16" else x.astype(np.float32)
+
+
+def kv_f64(x):
+    """Test-side widening of cache values (float32 by numpy's own cast)."""
+    return np.asarray(x).astype(np.float64) if np.asarray(x).dtype == np.float32 else pa.bf16_bits_to_f64(x)
+
+
+def random_case(rng, lens, hq, hkv, d, page_size, spare=3, permute=True, kv="bf16"):
+    """Random inputs (q bf16, cache of element type kv); pool pages
+    scattered; unused slots NaN."""
     lens = np.asarray(lens)
     need = [-(-int(L) // page_size) for L in lens]
     npg = sum(need) + spare
@@ -44,10 +62,10 @@ def random_case(rng, lens, hq, hkv, d, page_size, spare=3, permute=True):
     for b, n in enumerate(need):
         bt[b, :n] = perm[pos:pos + n]
         pos += n
-    k = f32_to_bf16_bits(rng.standard_normal((npg, hkv, page_size, d)))
-    v = f32_to_bf16_bits(rng.standard_normal((npg, hkv, page_size, d)))
+    k = kv_values(rng, (npg, hkv, page_size, d), kv)
+    v = kv_values(rng, (npg, hkv, page_size, d), kv)
     q = f32_to_bf16_bits(rng.standard_normal((len(lens), hq, d)))
-    nan = np.uint16(0x7FC0)
+    nan = np.uint16(0x7FC0) if kv == "bf16" else np.float32("nan")
     used = np.zeros(npg, dtype=bool)
     for b, L in enumerate(lens):
         used[bt[b, :need[b]]] = True
@@ -68,8 +86,8 @@ def sdpa_reference(q, k, v, bt, lens, scale, page_size):
         if L == 0:
             continue
         t = np.arange(L)
-        kk = pa.bf16_bits_to_f64(k[bt[b, t // page_size], :, t % page_size, :])   # [L][Hkv][D]
-        vv = pa.bf16_bits_to_f64(v[bt[b, t // page_size], :, t % page_size, :])
+        kk = kv_f64(k[bt[b, t // page_size], :, t % page_size, :])                # [L][Hkv][D]
+        vv = kv_f64(v[bt[b, t // page_size], :, t % page_size, :])
         qq = torch.from_numpy(pa.bf16_bits_to_f64(q[b]))[None, :, None, :]        # [1][Hq][1][D]
         kt = torch.from_numpy(kk).permute(1, 0, 2)[None]                          # [1][Hkv][L][D]
         vt = torch.from_numpy(vv).permute(1, 0, 2)[None]
@@ -81,11 +99,11 @@ def sdpa_reference(q, k, v, bt, lens, scale, page_size):
 
 # ---------------------------------------------------------------- pins ----
 
-def pin_sdpa(attend, seed=0):
+def pin_sdpa(attend, seed=0, kv="bf16"):
     rng = np.random.default_rng(seed)
     for (lens, hq, hkv, d, P) in [([37, 64], 4, 2, 16, 16), ([5, 1, 33], 8, 2, 32, 4),
                                   ([70], 4, 1, 64, 16), ([9], 2, 2, 8, 2)]:
-        q, k, v, bt, lens = random_case(rng, lens, hq, hkv, d, P)
+        q, k, v, bt, lens = random_case(rng, lens, hq, hkv, d, P, kv=kv)
         scale = 1.0 / math.sqrt(d)
         o, _ = attend(q, k, v, bt, lens, scale, P)
         ref = sdpa_reference(q, k, v, bt, lens, scale, P)
@@ -94,9 +112,9 @@ def pin_sdpa(attend, seed=0):
     return True
 
 
-def pin_permutation(attend, seed=1):
+def pin_permutation(attend, seed=1, kv="bf16"):
     rng = np.random.default_rng(seed)
-    q, k, v, bt, lens = random_case(rng, [45, 16, 7], 4, 2, 16, 4, spare=5)
+    q, k, v, bt, lens = random_case(rng, [45, 16, 7], 4, 2, 16, 4, spare=5, kv=kv)
     o1, l1 = attend(q, k, v, bt, lens, 0.25, 4)
     perm = rng.permutation(k.shape[0])           # new physical page of old page p: perm[p]
     k2 = np.empty_like(k)
@@ -108,23 +126,23 @@ def pin_permutation(attend, seed=1):
     return np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
-def pin_lse_law(attend, seed=2):
+def pin_lse_law(attend, seed=2, kv="bf16"):
     """Append a token with known score and value; O must mix by e^LSE."""
     rng = np.random.default_rng(seed)
     P, d = 4, 8
-    q, k, v, bt, lens = random_case(rng, [10], 2, 1, d, P, spare=2, permute=False)
+    q, k, v, bt, lens = random_case(rng, [10], 2, 1, d, P, spare=2, permute=False, kv=kv)
     scale = 0.5
     o1, l1 = attend(q, k, v, bt, lens, scale, P)
     # token 10 sits in logical page 2, row 2, currently past the end (NaN)
     phys = bt[0, 10 // P]
-    kstar = f32_to_bf16_bits(rng.standard_normal(d))
-    vstar = f32_to_bf16_bits(rng.standard_normal(d))
+    kstar = kv_values(rng, d, kv)
+    vstar = kv_values(rng, d, kv)
     k[phys, 0, 10 % P, :] = kstar
     v[phys, 0, 10 % P, :] = vstar
     o2, l2 = attend(q, k, v, bt, np.array([11]), scale, P)
     qf = pa.bf16_bits_to_f64(q[0])
-    s = scale * (qf @ pa.bf16_bits_to_f64(kstar))               # [Hq]
-    vs = pa.bf16_bits_to_f64(vstar)
+    s = scale * (qf @ kv_f64(kstar))                            # [Hq]
+    vs = kv_f64(vstar)
     for h in range(2):
         w_old, w_new = math.exp(l1[0, h]), math.exp(s[h])
         exp_o = (w_old * o1[0, h] + w_new * vs) / (w_old + w_new)
@@ -192,43 +210,43 @@ def pin_golden(attend):
     return True
 
 
-def pin_closed_forms(attend, seed=4):
+def pin_closed_forms(attend, seed=4, kv="bf16"):
     """q = 0 -> mean V and LSE = ln L;  constant V -> that constant;
     L = 1 -> v_0 and LSE = s_0;  equal K rows -> mean V, LSE = s + ln L."""
     rng = np.random.default_rng(seed)
     P, d = 8, 16
-    q, k, v, bt, lens = random_case(rng, [57, 1, 23], 4, 1, d, P)
+    q, k, v, bt, lens = random_case(rng, [57, 1, 23], 4, 1, d, P, kv=kv)
     scale = 0.25
     # q = 0
     qz = np.zeros_like(q)
     o, l = attend(qz, k, v, bt, lens, scale, P)
     for b, L in enumerate(lens):
         t = np.arange(L)
-        vv = pa.bf16_bits_to_f64(v[bt[b, t // P], 0, t % P, :])
+        vv = kv_f64(v[bt[b, t // P], 0, t % P, :])
         if not np.allclose(o[b], vv.mean(axis=0)[None], atol=1e-12, rtol=0):
             return False
         if not np.allclose(l[b], math.log(L), atol=1e-12, rtol=0):
             return False
     # L = 1 (row 1)
     o, l = attend(q, k, v, bt, lens, scale, P)
-    k0 = pa.bf16_bits_to_f64(k[bt[1, 0], 0, 0])
-    v0 = pa.bf16_bits_to_f64(v[bt[1, 0], 0, 0])
+    k0 = kv_f64(k[bt[1, 0], 0, 0])
+    v0 = kv_f64(v[bt[1, 0], 0, 0])
     s0 = scale * (pa.bf16_bits_to_f64(q[1]) @ k0)
     if not (np.allclose(o[1], v0[None], atol=1e-12, rtol=0)
             and np.allclose(l[1], s0, atol=1e-12, rtol=0)):
         return False
     # all K rows equal, V constant per dim
     k2, v2 = k.copy(), v.copy()
-    row = f32_to_bf16_bits(rng.standard_normal(d))
-    crow = f32_to_bf16_bits(rng.standard_normal(d))
+    row = kv_values(rng, d, kv)
+    crow = kv_values(rng, d, kv)
     for b, L in enumerate(lens):
         t = np.arange(L)
         k2[bt[b, t // P], 0, t % P, :] = row
         v2[bt[b, t // P], 0, t % P, :] = crow
     o, l = attend(q, k2, v2, bt, lens, scale, P)
     for b, L in enumerate(lens):
-        s = scale * (pa.bf16_bits_to_f64(q[b]) @ pa.bf16_bits_to_f64(row))
-        if not np.allclose(o[b], pa.bf16_bits_to_f64(crow)[None], atol=1e-12, rtol=0):
+        s = scale * (pa.bf16_bits_to_f64(q[b]) @ kv_f64(row))
+        if not np.allclose(o[b], kv_f64(crow)[None], atol=1e-12, rtol=0):
             return False
         if not np.allclose(l[b], s + math.log(L), atol=1e-12, rtol=0):
             return False
@@ -240,16 +258,22 @@ def attend_oracle(q, k, v, bt, lens, scale, P):
 
 
 def all_attention_pins(attend):
-    """Run every attention pin; a pin that raises counts as failed."""
+    """Run every attention pin, for both cache element types where the pin
+    takes one; a pin that raises counts as failed."""
     res = {}
-    for name, pin in [("sdpa", pin_sdpa), ("permutation", pin_permutation),
-                      ("lse_law", pin_lse_law), ("golden", pin_golden),
-                      ("closed_forms", pin_closed_forms)]:
-        try:
-            res[name] = bool(pin(attend))
-        except (ValueError, IndexError, FloatingPointError):
-            res[name] = False
+    for name, pin, kvs in [("sdpa", pin_sdpa, KVS), ("permutation", pin_permutation, KVS),
+                           ("lse_law", pin_lse_law, KVS), ("golden", pin_golden, (None,)),
+                           ("closed_forms", pin_closed_forms, KVS)]:
+        for kv in kvs:
+            key = name if kv is None else f"{name}/{kv}"
+            try:
+                res[key] = bool(pin(attend) if kv is None else pin(attend, kv=kv))
+            except (ValueError, IndexError, FloatingPointError, TypeError):
+                res[key] = False
     return res
+
+
+KVS = ("bf16", "f32")
 
 
 # --------------------------------------------------------------- tests ----
@@ -261,16 +285,30 @@ def test_bf16_widening_exact():
     assert got.tolist() == want
 
 
-def test_matches_library_sdpa():
-    assert pin_sdpa(attend_oracle)
+def test_f32_widening_exact_and_other_types_refused():
+    vals = np.array([1.0, 0.1, -3.4028234663852886e38, 1e-45, -0.0, 1.0 + 2.0 ** -23], dtype=np.float32)
+    got = pa.kv_to_f64(vals)
+    want = [1.0, 0.10000000149011612, -3.4028234663852886e38, 2.0 ** -149, -0.0, 1.0 + 2.0 ** -23]
+    assert got.tolist() == want and np.signbit(got[4])
+    assert pa.kv_to_f64(np.array([0x3F80], dtype=np.uint16)).tolist() == [1.0]
+    for bad in (np.zeros(2, np.float16), np.zeros(2, np.float64), np.zeros(2, np.int32)):
+        with pytest.raises(TypeError):
+            pa.kv_to_f64(bad)
 
 
-def test_page_permutation_invariance_bitwise():
-    assert pin_permutation(attend_oracle)
+@pytest.mark.parametrize("kv", KVS)
+def test_matches_library_sdpa(kv):
+    assert pin_sdpa(attend_oracle, kv=kv)
 
 
-def test_lse_consistency_law():
-    assert pin_lse_law(attend_oracle)
+@pytest.mark.parametrize("kv", KVS)
+def test_page_permutation_invariance_bitwise(kv):
+    assert pin_permutation(attend_oracle, kv=kv)
+
+
+@pytest.mark.parametrize("kv", KVS)
+def test_lse_consistency_law(kv):
+    assert pin_lse_law(attend_oracle, kv=kv)
 
 
 def test_merge_identity():
@@ -281,8 +319,20 @@ def test_golden_closed_forms():
     assert pin_golden(attend_oracle)
 
 
-def test_closed_forms_random():
-    assert pin_closed_forms(attend_oracle)
+@pytest.mark.parametrize("kv", KVS)
+def test_closed_forms_random(kv):
+    assert pin_closed_forms(attend_oracle, kv=kv)
+
+
+def test_f32_cache_of_bf16_values_equals_bf16_cache():
+    # an fp32 cache holding exactly the bf16 values gives bit-identical results
+    rng = np.random.default_rng(6)
+    q, k, v, bt, lens = random_case(rng, [33, 70, 0, 5], 8, 2, 32, 16)
+    o1, l1 = pa.decode_attention(q, k, v, bt, lens, 0.2, 16)
+    kf = (k.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    vf = (v.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    o2, l2 = pa.decode_attention(q, kf, vf, bt, lens, 0.2, 16)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
 def test_merge_all_neutral_and_empty():
@@ -334,6 +384,25 @@ def _mutant(monkeypatch, kind):
             q2[s, h_kv * g:(h_kv + 1) * g] = q[s, idx]
             return orig_range(q2, k, v, bt, s, h_kv, lo, hi, sc, P)
         monkeypatch.setattr(pa, "range_state", r)
+    elif kind == "f32_cache_rounded_to_bf16":
+        orig_widen = pa.kv_to_f64
+
+        def w(x):
+            x = np.asarray(x)
+            if x.dtype == np.float32:      # reads the cache as if it were bf16
+                u = x.view(np.uint32).astype(np.uint64)
+                x = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+            return orig_widen(x)
+        monkeypatch.setattr(pa, "kv_to_f64", w)
+    elif kind == "f32_cache_truncated":
+        orig_widen = pa.kv_to_f64
+
+        def w(x):
+            x = np.asarray(x)
+            if x.dtype == np.float32:      # drops the low 16 mantissa bits
+                x = (x.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+            return orig_widen(x)
+        monkeypatch.setattr(pa, "kv_to_f64", w)
     elif kind == "lse_log2":
         def r(*a):
             o, l = orig_range(*a)
@@ -344,7 +413,7 @@ def _mutant(monkeypatch, kind):
             o, l = orig_range(q, k, v, bt, s, h_kv, lo, hi, sc, P)
             if hi <= lo:
                 return o, l
-            kk = pa.bf16_bits_to_f64(orig_gather(k, bt, s, h_kv, lo, hi, P))
+            kk = pa.kv_to_f64(orig_gather(k, bt, s, h_kv, lo, hi, P))
             g = q.shape[1] // k.shape[1]
             m = (sc * (pa.bf16_bits_to_f64(q[s, h_kv * g:(h_kv + 1) * g]) @ kk.T)).max(axis=1)
             return o, l - m
@@ -355,7 +424,8 @@ def _mutant(monkeypatch, kind):
 
 @pytest.mark.parametrize("kind", ["drop_last_token", "ignore_block_table", "row_offset_swapped",
                                   "k_v_swapped", "no_scale", "head_map_modulo", "lse_log2",
-                                  "lse_missing_max"])
+                                  "lse_missing_max", "f32_cache_rounded_to_bf16",
+                                  "f32_cache_truncated"])
 def test_planted_attention_mistakes_are_caught(monkeypatch, kind):
     _mutant(monkeypatch, kind)
     with np.errstate(all="ignore"):
