@@ -60,7 +60,7 @@ def parse():
     ap.add_argument("--kv", default="bf16", choices=["bf16", "f32"],
                     help="KV-cache element type of the main workload (and of --profile-pass)")
     ap.add_argument("--no-f32", action="store_true",
-                    help="skip the fp32 KV-cache measurements of the long, mixed and short workloads")
+                    help="skip the fp32 KV-cache measurements (long, mixed and short workloads, session loop)")
     ap.add_argument("--profile-pass", action="store_true",
                     help="for hardware-counter runs: a few untimed decode steps of the workload, "
                          "then a 1 GiB copy probe of known size (the counter reference)")
@@ -162,7 +162,7 @@ def measure(torch, pkv, workloads, name, steps, warmup, order, wg_per_cu, copies
     return res, wl
 
 
-def measure_loop(torch, pkv, workloads, steps, runs, gate, say, append=False):
+def measure_loop(torch, pkv, workloads, steps, runs, gate, say, append=False, kv="bf16"):
     """The 56-session resident loop: 32 layers of 32/8-head, head_dim 128
     decode attention per session, contexts U[2048, 16384] growing one token
     per step.  The resident kernel is launched once per run; per step the host
@@ -170,10 +170,11 @@ def measure_loop(torch, pkv, workloads, steps, runs, gate, say, append=False):
     latency = pkv_decode wall time (publish -> completion observed).  With
     append, each step also writes every session's newest token into the
     cache inside the same kernel (pages from a free list), and the cache
-    starts with the tokens before step 0 only."""
+    starts with the tokens before step 0 only.  kv = "f32": the same loop
+    over an fp32 cache."""
     from oracle import paged_attention as pa
-    sl = workloads.session_loop(steps=max(steps, 3), append=append)
-    tag = "loop+append" if append else "loop"
+    sl = workloads.session_loop(steps=max(steps, 3), append=append, kv_dtype=kv)
+    tag = ("loop+append" if append else "loop") + (" (fp32 cache)" if kv == "f32" else "")
     dev = "cuda"
     t0 = time.perf_counter()
     k, v, q = sl.pools("k", dev), sl.pools("v", dev), sl.queries(dev)
@@ -187,13 +188,14 @@ def measure_loop(torch, pkv, workloads, steps, runs, gate, say, append=False):
     new_v = sl.new_kv("v", dev) if append else None
     torch.cuda.synchronize()
     say(f"{tag} inputs generated in {time.perf_counter() - t0:.1f} s "
-        f"({2 * k.numel() * 2 / 1e9:.1f} GB of K/V)")
+        f"({2 * k.numel() * sl.kv_elem_bytes / 1e9:.1f} GB of K/V)")
     S, H, D = sl.sessions, sl.num_q_heads, sl.head_dim
     strides = (S * H * D, sl.pages_per_layer * sl.num_kv_heads * 16 * D, S * sl.max_pages,
                S * H * D, S * H)
     cfg = pkv.make_config(H, sl.num_kv_heads, D, sl.pages_per_layer, S, sl.max_pages,
                           scale=sl.scale, persistent=1, num_layers=sl.layers, timeout_ms=20000,
-                          append=1 if append else 0)
+                          append=1 if append else 0,
+                          kv_dtype=pkv.PKV_KV_F32 if kv == "f32" else pkv.PKV_KV_BF16)
     G = H // sl.num_kv_heads
 
     def one_run(n):
@@ -234,7 +236,7 @@ def measure_loop(torch, pkv, workloads, steps, runs, gate, say, append=False):
                 npg = -(-L // 16)
 
                 def paged(which):
-                    rows = workloads.bits_u16(sl.token_rows(which, t, layer, s, hk))
+                    rows = workloads.kv_host(sl.token_rows(which, t, layer, s, hk))
                     full = np.zeros((npg * 16, D), dtype=rows.dtype)
                     full[:L] = rows
                     return full.reshape(npg, 1, 16, D)
@@ -263,18 +265,18 @@ def measure_loop(torch, pkv, workloads, steps, runs, gate, say, append=False):
         say(f"{tag} parity after timing (steps 0, {steps // 2}, {steps - 1}): max abs err "
             f"{check([0, steps // 2, steps - 1]):.2e}")
     allv = np.concatenate(runs_out)
-    kv = np.array([sl.kv_bytes(t) for t in range(steps)])
-    gbs = kv / 1e9 / (np.concatenate([x[None] for x in runs_out]).mean(axis=0) * 1e-3)
+    step_bytes = np.array([sl.kv_bytes(t) for t in range(steps)])
+    gbs = step_bytes / 1e9 / (np.concatenate([x[None] for x in runs_out]).mean(axis=0) * 1e-3)
     res = {"sessions": S, "layers": sl.layers, "steps": steps, "runs": runs,
            "items_per_layer": int(info.n_items), "split": bool(info.split),
            "p50_ms": round(float(np.median(allv)), 4),
            "p99_ms": round(float(np.percentile(allv, 99)), 4),
            "max_ms": round(float(allv.max()), 4),
            "p99_per_run_ms": [round(float(np.percentile(x, 99)), 4) for x in runs_out],
-           "kv_gb_per_step_mean": round(float(kv.mean() / 1e9), 3),
+           "kv_gb_per_step_mean": round(float(step_bytes.mean() / 1e9), 3),
            "kv_gbs_median": round(float(np.median(gbs)), 1),
            "pct_of_hbm_peak_median": round(float(np.median(gbs)) / HBM_PEAK_GBS * 100, 2),
-           "launches_per_step": 0, "append": bool(append)}
+           "launches_per_step": 0, "append": bool(append), "kv_dtype": kv}
     del k, v, q, out, lse, new_k, new_v
     torch.cuda.empty_cache()
     return res
@@ -639,13 +641,16 @@ def main():
             f32[name]["decode_frac"] = r["decode_gbs"] / HBM_PEAK_GBS
             say(f"{name} (fp32 cache): {r['gbs']:.1f} GB/s per step, decode {r['decode_gbs']:.1f} GB/s "
                 f"({r['decode_ms_mean'] * 1e3:.1f} us)")
-    loop = loop_append = None
+    loop = loop_append = loop_f32 = None
     if args.loop_steps > 0:
         loop = measure_loop(torch, pkv, workloads, args.loop_steps, args.loop_runs,
                             not args.no_gate, say)
         if not args.no_loop_append:
             loop_append = measure_loop(torch, pkv, workloads, args.loop_steps, args.loop_runs,
                                        not args.no_gate, say, append=True)
+        if not args.no_f32:
+            loop_f32 = measure_loop(torch, pkv, workloads, args.loop_steps, args.loop_runs,
+                                    not args.no_gate, say, kv="f32")
     abl = ablations(torch, pkv, workloads, args, say) if args.ablations else None
     density = density_search(torch, pkv, workloads, (10, 20), 160, 100, 3, say) if args.density else None
     cpu = None
@@ -685,6 +690,7 @@ def main():
         "session_loop_p99_ms": loop["p99_ms"] if loop else None,
         "session_loop": loop,
         "session_loop_append": loop_append,
+        "session_loop_f32": loop_f32,
         "session_density": density,
         "other_workloads": others,
         "kv_f32": f32 or None,

@@ -98,8 +98,8 @@ enum { PKV_SCHEDULE_ATOMIC = 0, PKV_SCHEDULE_STATIC = 1 };
  * as in the fp32 attention cache of the text-to-speech model on the WPK note
  * ("Same precision" list); the same kernels read twice the bytes per token,
  * q.K and P.V run in fp32 on the full-precision values (q stays bf16, widened
- * exactly).  q, out and lse keep their types.  The resident loop takes BF16
- * only. */
+ * exactly).  q, out and lse keep their types.  One-shot launches and the
+ * resident loop (with or without append) take either. */
 enum { PKV_KV_BF16 = 0, PKV_KV_F32 = 1 };
 
 /* How split rows are merged.  FUSED: inside the decode kernel, the last
@@ -160,7 +160,7 @@ typedef struct pkv_tensors {
      * same queue serves every layer).  Ignored when num_layers is 1. */
     int64_t layer_stride_q, layer_stride_kv, layer_stride_bt, layer_stride_out, layer_stride_lse;
     /* Resident loop with append = 1: the K and V of each session's newest token
-     * (token ctx_lens[b] - 1), bf16 [B][Hkv][D] per layer, layer l at
+     * (token ctx_lens[b] - 1), kv_dtype [B][Hkv][D] per layer, layer l at
      * new_k + l * layer_stride_new elements (likewise new_v).  Null otherwise. */
     const void* new_k;
     const void* new_v;

@@ -161,7 +161,7 @@ pkv_status start_loop(pkv_handle* h) {
         clock_khz = 100000;                                          // 100 MHz, the CDNA wall clock
     lp.timeout_ticks = (uint64_t)h->r.timeout_ms * (uint64_t)clock_khz;
     lp.max_batch = h->r.max_batch;
-    int rc = launch_resident(lp, h->r.d, h->r.g, h->grid, h->stream);
+    int rc = launch_resident(lp, h->r.d, h->r.g, h->r.kv_dtype, h->grid, h->stream);
     if (rc != 0) return hip_fail(h, (hipError_t)rc, "resident launch");
     h->loop_running = true;
     return PKV_OK;

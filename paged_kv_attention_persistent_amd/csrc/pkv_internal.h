@@ -222,6 +222,6 @@ int launch_debug_gather(const DecodeParams& p, int head_dim, int kv_dtype, int i
 bool supported_shape(int head_dim, int group);
 int launch_copy_probe(void* dst, const void* src, size_t bytes, int grid, void* stream);
 int launch_read_probe(const void* src, size_t bytes, void* sink, int grid, void* stream);
-int launch_resident(const LoopParams& lp, int head_dim, int group, int grid, void* stream);
+int launch_resident(const LoopParams& lp, int head_dim, int group, int kv_dtype, int grid, void* stream);
 
 }  // namespace pkv

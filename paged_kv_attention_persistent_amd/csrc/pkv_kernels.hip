@@ -867,9 +867,9 @@ __device__ __forceinline__ void st_agt(uint32_t* p, uint32_t v) {
 // for the row is the page id, and every head's item writes it into the block
 // table (the same value).  Stores are agent-coherent: later steps read the
 // row and the entry from other XCDs.  All threads of the workgroup call this.
-template <int D>
+template <int D, typename KV>
 __device__ void append_token(const DecodeParams& Q, const int32_t* grants, const ItemRef& it,
-                             const uint16_t* new_k, const uint16_t* new_v, int tid) {
+                             const char* new_k, const char* new_v, int tid) {
     const uint32_t j = it.te - 1;
     const int pj = (int)(j / kPageSize), off = (int)(j % kPageSize);
     uint32_t* btw = reinterpret_cast<uint32_t*>(const_cast<int32_t*>(Q.block_table) + (size_t)it.b * Q.bt_stride + pj);
@@ -881,13 +881,13 @@ __device__ void append_token(const DecodeParams& Q, const int32_t* grants, const
         return;
     }
     if (off == 0 && tid == 0) st_agt(btw, (uint32_t)page);
-    const size_t row = (((size_t)page * Q.hkv + it.hk) * kPageSize + off) * D;
-    const size_t src = ((size_t)it.b * Q.hkv + it.hk) * D;
-    uint32_t* dk = reinterpret_cast<uint32_t*>(const_cast<uint16_t*>(Q.k_pool) + row);
-    uint32_t* dv = reinterpret_cast<uint32_t*>(const_cast<uint16_t*>(Q.v_pool) + row);
+    const size_t row = (((size_t)page * Q.hkv + it.hk) * kPageSize + off) * D * KV::kBytes;
+    const size_t src = ((size_t)it.b * Q.hkv + it.hk) * D * KV::kBytes;
+    uint32_t* dk = reinterpret_cast<uint32_t*>(const_cast<char*>(reinterpret_cast<const char*>(Q.k_pool)) + row);
+    uint32_t* dv = reinterpret_cast<uint32_t*>(const_cast<char*>(reinterpret_cast<const char*>(Q.v_pool)) + row);
     const uint32_t* sk = reinterpret_cast<const uint32_t*>(new_k + src);
     const uint32_t* sv = reinterpret_cast<const uint32_t*>(new_v + src);
-    for (int t = tid; t < D / 2; t += kThreads) {
+    for (int t = tid; t < D * KV::kBytes / 4; t += kThreads) {
         st_agt(dk + t, ld_sys(sk + t));
         st_agt(dv + t, ld_sys(sv + t));
     }
@@ -906,7 +906,7 @@ __device__ __forceinline__ bool wait_at_least(const uint32_t* p, uint32_t target
     return true;
 }
 
-template <int D, int G>
+template <int D, int G, typename KV>
 __global__ __launch_bounds__(kThreads) void resident_kernel(LoopParams L) {
     __shared__ Smem<D, G> sm;
     __shared__ uint32_t s_epoch, s_exit;
@@ -1011,8 +1011,8 @@ __global__ __launch_bounds__(kThreads) void resident_kernel(LoopParams L) {
         P.batch = (int32_t)uni((uint32_t)s_desc[11]);
         P.bt_stride = (int32_t)uni((uint32_t)(s_desc[11] >> 32));
         const int n_layers = (int)uni((uint32_t)s_desc[12]);
-        const uint16_t* new_k = reinterpret_cast<const uint16_t*>(uni64(s_desc[13]));
-        const uint16_t* new_v = reinterpret_cast<const uint16_t*>(uni64(s_desc[14]));
+        const char* new_k = reinterpret_cast<const char*>(uni64(s_desc[13]));
+        const char* new_v = reinterpret_cast<const char*>(uni64(s_desc[14]));
         const int64_t ls_new = (int64_t)uni64(s_desc[15]);
         const int32_t* grants = reinterpret_cast<const int32_t*>(slot + L.grant_off);
         P.qhdr = reinterpret_cast<const QHdr*>(slot + L.q_hdr_off);
@@ -1037,8 +1037,11 @@ __global__ __launch_bounds__(kThreads) void resident_kernel(LoopParams L) {
                 const uint32_t i = idx - (uint32_t)layer * n_items;
                 DecodeParams Q = P;
                 Q.q = P.q + layer * ls_q;
-                Q.k_pool = P.k_pool + layer * ls_kv;
-                Q.v_pool = P.v_pool + layer * ls_kv;
+                // the layer stride counts cache elements
+                Q.k_pool = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(P.k_pool) +
+                                                             layer * ls_kv * KV::kBytes);
+                Q.v_pool = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(P.v_pool) +
+                                                             layer * ls_kv * KV::kBytes);
                 Q.block_table = P.block_table + layer * ls_bt;
                 Q.out = P.out + layer * ls_out;
                 Q.lse = P.lse + layer * ls_lse;
@@ -1069,8 +1072,9 @@ __global__ __launch_bounds__(kThreads) void resident_kernel(LoopParams L) {
                     if (s_exit) { ok = false; break; }
                 }
                 if (L.append && it.ok && it.chunk == it.nch - 1)
-                    append_token<D>(Q, grants, it, new_k + layer * ls_new, new_v + layer * ls_new, tid);
-                process_item<D, G, KvBf16>(Q, sm, it, nxt);
+                    append_token<D, KV>(Q, grants, it, new_k + layer * ls_new * KV::kBytes,
+                                        new_v + layer * ls_new * KV::kBytes, tid);
+                process_item<D, G, KV>(Q, sm, it, nxt);
             } else {
                 // rows with no tokens take the neutral state, in every layer;
                 // thread 0 finds them (64 merge rows at a time), all threads write
@@ -1467,13 +1471,16 @@ int launch_zero(void* p, size_t bytes, void* stream) {
 }
 
 template <int D, int G>
-int launch_resident_t(const LoopParams& lp, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((resident_kernel<D, G>), dim3(grid), dim3(kThreads), 0, s, lp);
+int launch_resident_t(const LoopParams& lp, int kv_dtype, int grid, hipStream_t s) {
+    if (kv_dtype == PKV_KV_F32)
+        hipLaunchKernelGGL((resident_kernel<D, G, KvF32>), dim3(grid), dim3(kThreads), 0, s, lp);
+    else
+        hipLaunchKernelGGL((resident_kernel<D, G, KvBf16>), dim3(grid), dim3(kThreads), 0, s, lp);
     return (int)hipGetLastError();
 }
 
-int launch_resident(const LoopParams& lp, int head_dim, int group, int grid, void* stream) {
-    PKV_DISPATCH(launch_resident_t, head_dim, group, lp, grid, (hipStream_t)stream);
+int launch_resident(const LoopParams& lp, int head_dim, int group, int kv_dtype, int grid, void* stream) {
+    PKV_DISPATCH(launch_resident_t, head_dim, group, lp, kv_dtype, grid, (hipStream_t)stream);
 }
 
 int launch_decode(const DecodeParams& p, int head_dim, int group, int kv_dtype, int grid, void* stream) {

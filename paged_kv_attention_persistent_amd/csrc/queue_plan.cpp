@@ -94,7 +94,6 @@ pkv_status resolve_config(const pkv_config* cfg, int device_cus, Resolved* r, co
     if (cfg->append && !r->persistent) { *why = "append needs the resident loop"; return PKV_ERR_INVALID_ARG; }
     r->append = cfg->append;
     if (cfg->kv_dtype != PKV_KV_BF16 && cfg->kv_dtype != PKV_KV_F32) { *why = "unknown kv_dtype"; return PKV_ERR_INVALID_ARG; }
-    if (cfg->kv_dtype != PKV_KV_BF16 && r->persistent) { *why = "the resident loop reads a bf16 cache"; return PKV_ERR_UNSUPPORTED; }
     r->kv_dtype = cfg->kv_dtype;
     if ((int64_t)r->max_items * r->num_layers > ((int64_t)1 << 31) / (4 * r->g * r->d)) {
         *why = "partial-state storage too large"; return PKV_ERR_CAPACITY;

@@ -381,10 +381,25 @@ class SessionLoop:
     scale: float = 0.0
     append: bool = False
     free_pages: np.ndarray = None     # append: page ids not in use before step 0
+    kv_dtype: str = "bf16"            # element type of the cache (pools and new tokens)
 
     def __post_init__(self):
         if self.scale == 0.0:
             self.scale = 1.0 / math.sqrt(self.head_dim)
+        if self.kv_dtype not in KV_DTYPES:
+            raise ValueError(f"kv_dtype must be one of {sorted(KV_DTYPES)}")
+
+    @property
+    def kv_torch_dtype(self):
+        return KV_DTYPES[self.kv_dtype]
+
+    @property
+    def kv_elem_bytes(self) -> int:
+        return 4 if self.kv_dtype == "f32" else 2
+
+    def with_kv_dtype(self, kv_dtype: str) -> "SessionLoop":
+        """The same loop (same streams, same tables) with another cache type."""
+        return replace(self, kv_dtype=kv_dtype)
 
     @property
     def max_pages(self) -> int:
@@ -395,14 +410,14 @@ class SessionLoop:
 
     def kv_bytes(self, t: int) -> int:
         return int(self.ctx_lens(t).astype(np.int64).sum()) * self.layers * self.num_kv_heads \
-            * self.head_dim * 2 * 2
+            * self.head_dim * self.kv_elem_bytes * 2
 
     def pools(self, which: str, device) -> torch.Tensor:
-        """[layers][pages][Hkv][P][D] bf16 (one stream per tensor name).  With
-        append, rows that hold no token before step 0 are NaN."""
+        """[layers][pages][Hkv][P][D] of kv_dtype (one stream per tensor name).
+        With append, rows that hold no token before step 0 are NaN."""
         t = torch.empty(self.layers, self.pages_per_layer, self.num_kv_heads, self.page_size,
-                        self.head_dim, dtype=torch.bfloat16, device=device)
-        t = fill_normal_bf16(t, self.seed, self.name + "/" + which)
+                        self.head_dim, dtype=self.kv_torch_dtype, device=device)
+        t = fill_normal(t, self.seed, self.name + "/" + which)
         if self.append:
             P = self.page_size
             valid = np.zeros((self.layers, self.pages_per_layer, P), dtype=bool)
@@ -414,26 +429,30 @@ class SessionLoop:
                 valid[lay, self.block_tables[:, s, :n - 1]] = True          # full pages
                 valid[np.arange(self.layers), self.block_tables[:, s, n - 1], :int(L) - (n - 1) * P] = True
             bad = torch.as_tensor(~valid).to(device)[:, :, None, :, None].expand_as(t)
-            t.view(torch.int16)[bad] = 0x7FC0
+            if t.dtype == torch.float32:
+                t.view(torch.int32)[bad] = F32_NAN
+            else:
+                t.view(torch.int16)[bad] = BF16_NAN
         return t
 
     def new_kv(self, which: str, device) -> torch.Tensor:
-        """Append: K or V of each step's new token, [steps][layers][sessions][Hkv][D] bf16."""
+        """Append: K or V of each step's new token, [steps][layers][sessions][Hkv][D]
+        of kv_dtype."""
         t = torch.empty(self.steps, self.layers, self.sessions, self.num_kv_heads, self.head_dim,
-                        dtype=torch.bfloat16, device=device)
-        return fill_normal_bf16(t, self.seed, self.name + "/new_" + which)
+                        dtype=self.kv_torch_dtype, device=device)
+        return fill_normal(t, self.seed, self.name + "/new_" + which)
 
     def new_kv_unit(self, which: str, t: int, layer: int, s: int, kv_head: int) -> torch.Tensor:
         """CPU regeneration of new_kv(which)[t][layer][s][kv_head] ([D])."""
         D = self.head_dim
         off = (((t * self.layers + layer) * self.sessions + s) * self.num_kv_heads + kv_head) * D
         idx = torch.arange(off, off + D, dtype=torch.int64)
-        return _to_bf16(normal_bf16_bits(self.seed, self.name + "/new_" + which, idx))
+        return normal_values(self.seed, self.name + "/new_" + which, idx, self.kv_torch_dtype)
 
     def token_rows(self, which: str, t: int, layer: int, s: int, kv_head: int) -> torch.Tensor:
         """The L_s(t) tokens of (layer, session, KV head) at step t in order, [L][D]
-        bf16: the cache's tokens before step 0, then with append the tokens of
-        steps 0..t."""
+        of kv_dtype: the cache's tokens before step 0, then with append the
+        tokens of steps 0..t."""
         L = int(self.ctx_lens(t)[s])
         P = self.page_size
         if not self.append:
@@ -482,14 +501,14 @@ class SessionLoop:
         pages = torch.as_tensor(np.asarray(pages, dtype=np.int64))
         idx = (base + pages[:, None] * per_page + kv_head * slab
                + torch.arange(slab, dtype=torch.int64)[None, :])
-        bits = normal_bf16_bits(self.seed, self.name + "/" + which, idx.reshape(-1))
-        return _to_bf16(bits).view(len(pages), self.page_size, self.head_dim)
+        vals = normal_values(self.seed, self.name + "/" + which, idx.reshape(-1), self.kv_torch_dtype)
+        return vals.view(len(pages), self.page_size, self.head_dim)
 
 
 def session_loop(seed: int = MEASURE_SEED, sessions: int = 56, layers: int = 32,
                  steps: int = 200, lo: int = 2048, hi: int = 16384, num_q_heads: int = 32,
                  num_kv_heads: int = 8, head_dim: int = 128, name: str = "loop",
-                 append: bool = False) -> SessionLoop:
+                 append: bool = False, kv_dtype: str = "bf16") -> SessionLoop:
     """56 sessions x 32 layers, contexts U[2048, 16384] growing one token per
     step for 200 steps, 32/8 heads, head_dim 128.  append=True: see SessionLoop."""
     rng = np.random.default_rng([seed, 5, zlib.crc32(name.encode())])
@@ -510,7 +529,8 @@ def session_loop(seed: int = MEASURE_SEED, sessions: int = 56, layers: int = 32,
                 pos += n
         free = np.arange(n_init, n_init + n_grow, dtype=np.int32)
         return SessionLoop(name, sessions, layers, steps, num_q_heads, num_kv_heads, head_dim,
-                           l0, bts, max(n_init + n_grow, 1), seed, append=True, free_pages=free)
+                           l0, bts, max(n_init + n_grow, 1), seed, append=True, free_pages=free,
+                           kv_dtype=kv_dtype)
     need = [-(-int(L + steps) // 16) for L in l0]
     npg = int(sum(need))
     maxp = max(need)
@@ -522,4 +542,4 @@ def session_loop(seed: int = MEASURE_SEED, sessions: int = 56, layers: int = 32,
             bts[layer, s, :n] = perm[pos:pos + n]
             pos += n
     return SessionLoop(name, sessions, layers, steps, num_q_heads, num_kv_heads, head_dim,
-                       l0, bts, npg, seed)
+                       l0, bts, npg, seed, kv_dtype=kv_dtype)

@@ -137,7 +137,7 @@ def test_config_validation():
            dict(kv_chunk_tokens=-16),
            dict(num_pages=0), dict(wg_per_cu=9), dict(policy=7), dict(num_q_heads=64),
            dict(merge_mode=2), dict(schedule=2), dict(persistent=1, schedule=1), dict(append=2),
-           dict(append=1), dict(kv_dtype=2), dict(kv_dtype=-1), dict(persistent=1, kv_dtype=1)]
+           dict(append=1), dict(kv_dtype=2), dict(kv_dtype=-1)]
     base = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, num_pages=100, max_batch=4,
                 max_pages_per_seq=10, num_cus=256)
     for b in bad:
@@ -153,9 +153,7 @@ def test_config_validation():
     c.reserved[1] = 1
     with pytest.raises(pkv.PkvError):
         pkv.pkv_workspace_size(c)
-    with pytest.raises(pkv.PkvError) as e:
-        pkv.pkv_workspace_size(pkv.make_config(**dict(base, persistent=1, kv_dtype=1)))
-    assert e.value.status == pkv.PKV_ERR_UNSUPPORTED
+    assert pkv.pkv_workspace_size(pkv.make_config(**dict(base, persistent=1, kv_dtype=1))) > 0
 
 
 def test_f32_cache_plan_and_layout():

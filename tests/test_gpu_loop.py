@@ -5,6 +5,7 @@ host publishes; no other GPU work may be queued while it runs (it holds every
 CU), so each test writes all steps' outputs into per-step buffers and reads
 them only after pkv_destroy.  Parity bar as for the one-shot path: max-abs
 2e-2 and mean-abs 2e-3 against the float64 oracle, for O and for the LSE.
+Loops run with a bf16 and with an fp32 KV cache.
 """
 
 import time
@@ -47,6 +48,7 @@ class Loop:
         self.lens = torch.zeros(sl.sessions, dtype=torch.int32, device=dev)
         torch.cuda.synchronize()
         cfgkw.setdefault("num_cus", torch.cuda.get_device_properties(0).multi_processor_count)
+        cfgkw.setdefault("kv_dtype", pkv.PKV_KV_F32 if sl.kv_dtype == "f32" else pkv.PKV_KV_BF16)
         self.cfg = pkv.make_config(sl.num_q_heads, sl.num_kv_heads, sl.head_dim, sl.pages_per_layer,
                                    sl.sessions, sl.max_pages, scale=sl.scale, persistent=1,
                                    num_layers=sl.layers, timeout_ms=timeout_ms, **cfgkw)
@@ -89,7 +91,7 @@ def oracle_unit(sl, t, layer, s, hk):
     npg = -(-L // 16)
 
     def paged(which):
-        rows = workloads.bits_u16(sl.token_rows(which, t, layer, s, hk))
+        rows = workloads.kv_host(sl.token_rows(which, t, layer, s, hk))
         full = np.zeros((npg * 16, sl.head_dim), dtype=rows.dtype)
         full[:L] = rows
         return full.reshape(npg, 1, 16, sl.head_dim)
@@ -122,9 +124,12 @@ def check_all(lp, units=None):
     assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS and lerr.max() <= MAX_ABS
 
 
-@pytest.mark.parametrize("variant", ["nosplit_d128", "split_d128", "nosplit_d64_g8", "many_steps"])
+@pytest.mark.parametrize("variant", ["nosplit_d128", "split_d128", "nosplit_d64_g8", "many_steps",
+                                     "nosplit_d128_f32", "split_d128_f32", "nosplit_d64_g8_f32"])
 def test_small_loop_every_output(variant):
     say("variant", variant)
+    kv = "f32" if variant.endswith("_f32") else "bf16"
+    variant = variant.removesuffix("_f32")
     if variant == "nosplit_d128":
         sl = workloads.session_loop(seed=11, sessions=5, layers=3, steps=4, lo=1, hi=60,
                                     num_q_heads=8, num_kv_heads=2, name="loop_small")
@@ -144,7 +149,7 @@ def test_small_loop_every_output(variant):
         sl = workloads.session_loop(seed=17, sessions=3, layers=2, steps=48, lo=1, hi=70,
                                     num_q_heads=4, num_kv_heads=1, name="loop_many")
         kw = dict(policy=pkv.PKV_POLICY_AUTO, kv_chunk_tokens=32)
-    lp = Loop(sl, **kw)
+    lp = Loop(sl.with_kv_dtype(kv), **kw)
     try:
         for t in range(sl.steps):
             dt, info = lp.step(t)
@@ -198,14 +203,16 @@ def test_loop_rejects_one_shot_only_calls():
         lp.close()
 
 
+@pytest.mark.parametrize("kv", ["bf16", "f32"])
 @pytest.mark.parametrize("variant", ["nosplit", "split"])
-def test_loop_append_writes_tokens_and_grows_block_tables(variant):
+def test_loop_append_writes_tokens_and_grows_block_tables(variant, kv):
     # each step appends every session's newest token and takes a page from the
     # free list when it opens one; outputs match the oracle over the logical
     # token sequence, and the cache and block tables end up bit-exact
-    say("append", variant)
+    say("append", variant, kv)
     sl = workloads.session_loop(seed=21, sessions=5, layers=2, steps=40, lo=1, hi=40,
-                                num_q_heads=8, num_kv_heads=2, name="loop_append", append=True)
+                                num_q_heads=8, num_kv_heads=2, name="loop_append", append=True,
+                                kv_dtype=kv)
     kw = dict(policy=pkv.PKV_POLICY_NO_SPLIT) if variant == "nosplit" else \
         dict(policy=pkv.PKV_POLICY_SPLIT, kv_chunk_tokens=32)
     lp = Loop(sl, **kw)
@@ -218,17 +225,17 @@ def test_loop_append_writes_tokens_and_grows_block_tables(variant):
     check_all(lp)
     want_bt = sl.appended_block_tables(sl.steps)
     assert np.array_equal(lp.bt.cpu().numpy(), want_bt)
-    kb, vb = workloads.bits_u16(lp.k.cpu()), workloads.bits_u16(lp.v.cpu())
+    kb, vb = workloads.kv_host(lp.k.cpu()), workloads.kv_host(lp.v.cpu())
     for layer in range(sl.layers):
         for s in range(sl.sessions):
             for hk in range(sl.num_kv_heads):
                 for t in range(sl.steps):
                     j = int(sl.l0[s]) - 1 + t
                     pg = want_bt[layer, s, j // 16]
-                    assert np.array_equal(kb[layer, pg, hk, j % 16],
-                                          workloads.bits_u16(sl.new_kv_unit("k", t, layer, s, hk)))
-                    assert np.array_equal(vb[layer, pg, hk, j % 16],
-                                          workloads.bits_u16(sl.new_kv_unit("v", t, layer, s, hk)))
+                    want_k = workloads.kv_host(sl.new_kv_unit("k", t, layer, s, hk))
+                    want_v = workloads.kv_host(sl.new_kv_unit("v", t, layer, s, hk))
+                    assert kb[layer, pg, hk, j % 16].tobytes() == want_k.tobytes()
+                    assert vb[layer, pg, hk, j % 16].tobytes() == want_v.tobytes()
 
 
 def test_loop_append_errors():
