@@ -395,12 +395,14 @@ def density_search(torch, pkv, workloads, periods_ms, max_sessions, steps, runs,
     return res
 
 
-def measured_traffic(root):
-    """HBM bytes per decode launch from the committed counter summary, if it
-    was taken on the kernel source as it is now (else None)."""
+def measured_traffic(root, kv="bf16"):
+    """HBM bytes per decode launch of the long context from the committed
+    counter summary, if it was taken on the kernel source as it is now (else
+    None)."""
     import hashlib
     import re
-    prof = os.path.join(root, "profiles", "decode_kernel_long_context_traffic.md")
+    name = "decode_kernel_long_context" + ("_fp32_cache" if kv == "f32" else "") + "_traffic.md"
+    prof = os.path.join(root, "profiles", name)
     src = os.path.join(root, "paged_kv_attention_persistent_amd", "csrc", "pkv_kernels.hip")
     try:
         text = open(prof).read()
@@ -639,6 +641,8 @@ def main():
                                            "items", "chunk_tokens", "kv_bytes")}
             f32[name]["pct_of_hbm_peak"] = 100.0 * r["gbs"] / HBM_PEAK_GBS
             f32[name]["decode_frac"] = r["decode_gbs"] / HBM_PEAK_GBS
+            if name == "long":
+                f32[name]["traffic"] = measured_traffic(os.path.dirname(os.path.abspath(__file__)), "f32")
             say(f"{name} (fp32 cache): {r['gbs']:.1f} GB/s per step, decode {r['decode_gbs']:.1f} GB/s "
                 f"({r['decode_ms_mean'] * 1e3:.1f} us)")
     loop = loop_append = loop_f32 = None
@@ -682,8 +686,8 @@ def main():
                    "kv_bytes_per_step": main_res["kv_bytes"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__)))
-                     if args.workload == "long" and args.kv == "bf16" else None,
+                     "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__)), args.kv)
+                     if args.workload == "long" else None,
                      "kernel": f"decode_kernel<128,4,{'KvF32' if args.kv == 'f32' else 'KvBf16'}>",
                      "decode_us_mean": round(main_res["decode_ms_mean"] * 1e3, 3)},
         "cpu_baseline": cpu,

@@ -211,6 +211,8 @@ typedef struct pkv_layout {
     uint64_t arrive_off;        /* uint32 [layers][max_batch][Hkv] arrival counters of the fused merge */
     uint64_t loop_off;          /* resident loop: control mirror and two slots of step counters */
     uint64_t loop_mirror_off;   /* resident loop: device copies of the two host queue slots */
+    uint64_t sink_off;          /* 4 KiB read by the gather's look-ahead past the end of a
+                                   page window (the values are never used) */
     uint64_t total_bytes;
     int32_t max_items;
     int32_t reserved;

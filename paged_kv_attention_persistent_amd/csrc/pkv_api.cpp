@@ -90,6 +90,7 @@ DecodeParams make_params(const pkv_handle* h, const pkv_tensors* t) {
     p.merge_rows = reinterpret_cast<const int32_t*>(h->ws + h->lay.merge_rows_off);
     p.items = reinterpret_cast<const Item*>(h->ws + h->lay.items_off);
     p.partial_o = reinterpret_cast<float*>(h->ws + h->lay.partial_o_off);
+    p.sink = reinterpret_cast<const char*>(h->ws + h->lay.sink_off);
     p.partial_lse = reinterpret_cast<float*>(h->ws + h->lay.partial_lse_off);
     p.arrive = reinterpret_cast<uint32_t*>(h->ws + h->lay.arrive_off);
     p.trace = h->trace;

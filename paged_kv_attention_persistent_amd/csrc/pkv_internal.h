@@ -14,6 +14,7 @@ constexpr int kPageSize = 16;          // tokens per page (the only size built)
 constexpr int kThreads = 512;          // 8 waves of 64 lanes per workgroup
 constexpr int kWaves = kThreads / 64;
 constexpr int kFitMinPages = 64;       // chunk mode "fit": ranges of at least 64 pages
+constexpr int kSinkBytes = 4096;       // >= the largest tile (16 rows x 128 bf16, 8 rows x 128 fp32)
 
 // One queue item: a non-empty token range [tok_begin, tok_end) of one
 // (sequence, KV head).  16 bytes, little-endian.
@@ -169,6 +170,7 @@ struct DecodeParams {
     int32_t fused_merge;        // 1: last arriver merges inside the decode kernel
     int32_t static_sched;       // 1: workgroup g runs items g, g + grid, ... (no claims)
     float scale_log2;           // scale * log2(e)
+    const char* sink;           // kSinkBytes the look-ahead reads past a window's end
 };
 
 // Resident-loop kernel parameters: the per-step constant part of the decode

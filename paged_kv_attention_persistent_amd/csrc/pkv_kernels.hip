@@ -118,25 +118,37 @@ __device__ __forceinline__ void report(const Ctrl* c0, uint32_t* host_error, uin
 // lane, 8*j + r for j = 0, 1), half a page for fp32 (one token row per lane,
 // row 8*h + r of half h); either way 8 KB per wave at D = 128, so both
 // element types keep the same registers per tile and the same pipeline.
+//
+// Lane p of a row's 8 lanes holds 16-byte word w of the row at byte
+// 128 w + 16 p, so each load instruction of the 8 lanes covers one whole
+// 128-byte line.  Word w holds dims dim(p, w, 0 ..): bf16, 8 dims from
+// 64 w + 8 p; fp32, 4 dims from 32 w + 4 p.
 struct KvBf16 {
     static constexpr int kBytes = 2;
     static constexpr int kRows = 2;            // token rows per lane in a tile
     static constexpr int kTilesPerPage = 1;
+    static constexpr int kDimsPerWord = 8;
 };
 struct KvF32 {
     static constexpr int kBytes = 4;
     static constexpr int kRows = 1;
     static constexpr int kTilesPerPage = 2;
+    static constexpr int kDimsPerWord = 4;
 };
 
-// Per-lane share of one tile of K and V: kRows token rows times D/64 pieces
-// of 8 dims (piece 8*k + p of the row), each piece QW 16-byte words.
+// Dim held by lane p in element i of its word w.
+template <typename KV>
+__device__ __forceinline__ int word_dim(int p, int w, int i) {
+    return KV::kDimsPerWord * (8 * w + p) + i;
+}
+
+// Per-lane share of one tile of K and V: kRows token rows times NW 16-byte
+// words of the row (D / 64 words for bf16, D / 32 for fp32).
 template <int D, typename KV>
 struct Tile {
-    static constexpr int NPC = D / 64;
-    static constexpr int QW = KV::kBytes / 2;
-    u32x4 k[KV::kRows][NPC * QW];
-    u32x4 v[KV::kRows][NPC * QW];
+    static constexpr int NW = D * KV::kBytes / 128;
+    u32x4 k[KV::kRows][NW];
+    u32x4 v[KV::kRows][NW];
 };
 
 // Byte offsets of the lane's token rows inside a tile (the tile's first row
@@ -152,7 +164,7 @@ __device__ __forceinline__ LaneOff lane_offsets(int r, int p, int valid) {
     constexpr int RB = D * KV::kBytes;                        // bytes per token row
     const int t0 = r < valid ? r : 0;
     const int t1 = 8 + r < valid ? 8 + r : 0;
-    return {(uint32_t)(t0 * RB + p * 8 * KV::kBytes), (uint32_t)(t1 * RB + p * 8 * KV::kBytes)};
+    return {(uint32_t)(t0 * RB + p * 16), (uint32_t)(t1 * RB + p * 16)};
 }
 
 // Streaming 16-byte load with the non-temporal hint: K/V pages are read
@@ -164,21 +176,18 @@ __device__ __forceinline__ u32x4 ld_stream(const char* p) {
 }
 
 // The gather of one tile: ks / vs are the wave-uniform addresses of the
-// tile's first row, the lane adds its 32-bit row offset; piece k sits
-// 64 * element-size bytes further on, and its QW words are consecutive.
+// tile's first row, the lane adds its 32-bit row offset; word w sits 128 w
+// bytes further on.
 template <int D, typename KV>
 __device__ __forceinline__ void load_tile(Tile<D, KV>& t, const char* ks, const char* vs, LaneOff o) {
-    constexpr int QW = Tile<D, KV>::QW;
 #pragma unroll
-    for (int k = 0; k < Tile<D, KV>::NPC; ++k)
-#pragma unroll
-        for (int q = 0; q < QW; ++q) {
-            const uint32_t off = 64 * KV::kBytes * k + 16 * q;
-            t.k[0][k * QW + q] = ld_stream(ks + o.o0 + off);
-            if constexpr (KV::kRows == 2) t.k[1][k * QW + q] = ld_stream(ks + o.o1 + off);
-            t.v[0][k * QW + q] = ld_stream(vs + o.o0 + off);
-            if constexpr (KV::kRows == 2) t.v[1][k * QW + q] = ld_stream(vs + o.o1 + off);
-        }
+    for (int w = 0; w < Tile<D, KV>::NW; ++w) {
+        const uint32_t off = 128 * w;
+        t.k[0][w] = ld_stream(ks + o.o0 + off);
+        if constexpr (KV::kRows == 2) t.k[1][w] = ld_stream(ks + o.o1 + off);
+        t.v[0][w] = ld_stream(vs + o.o0 + off);
+        if constexpr (KV::kRows == 2) t.v[1][w] = ld_stream(vs + o.o1 + off);
+    }
 }
 
 template <int D, int G>
@@ -197,7 +206,7 @@ __device__ __forceinline__ void consume_tile(const Tile<D, KV>& t, const u32x4 (
                                              State<D, G>& st, float c, int r, int valid) {
     constexpr int NPC = D / 64;
     constexpr int R = KV::kRows;
-    constexpr int NW = NPC * Tile<D, KV>::QW;    // 16-byte words per row and lane
+    constexpr int NW = Tile<D, KV>::NW;          // 16-byte words per row and lane
     float s[R][G];
 #pragma unroll
     for (int j = 0; j < R; ++j) {
@@ -316,8 +325,9 @@ struct WaveItem {
 // One window of up to 64 of this wave's pages: i = wb .. wb + n - 1 of the
 // wave's page list (item page w + 8 i), walked tile by tile (a tile is a
 // page, or half of one for an fp32 cache).  Loads run ahead of the tile being
-// consumed; past the end the prefetch re-reads the last full tile (a cache
-// hit) so that every iteration issues the same loads and the wait counts the
+// consumed; past the end the look-ahead reads a small workspace region that
+// every wave shares (it stays in L2, and its values are never used), so
+// that every iteration issues the same loads and the wait counts the
 // compiler derives stay exact.  btv holds the window's validated page ids.
 template <int D, int G, typename KV>
 __device__ __forceinline__ void run_window(const DecodeParams& P, const u32x4 (&qv)[G][D / 64],
@@ -348,15 +358,21 @@ __device__ __forceinline__ void run_window(const DecodeParams& P, const u32x4 (&
     const int nf = vlast < kPageSize ? n - 1 : n;               // full pages in the window
     const int nt = nf * TPP;                                    // their tiles
     const LaneOff full = lane_offsets<D, KV>(r, p, kTileRows);
+    static_assert(kTileBytes <= (uint64_t)kSinkBytes, "the look-ahead sink must hold a tile");
     auto issue = [&](Tile<D, KV>& T, int ii) {
         int unused;
-        const int ti = ii < nt ? ii : nt - 1;
-        const uint64_t so = page_of(ti / TPP, unused) + (uint64_t)(ti % TPP) * kTileBytes;
+        const char* ks = P.sink;
+        const char* vs = P.sink;
+        if (ii < nt) {
+            const uint64_t so = page_of(ii / TPP, unused) + (uint64_t)(ii % TPP) * kTileBytes;
+            ks = kbase + so;
+            vs = vbase + so;
+        }
         LaneOff o = full;
         // Keep the lane offset a 32-bit VGPR inside the loop so the loads use
         // the scalar-base + 32-bit-offset form (no 64-bit per-lane address math).
         __asm__ volatile("" : "+v"(o.o0), "+v"(o.o1));
-        load_tile<D, KV>(T, kbase + so, vbase + so, o);
+        load_tile<D, KV>(T, ks, vs, o);
     };
     // The loop is rotated so that every iteration first consumes a tile and
     // then refills the registers it just freed: no instruction at the loop
@@ -574,21 +590,38 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, const ItemRe
     const int first_page = (int)(tb / kPageSize);
     const int nw = n_pages > w ? (n_pages - w + kWaves - 1) / kWaves : 0;
 
+    // q as packed bf16, in the dims this lane's cache words hold: qv[g][k]
+    // pairs with word k (bf16) or words 2k, 2k + 1 (fp32, two halves)
     u32x4 qv[G][NPC];
     const uint16_t* qrow = P.q + ((size_t)b * P.hq + (size_t)hk * G) * D;
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int k = 0; k < NPC; ++k) {
-            const uint16_t* src = qrow + g * D + (8 * k + p) * 8;
-            if (P.coherent_in) {            // the host may rewrite q between steps
-                const uint64_t* s64 = reinterpret_cast<const uint64_t*>(src);
-                const uint64_t lo = __hip_atomic_load(s64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-                const uint64_t hi = __hip_atomic_load(s64 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-                qv[g][k] = u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+            const uint16_t* lo_src;
+            const uint16_t* hi_src;
+            if constexpr (KV::kBytes == 2) {
+                lo_src = qrow + g * D + word_dim<KV>(p, k, 0);
+                hi_src = lo_src + 4;
             } else {
-                qv[g][k] = *reinterpret_cast<const u32x4*>(src);
+                lo_src = qrow + g * D + word_dim<KV>(p, 2 * k, 0);
+                hi_src = qrow + g * D + word_dim<KV>(p, 2 * k + 1, 0);
             }
+            const uint64_t* l64 = reinterpret_cast<const uint64_t*>(lo_src);
+            const uint64_t* h64 = reinterpret_cast<const uint64_t*>(hi_src);
+            uint64_t lo, hi;
+            if (P.coherent_in) {            // the host may rewrite q between steps
+                lo = __hip_atomic_load(l64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                hi = __hip_atomic_load(h64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            } else if constexpr (KV::kBytes == 2) {
+                const u32x4 x = *reinterpret_cast<const u32x4*>(lo_src);
+                lo = (uint64_t)x.x | ((uint64_t)x.y << 32);
+                hi = (uint64_t)x.z | ((uint64_t)x.w << 32);
+            } else {
+                lo = *l64;
+                hi = *h64;
+            }
+            qv[g][k] = u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
         }
 
     State<D, G> st;
@@ -647,12 +680,14 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, const ItemRe
         st.l[g] = l;
     }
     if (r == 0) {
+        constexpr int DPW = KV::kDimsPerWord;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
 #pragma unroll
-            for (int k = 0; k < NPC; ++k)
+            for (int ww = 0; ww < Tile<D, KV>::NW; ++ww)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) sm.acc[w][g * D + (8 * k + p) * 8 + e] = st.acc[g][k * 8 + e];
+                for (int e = 0; e < DPW; ++e)
+                    sm.acc[w][g * D + word_dim<KV>(p, ww, e)] = st.acc[g][ww * DPW + e];
             if (p == 0) { sm.m[w][g] = st.m[g]; sm.l[w][g] = st.l[g]; }
         }
     }
@@ -1320,7 +1355,7 @@ __global__ __launch_bounds__(kBuildThreads) void build_queue_kernel(BuildParams 
 template <int D, typename KV>
 __global__ __launch_bounds__(64) void debug_gather_kernel(DecodeParams P, int item_index,
                                                           char* k_out, char* v_out) {
-    constexpr int TPP = KV::kTilesPerPage, kTileRows = kPageSize / TPP, QW = Tile<D, KV>::QW;
+    constexpr int TPP = KV::kTilesPerPage, kTileRows = kPageSize / TPP;
     constexpr size_t kRowBytes = (size_t)D * KV::kBytes;
     const int lane = threadIdx.x;
     const int r = lane >> 3, p = lane & 7;
@@ -1351,13 +1386,11 @@ __global__ __launch_bounds__(64) void debug_gather_kernel(DecodeParams P, int it
                 if (tok >= vh) continue;
                 const size_t row = (size_t)(j * kPageSize + h * kTileRows + tok) * kRowBytes;
 #pragma unroll
-                for (int k = 0; k < Tile<D, KV>::NPC; ++k)
-#pragma unroll
-                    for (int q = 0; q < QW; ++q) {
-                        const size_t off = row + (size_t)(8 * k + p) * 8 * KV::kBytes + 16 * q;
-                        *reinterpret_cast<u32x4*>(k_out + off) = t.k[jj][k * QW + q];
-                        *reinterpret_cast<u32x4*>(v_out + off) = t.v[jj][k * QW + q];
-                    }
+                for (int w = 0; w < Tile<D, KV>::NW; ++w) {
+                    const size_t off = row + 128 * w + 16 * p;
+                    *reinterpret_cast<u32x4*>(k_out + off) = t.k[jj][w];
+                    *reinterpret_cast<u32x4*>(v_out + off) = t.v[jj][w];
+                }
             }
         }
     }

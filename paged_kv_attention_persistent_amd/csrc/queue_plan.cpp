@@ -138,6 +138,8 @@ void compute_layout(const Resolved& r, pkv_layout* lay) {
     if (r.persistent) off = align256(off + sizeof(LoopGlobal) + 2ull * loop_counter_bytes(r));
     lay->loop_mirror_off = off;
     if (r.persistent) off = align256(off + 2ull * loop_slot_bytes(r, *lay));
+    lay->sink_off = off;
+    off = align256(off + kSinkBytes);
     lay->total_bytes = off;
     lay->max_items = r.max_items;
 }

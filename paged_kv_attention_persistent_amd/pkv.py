@@ -88,7 +88,8 @@ class pkv_layout(C.Structure):
                 ("merge_rows_off", C.c_uint64), ("items_off", C.c_uint64),
                 ("partial_o_off", C.c_uint64), ("partial_lse_off", C.c_uint64),
                 ("arrive_off", C.c_uint64), ("loop_off", C.c_uint64),
-                ("loop_mirror_off", C.c_uint64), ("total_bytes", C.c_uint64),
+                ("loop_mirror_off", C.c_uint64), ("sink_off", C.c_uint64),
+                ("total_bytes", C.c_uint64),
                 ("max_items", C.c_int32),
                 ("reserved", C.c_int32)]
 
