@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--order", default="canonical", choices=["canonical", "lpt"])
     ap.add_argument("--wg-per-cu", type=int, default=0)
     ap.add_argument("--merge", default="fused", choices=["fused", "separate"])
+    ap.add_argument("--schedule", default="atomic", choices=["atomic", "static", "pages"],
+                    help="item assignment of the one-shot launches (pages: split rows' pages "
+                         "claimed from a shared cursor)")
     ap.add_argument("--copies", type=int, default=2)
     ap.add_argument("--no-gate", action="store_true")
     ap.add_argument("--loop-steps", type=int, default=200,
@@ -497,18 +500,24 @@ def measure_bucketed(torch, pkv, workloads, name, steps, warmup, say):
 
 
 def ablations(torch, pkv, workloads, args, say):
-    """Scheduling ablations (static vs atomic item assignment; exact-length
-    bucketed launches vs the compact queue) on the one-shot workloads."""
+    """Scheduling ablations (static vs atomic item assignment vs page claims;
+    exact-length bucketed launches vs the compact queue) on the one-shot
+    workloads, with both cache types for the assignment."""
     res = {"schedule": {}, "bucketed": {}}
     steps = max(args.steps // 2, 10)
-    for name in ("long", "mixed", "short"):
-        row = {}
-        for label, sched in (("atomic", pkv.PKV_SCHEDULE_ATOMIC), ("static", pkv.PKV_SCHEDULE_STATIC)):
-            r, _ = measure(torch, pkv, workloads, name, steps, args.warmup, args.order, args.wg_per_cu,
-                           args.copies, not args.no_gate, say, args.merge, sched)
-            row[label] = {"gbs": round(r["gbs"], 1), "decode_us": round(r["decode_ms_mean"] * 1e3, 2)}
-        res["schedule"][name] = row
-        say(f"ablation {name}: atomic {row['atomic']['gbs']} GB/s, static {row['static']['gbs']} GB/s")
+    for kv in ("bf16", "f32"):
+        for name in ("long", "mixed", "short"):
+            row = {}
+            for label, sched in (("atomic", pkv.PKV_SCHEDULE_ATOMIC), ("static", pkv.PKV_SCHEDULE_STATIC),
+                                 ("pages", pkv.PKV_SCHEDULE_PAGES)):
+                r, _ = measure(torch, pkv, workloads, name, steps, args.warmup, args.order, args.wg_per_cu,
+                               args.copies, not args.no_gate, say, args.merge, sched, kv=kv)
+                row[label] = {"gbs": round(r["gbs"], 1), "decode_gbs": round(r["decode_gbs"], 1),
+                              "decode_us": round(r["decode_ms_mean"] * 1e3, 2)}
+            key = name if kv == "bf16" else f"{name}_f32"
+            res["schedule"][key] = row
+            say(f"ablation {key}: atomic {row['atomic']['gbs']} GB/s, static {row['static']['gbs']} GB/s, "
+                f"page claims {row['pages']['gbs']} GB/s")
     for name in ("mixed", "short"):
         r, _ = measure(torch, pkv, workloads, name, steps, args.warmup, args.order, args.wg_per_cu,
                        args.copies, False, say, args.merge)
@@ -575,6 +584,8 @@ def profile_pass(torch, pkv, workloads, args, say):
     cfg = pkv.make_config(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages, wl.batch,
                           wl.max_pages_per_seq, scale=wl.scale,
                           kv_dtype=pkv.PKV_KV_F32 if args.kv == "f32" else pkv.PKV_KV_BF16,
+                          schedule={"atomic": pkv.PKV_SCHEDULE_ATOMIC, "static": pkv.PKV_SCHEDULE_STATIC,
+                                    "pages": pkv.PKV_SCHEDULE_PAGES}[args.schedule],
                           merge_mode=pkv.PKV_MERGE_SEPARATE if args.merge == "separate" else pkv.PKV_MERGE_FUSED)
     dec = pkv.PagedDecoder(cfg)
     info = dec.build_queue(wl.ctx_lens)
@@ -615,15 +626,17 @@ def main():
     if args.profile_pass:
         profile_pass(torch, pkv, workloads, args, say)
         return
+    sched = {"atomic": pkv.PKV_SCHEDULE_ATOMIC, "static": pkv.PKV_SCHEDULE_STATIC,
+             "pages": pkv.PKV_SCHEDULE_PAGES}[args.schedule]
     main_res, wl = measure(torch, pkv, workloads, args.workload, args.steps, args.warmup,
                            args.order, args.wg_per_cu, args.copies, not args.no_gate, say, args.merge,
-                           kv=args.kv)
+                           sched, kv=args.kv)
     say(f"{args.workload}: {main_res['gbs']:.1f} GB/s per step, decode kernel "
         f"{main_res['decode_gbs']:.1f} GB/s ({main_res['decode_ms_mean'] * 1e3:.1f} us)")
     others = {}
     for name in [x for x in args.others.split(",") if x and x != args.workload]:
         r, _ = measure(torch, pkv, workloads, name, max(args.steps // 2, 10), args.warmup,
-                       args.order, args.wg_per_cu, args.copies, not args.no_gate, say, args.merge)
+                       args.order, args.wg_per_cu, args.copies, not args.no_gate, say, args.merge, sched)
         others[name] = {k: r[k] for k in ("gbs", "decode_gbs", "ms_per_step", "decode_ms_mean",
                                           "items", "split", "chunk_tokens", "kv_bytes",
                                           "launches_per_step")}
@@ -636,7 +649,7 @@ def main():
                 continue
             r, _ = measure(torch, pkv, workloads, name, max(args.steps // 2, 10), args.warmup,
                            args.order, args.wg_per_cu, args.copies, not args.no_gate, say, args.merge,
-                           kv="f32")
+                           sched, kv="f32")
             f32[name] = {k: r[k] for k in ("gbs", "decode_gbs", "ms_per_step", "decode_ms_mean",
                                            "items", "chunk_tokens", "kv_bytes")}
             f32[name]["pct_of_hbm_peak"] = 100.0 * r["gbs"] / HBM_PEAK_GBS
@@ -680,7 +693,8 @@ def main():
                    "kv_chunk_tokens": main_res["chunk_tokens"], "items": main_res["items"],
                    "launches_per_step": main_res["launches_per_step"],
                    "kv_bytes_per_step": main_res["kv_bytes"], "grid": main_res["grid"],
-                   "order": args.order, "merge": args.merge, "kv_dtype": args.kv}
+                   "order": args.order, "merge": args.merge, "schedule": args.schedule,
+                   "kv_dtype": args.kv}
                   if args.workload == "long" else
                   {"workload": args.workload, "items": main_res["items"], "kv_dtype": args.kv,
                    "kv_bytes_per_step": main_res["kv_bytes"]},

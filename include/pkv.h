@@ -90,9 +90,15 @@ enum { PKV_ORDER_CANONICAL = 0, PKV_ORDER_LPT = 1 };
  * further items with an atomic counter as it finishes.  STATIC: the WPK note's
  * compiled schedule -- workgroup g runs items g, g + grid, g + 2 grid, ...
  * with no claims.  Every item is computed the same way in both, so outputs
- * are identical; only the time differs (a scheduling ablation).  The resident
- * loop always claims. */
-enum { PKV_SCHEDULE_ATOMIC = 0, PKV_SCHEDULE_STATIC = 1 };
+ * are identical; only the time differs (a scheduling ablation).  PAGES: items
+ * are claimed as in ATOMIC, but the workgroups of a split (row, KV head) no
+ * longer read fixed token ranges: their waves claim groups of pages (6 tiles,
+ * 48 KiB of K+V at D = 128) from a cursor shared by the row's items, so
+ * faster workgroups take more of the row; each item still yields one partial
+ * state and the merge is the same exact merge (over disjoint page sets).
+ * Outputs agree with the other schedules to rounding, not bit for bit.  The
+ * resident loop always claims items (ATOMIC). */
+enum { PKV_SCHEDULE_ATOMIC = 0, PKV_SCHEDULE_STATIC = 1, PKV_SCHEDULE_PAGES = 2 };
 
 /* Element type of the KV cache.  BF16: 2-byte values.  F32: 4-byte values,
  * as in the fp32 attention cache of the text-to-speech model on the WPK note
@@ -203,12 +209,15 @@ typedef struct pkv_layout {
                                    chunk_tokens, batch */
     uint64_t n_chunks_off;      /* int32 [max_batch] */
     uint64_t part_off_off;      /* int32 [max_batch + 1] */
+    uint64_t row_len_off;       /* int32 [max_batch]: each row's length in tokens */
     uint64_t merge_rows_off;    /* int32 [max_batch] */
     uint64_t items_off;         /* 16-byte items [max_items]: u32 seq, u16 kv_head,
                                    u16 chunk, u32 tok_begin, u32 tok_end */
     uint64_t partial_o_off;     /* fp32 [layers][max_items][G][D], normalised partial outputs */
     uint64_t partial_lse_off;   /* fp32 [layers][max_items][G], natural-log partial LSE */
     uint64_t arrive_off;        /* uint32 [layers][max_batch][Hkv] arrival counters of the fused merge */
+    uint64_t cursor_off;        /* PKV_SCHEDULE_PAGES: uint32 page cursors, one 128-byte line per
+                                   (row, KV head); empty otherwise */
     uint64_t loop_off;          /* resident loop: control mirror and two slots of step counters */
     uint64_t loop_mirror_off;   /* resident loop: device copies of the two host queue slots */
     uint64_t sink_off;          /* 4 KiB read by the gather's look-ahead past the end of a

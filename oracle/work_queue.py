@@ -110,6 +110,9 @@ def build_queue(ctx_lens, num_kv_heads: int, num_cus: int, chunk_tokens: int,
       n_chunks   int32 [B]
       part_off   int32 [B + 1]
       merge_rows int32 list of rows needing the merge/finalize pass
+      row_len    int32 [B], each row's length in tokens (the input, carried
+                 with the queue so a schedule that shares a row's pages
+                 among its items knows where the row ends)
     """
     lens = [int(x) for x in ctx_lens]
     for L in lens:
@@ -157,7 +160,8 @@ def build_queue(ctx_lens, num_kv_heads: int, num_cus: int, chunk_tokens: int,
 
     merge_rows = np.array([b for b in range(bsz) if n_chunks[b] != 1], dtype=np.int32)
     return {"split": split, "items": items, "n_chunks": n_chunks,
-            "part_off": part_off, "merge_rows": merge_rows, "chunk_tokens": chunk_tokens}
+            "part_off": part_off, "merge_rows": merge_rows, "chunk_tokens": chunk_tokens,
+            "row_len": np.asarray(lens, dtype=np.int32).reshape(-1)}
 
 
 def partial_slot(item, part_off, num_kv_heads: int) -> int:

@@ -91,6 +91,9 @@ DecodeParams make_params(const pkv_handle* h, const pkv_tensors* t) {
     p.items = reinterpret_cast<const Item*>(h->ws + h->lay.items_off);
     p.partial_o = reinterpret_cast<float*>(h->ws + h->lay.partial_o_off);
     p.sink = reinterpret_cast<const char*>(h->ws + h->lay.sink_off);
+    p.row_len = reinterpret_cast<const int32_t*>(h->ws + h->lay.row_len_off);
+    p.cursors = h->r.schedule == PKV_SCHEDULE_PAGES ? reinterpret_cast<uint32_t*>(h->ws + h->lay.cursor_off)
+                                                     : nullptr;
     p.partial_lse = reinterpret_cast<float*>(h->ws + h->lay.partial_lse_off);
     p.arrive = reinterpret_cast<uint32_t*>(h->ws + h->lay.arrive_off);
     p.trace = h->trace;
@@ -355,6 +358,8 @@ PKV_API pkv_status pkv_create(const pkv_config* cfg, void* workspace, size_t wor
                               h->r.max_batch * h->r.hkv * h->r.num_layers, h->stream);
     if (rc == 0 && h->r.persistent)
         rc = launch_zero(h->ws + h->lay.loop_off, sizeof(LoopGlobal) + 2 * loop_counter_bytes(h->r), h->stream);
+    if (rc == 0 && h->r.schedule == PKV_SCHEDULE_PAGES)     // cursors start at zero; the merge re-arms them
+        rc = launch_zero(h->ws + h->lay.cursor_off, 4ull * kCursorStride * h->r.max_batch * h->r.hkv, h->stream);
     if (rc != 0) { pkv_destroy(h); return PKV_ERR_HIP; }
     // an empty queue until the first build
     QHdr* qh = reinterpret_cast<QHdr*>(h->staging[0]);
@@ -387,7 +392,8 @@ PKV_API pkv_status pkv_build_queue(pkv_handle* h, const int32_t* ctx_lens_host, 
                                   reinterpret_cast<int32_t*>(st + (h->lay.n_chunks_off - q0)),
                                   reinterpret_cast<int32_t*>(st + (h->lay.part_off_off - q0)),
                                   reinterpret_cast<int32_t*>(st + (h->lay.merge_rows_off - q0)),
-                                  reinterpret_cast<Item*>(st + (h->lay.items_off - q0)), h->r.max_items, &qi, &why);
+                                  reinterpret_cast<Item*>(st + (h->lay.items_off - q0)), h->r.max_items, &qi, &why,
+                                  reinterpret_cast<int32_t*>(st + (h->lay.row_len_off - q0)));
         if (s != PKV_OK) return fail(h, s, why);
         qi.launches_per_step = 0;             // nothing is launched per step
         h->lens.assign(ctx_lens_host, ctx_lens_host + batch);
@@ -413,8 +419,9 @@ PKV_API pkv_status pkv_build_queue(pkv_handle* h, const int32_t* ctx_lens_host, 
     Item* items = reinterpret_cast<Item*>(st + (h->lay.items_off - q0));
     pkv_queue_info qi;
     const char* why;
+    int32_t* row_len = reinterpret_cast<int32_t*>(st + (h->lay.row_len_off - q0));
     pkv_status s = plan_queue(h->r, ctx_lens_host, batch, qh, n_chunks, part_off, merge_rows, items,
-                              h->r.max_items, &qi, &why);
+                              h->r.max_items, &qi, &why, row_len);
     if (s != PKV_OK) return fail(h, s, why);
     const size_t bytes = (h->lay.items_off - q0) + 16ull * qi.n_items;
     if ((e = hipMemcpyAsync(h->ws + q0, st, bytes, hipMemcpyHostToDevice, h->stream)) != hipSuccess)
@@ -446,6 +453,7 @@ PKV_API pkv_status pkv_build_queue_device(pkv_handle* h, const int32_t* ctx_lens
     p.qhdr = reinterpret_cast<QHdr*>(h->ws + h->lay.queue_off);
     p.n_chunks = reinterpret_cast<int32_t*>(h->ws + h->lay.n_chunks_off);
     p.part_off = reinterpret_cast<int32_t*>(h->ws + h->lay.part_off_off);
+    p.row_len = reinterpret_cast<int32_t*>(h->ws + h->lay.row_len_off);
     p.merge_rows = reinterpret_cast<int32_t*>(h->ws + h->lay.merge_rows_off);
     p.items = reinterpret_cast<Item*>(h->ws + h->lay.items_off);
     p.ctrl = reinterpret_cast<Ctrl*>(h->ws + h->lay.ctrl_off);

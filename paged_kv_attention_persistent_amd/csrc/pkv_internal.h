@@ -14,6 +14,7 @@ constexpr int kPageSize = 16;          // tokens per page (the only size built)
 constexpr int kThreads = 512;          // 8 waves of 64 lanes per workgroup
 constexpr int kWaves = kThreads / 64;
 constexpr int kFitMinPages = 64;       // chunk mode "fit": ranges of at least 64 pages
+constexpr int kCursorStride = 32;      // u32 words between page cursors (one 128-byte line each)
 constexpr int kSinkBytes = 4096;       // >= the largest tile (16 rows x 128 bf16, 8 rows x 128 fp32)
 
 // One queue item: a non-empty token range [tok_begin, tok_end) of one
@@ -133,7 +134,8 @@ uint64_t loop_grant_bytes(const Resolved& r);      // append page grants in a sl
 // and items into the caller's arrays.  Returns PKV_OK or an error.
 pkv_status plan_queue(const Resolved& r, const int32_t* ctx_lens, int32_t batch, QHdr* qh,
                       int32_t* n_chunks, int32_t* part_off, int32_t* merge_rows, Item* items,
-                      int32_t items_cap, pkv_queue_info* info, const char** why);
+                      int32_t items_cap, pkv_queue_info* info, const char** why,
+                      int32_t* row_len = nullptr);
 
 // Kernel parameters (passed by value).
 struct DecodeParams {
@@ -171,6 +173,9 @@ struct DecodeParams {
     int32_t static_sched;       // 1: workgroup g runs items g, g + grid, ... (no claims)
     float scale_log2;           // scale * log2(e)
     const char* sink;           // kSinkBytes the look-ahead reads past a window's end
+    const int32_t* row_len;     // [batch] tokens per row (the queue's copy of ctx_lens)
+    uint32_t* cursors;          // page-claim schedule: [max_batch][Hkv] cursors, kCursorStride apart
+                                // (null: split items read their own token range)
 };
 
 // Resident-loop kernel parameters: the per-step constant part of the decode
@@ -200,6 +205,7 @@ struct BuildParams {
     QHdr* qhdr;
     int32_t* n_chunks;
     int32_t* part_off;
+    int32_t* row_len;
     int32_t* merge_rows;
     Item* items;
     Ctrl* ctrl;

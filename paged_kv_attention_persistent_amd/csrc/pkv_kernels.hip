@@ -426,6 +426,139 @@ __device__ __forceinline__ void run_window(const DecodeParams& P, const u32x4 (&
     }
 }
 
+// Page-claim schedule for a split (row, KV head): the waves of every item of
+// the row claim groups of TPG tiles (PG pages) from a cursor the row's items
+// share, so a workgroup on a faster XCD takes more of the row; each wave keeps
+// its own online-softmax state over the pages it claimed, and the item's
+// partial state covers the pages its waves claimed (disjoint sets, merged
+// exactly like ranges).  Claim value 0 is the row's last group when that group
+// is short or ends in a partial page (handled first, masked and unpipelined,
+// by whichever wave draws it); every other value v names full group
+// v - has_tail, whose pages are all full.  The full groups run through the
+// three-tile pipeline without a drain between groups: a wave claims the group
+// after next at the top of each group and loads the next group's page ids
+// there, so both are back before their first use and every wait in the loop
+// is for a tile that is consumed next.  When the claims run out the
+// look-ahead reads the sink.
+template <int D, int G, typename KV>
+__device__ __forceinline__ void run_claimed(const DecodeParams& P, const u32x4 (&qv)[G][D / 64],
+                                            State<D, G>& st, uint32_t* cursor, const int32_t* bt0,
+                                            uint32_t len, int hk, int lane, int r, int p) {
+    constexpr int TPP = KV::kTilesPerPage;
+    constexpr int TPG = 6;
+    constexpr int PG = TPG / TPP;
+    constexpr int kTileRows = kPageSize / TPP;
+    constexpr uint64_t kSlabBytes = (uint64_t)kPageSize * D * KV::kBytes;
+    constexpr uint64_t kTileBytes = kSlabBytes / TPP;
+    static_assert(PG * TPP == TPG && PG <= 64 && TPG % 3 == 0 && TPG >= 6, "whole pages per group");
+    static_assert(kTileBytes <= (uint64_t)kSinkBytes, "the look-ahead sink must hold a tile");
+    const char* kbase = reinterpret_cast<const char*>(P.k_pool);
+    const char* vbase = reinterpret_cast<const char*>(P.v_pool);
+    const uint64_t head_off = (uint64_t)hk * kSlabBytes;
+    const uint64_t page_stride = (uint64_t)P.hkv * kSlabBytes;
+    const float c = P.scale_log2;
+    const int n_row = (int)((len + kPageSize - 1) / kPageSize);
+    const int gf = (int)(len / kPageSize) / PG;           // groups made of full pages only
+    const uint32_t has_tail = gf * PG < n_row ? 1u : 0u;  // the rest: short, or a partial last page
+
+    auto claim = [&]() -> uint32_t {
+        uint32_t v = 0;
+        if (lane == 0) {
+            // a lane-private copy of the address keeps this a one-lane atomic
+            __attribute__((address_space(1))) uint32_t* cp = (__attribute__((address_space(1))) uint32_t*)cursor;
+            __asm__ volatile("" : "+v"(cp));
+            v = __hip_atomic_fetch_add(cp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        return v;
+    };
+    auto full_group = [&](uint32_t v) -> int {           // -1: the tail, or nothing left
+        const uint32_t g = v - has_tail;
+        return (has_tail && v == 0u) || g >= (uint32_t)gf ? -1 : (int)g;
+    };
+    // page ids of cnt pages from row page p0 (lanes 0 .. cnt - 1); entries
+    // outside the pool are reported and replaced by page 0
+    auto load_ids = [&](int p0, int cnt) -> int32_t {
+        int32_t v = 0;
+        if (lane < cnt) v = bt0[p0 + lane];
+        return v;
+    };
+    auto check_ids = [&](int32_t v, int cnt) -> int32_t {
+        const bool bad = lane < cnt && (uint32_t)v >= (uint32_t)P.num_pages;
+        const unsigned long long m = __ballot(bad);
+        if (m) {
+            if (lane == __ffsll(m) - 1) report(P.ctrl, P.host_error, PKV_DEVERR_PAGE_OOB, (uint32_t)v);
+            v = bad ? 0 : v;
+        }
+        return v;
+    };
+    const LaneOff full = lane_offsets<D, KV>(r, p, kTileRows);
+    auto issue = [&](Tile<D, KV>& T, int32_t ids, int t, bool ok) {
+        const char* ks = P.sink;
+        const char* vs = P.sink;
+        if (ok) {
+            const int32_t pg = __builtin_amdgcn_readlane(ids, t / TPP);
+            const uint64_t so = (uint64_t)(uint32_t)pg * page_stride + head_off + (uint64_t)(t % TPP) * kTileBytes;
+            ks = kbase + so;
+            vs = vbase + so;
+        }
+        LaneOff o = full;
+        __asm__ volatile("" : "+v"(o.o0), "+v"(o.o1));
+        load_tile<D, KV>(T, ks, vs, o);
+    };
+
+    uint32_t v = (uint32_t)__builtin_amdgcn_readfirstlane((int)claim());
+    if (has_tail && v == 0u) {
+        const int p0 = gf * PG;
+        const int cnt = n_row - p0;                       // 1 .. PG pages
+        const int32_t ids = check_ids(load_ids(p0, cnt), cnt);
+        for (int j = 0; j < cnt; ++j) {
+            const int32_t pg = __builtin_amdgcn_readlane(ids, j);
+            for (int h = 0; h < TPP; ++h) {
+                const int vh = min((int)len - ((p0 + j) * kPageSize + h * kTileRows), kTileRows);
+                if (vh <= 0) break;
+                Tile<D, KV> T;
+                const uint64_t so = (uint64_t)(uint32_t)pg * page_stride + head_off + (uint64_t)h * kTileBytes;
+                load_tile<D, KV>(T, kbase + so, vbase + so, lane_offsets<D, KV>(r, p, vh));
+                consume_tile<D, G, KV, true>(T, qv, st, c, r, vh);
+            }
+        }
+        v = (uint32_t)__builtin_amdgcn_readfirstlane((int)claim());
+    }
+    int g = full_group(v);
+    if (g < 0) return;
+    int32_t ids = check_ids(load_ids(g * PG, PG), PG);
+    uint32_t cv = claim();                                // the group after this one
+    Tile<D, KV> A, B, C;
+    issue(A, ids, 0, true);
+    issue(B, ids, 1, true);
+    issue(C, ids, 2, true);
+    for (;;) {
+        const int gn = full_group((uint32_t)__builtin_amdgcn_readfirstlane((int)cv));
+        const int32_t ids_raw = load_ids((gn >= 0 ? gn : g) * PG, PG);
+        cv = claim();                                     // the group after next
+        const bool more = gn >= 0;
+        int32_t idn = 0;
+        // TPG / 3 rounds of the rotation; tile t + 3 is issued after tile t
+        // is consumed, from this group or (the last three) the next one
+#pragma unroll
+        for (int rnd = 0; rnd < TPG / 3; ++rnd) {
+            const int t = 3 * rnd;
+            consume_tile<D, G, KV, false>(A, qv, st, c, r, kTileRows);
+            if (rnd == TPG / 3 - 1) idn = check_ids(ids_raw, PG);
+            if (t + 3 < TPG) issue(A, ids, t + 3, true); else issue(A, idn, t + 3 - TPG, more);
+            consume_tile<D, G, KV, false>(B, qv, st, c, r, kTileRows);
+            if (t + 4 < TPG) issue(B, ids, t + 4, true); else issue(B, idn, t + 4 - TPG, more);
+            consume_tile<D, G, KV, false>(C, qv, st, c, r, kTileRows);
+            if (t + 5 < TPG) issue(C, ids, t + 5, true); else issue(C, idn, t + 5 - TPG, more);
+        }
+        if (!more) break;
+        g = gn;
+        ids = idn;
+    }
+    // the look-ahead of the last group (sink reads) and the spare claim
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 template <int D, int G>
 struct Smem {
     float acc[kWaves][G * D];
@@ -535,6 +668,7 @@ struct ItemRef {
     uint32_t idx;
     int b, hk, chunk;
     uint32_t tb, te;
+    uint32_t len;          // the row's length in tokens
     int nch, base;
     bool ok;
 };
@@ -552,16 +686,20 @@ __device__ __forceinline__ ItemRef read_item(const DecodeParams& P, uint32_t idx
             it.te <= (uint32_t)P.max_tokens && (it.tb % kPageSize) == 0;
     it.nch = 1;
     it.base = 0;
+    it.len = it.te;
     if (it.ok) {
-        // both row words in one round trip (part_off has batch + 1 entries)
+        // the row words in one round trip (part_off has batch + 1 entries)
         const int nch = P.n_chunks[it.b];
         const int base = P.part_off[it.b];
+        const int len = P.row_len[it.b];
         it.nch = __builtin_amdgcn_readfirstlane(nch);
         const int base_u = __builtin_amdgcn_readfirstlane(base);
+        it.len = (uint32_t)__builtin_amdgcn_readfirstlane(len);
         if (it.nch > 1) {
             it.base = base_u;
             const int slot = (it.base + it.chunk) * P.hkv + it.hk;
-            it.ok = it.chunk < it.nch && slot >= 0 && (it.base + it.nch) * P.hkv <= P.max_items;
+            it.ok = it.chunk < it.nch && slot >= 0 && (it.base + it.nch) * P.hkv <= P.max_items &&
+                    it.len >= it.te && it.len <= (uint32_t)P.max_tokens;
         } else {
             it.ok = it.nch == 1;
         }
@@ -635,22 +773,27 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, const ItemRe
 
     const WaveItem wi{tb, te, w, hk};
     const int32_t* bt_row = P.block_table + (size_t)b * P.bt_stride + first_page + w;
-    for (int wb = 0; wb < nw; wb += 64) {
-        const int n = nw - wb < 64 ? nw - wb : 64;
-        int32_t btv = 0;
-        if (lane < n) {
-            const int32_t* e = bt_row + (size_t)kWaves * (wb + lane);
-            btv = P.coherent_in ? (int32_t)__hip_atomic_load(reinterpret_cast<const uint32_t*>(e), __ATOMIC_RELAXED,
-                                                             __HIP_MEMORY_SCOPE_SYSTEM)
-                                : *e;
+    if (P.cursors && it.nch > 1) {                // page-claim schedule: the row's pages are shared
+        run_claimed<D, G, KV>(P, qv, st, P.cursors + ((size_t)b * P.hkv + hk) * kCursorStride,
+                              P.block_table + (size_t)b * P.bt_stride, it.len, hk, lane, r, p);
+    } else {
+        for (int wb = 0; wb < nw; wb += 64) {
+            const int n = nw - wb < 64 ? nw - wb : 64;
+            int32_t btv = 0;
+            if (lane < n) {
+                const int32_t* e = bt_row + (size_t)kWaves * (wb + lane);
+                btv = P.coherent_in ? (int32_t)__hip_atomic_load(reinterpret_cast<const uint32_t*>(e), __ATOMIC_RELAXED,
+                                                                 __HIP_MEMORY_SCOPE_SYSTEM)
+                                    : *e;
+            }
+            const bool badl = lane < n && (uint32_t)btv >= (uint32_t)P.num_pages;
+            const unsigned long long badm = __ballot(badl);
+            if (badm) {                                   // never read outside the pool
+                if (lane == __ffsll(badm) - 1) report(P.ctrl, P.host_error, PKV_DEVERR_PAGE_OOB, (uint32_t)btv);
+                btv = badl ? 0 : btv;
+            }
+            run_window<D, G, KV>(P, qv, st, btv, n, wb, wi, r, p);
         }
-        const bool badl = lane < n && (uint32_t)btv >= (uint32_t)P.num_pages;
-        const unsigned long long badm = __ballot(badl);
-        if (badm) {                                   // never read outside the pool
-            if (lane == __ffsll(badm) - 1) report(P.ctrl, P.host_error, PKV_DEVERR_PAGE_OOB, (uint32_t)btv);
-            btv = badl ? 0 : btv;
-        }
-        run_window<D, G, KV>(P, qv, st, btv, n, wb, wi, r, p);
     }
     // Claim the next item only now, near the end of this one: a claim made
     // earlier would hold an item this workgroup cannot start while another
@@ -713,9 +856,13 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, const ItemRe
             O0 = fmaf(sm.acc[ww][g * D + d], a, O0);
             O1 = fmaf(sm.acc[ww][g * D + d + 1], a, O1);
         }
-        O0 = O0 / L;
-        O1 = O1 / L;
-        const float lse = (M + log2f(L)) * kLn2;
+        // a state with no tokens (possible only under the page-claim
+        // schedule, for an item whose waves found the row's pages taken) is
+        // the neutral partial state
+        const bool any = L > 0.0f;
+        O0 = any ? O0 / L : 0.0f;
+        O1 = any ? O1 / L : 0.0f;
+        const float lse = any ? (M + log2f(L)) * kLn2 : -INFINITY;
         if (split) {
             float* po = P.partial_o + ((size_t)slot * G + g) * D + d;
             if (P.fused_merge) {
@@ -748,7 +895,12 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, const ItemRe
         __syncthreads();
         if (sm.last) {
             merge_row<D, G, kThreads, true>(P, b, hk, it.nch, it.base, tid);
-            if (tid == 0) atomicExch(&P.arrive[(size_t)b * P.hkv + hk], 0u);
+            if (tid == 0) {
+                atomicExch(&P.arrive[(size_t)b * P.hkv + hk], 0u);
+                // every item of the row has arrived, so no wave claims from
+                // its cursor any more: the next launch starts it at zero
+                if (P.cursors) atomicExch(P.cursors + ((size_t)b * P.hkv + hk) * kCursorStride, 0u);
+            }
         }
     }
 }
@@ -876,6 +1028,7 @@ __device__ __forceinline__ ItemRef read_item_mirror(const DecodeParams& P, uint3
             it.te <= (uint32_t)P.max_tokens && (it.tb % kPageSize) == 0;
     it.nch = 1;
     it.base = 0;
+    it.len = it.te;              // the loop reads each item's own range only
     if (it.ok) {
         const uint32_t nch = ld_agt(P.n_chunks + it.b), base = ld_agt(P.part_off + it.b);
         it.nch = __builtin_amdgcn_readfirstlane((int)nch);
@@ -1096,6 +1249,7 @@ __global__ __launch_bounds__(kThreads) void resident_kernel(LoopParams L) {
                 it.te = uni(s_it.te);
                 it.nch = (int)uni((uint32_t)s_it.nch);
                 it.base = (int)uni((uint32_t)s_it.base);
+                it.len = uni(s_it.len);
                 it.ok = uni(s_it.ok ? 1u : 0u) != 0u;
                 row = it.ok ? it.b : -1;
                 if (layer > 0 && it.ok) {            // the row's previous layer must be complete
@@ -1194,6 +1348,8 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
     const int nc = P.n_chunks[b];
     if (nc == 1 || (P.part_off[b] + nc) * P.hkv > P.max_items) return;
     merge_row<D, G, 256, false>(P, b, hk, nc, P.part_off[b], threadIdx.x);
+    // the decode kernel has finished: its page cursor starts the next launch at zero
+    if (P.cursors && threadIdx.x == 0) P.cursors[((size_t)b * P.hkv + hk) * kCursorStride] = 0u;
 }
 
 // Device queue builder: the same bytes as the host builder, from device
@@ -1300,6 +1456,7 @@ __global__ __launch_bounds__(kBuildThreads) void build_queue_kernel(BuildParams 
     for (int b = r0; b < r1; ++b) {
         const int nc = nchunks(P.ctx_lens[b]);
         P.n_chunks[b] = nc;
+        P.row_len[b] = P.ctx_lens[b];
         P.part_off[b] = o_parts;
         s_item0[b] = o_items;
         if (nc != 1) P.merge_rows[o_merge++] = b;

@@ -85,7 +85,8 @@ pkv_status resolve_config(const pkv_config* cfg, int device_cus, Resolved* r, co
     r->timeout_ms = cfg->timeout_ms == 0 ? 10000 : cfg->timeout_ms;
     if (r->timeout_ms < 1 || r->timeout_ms > 3600000) { *why = "timeout_ms must be 1..3600000"; return PKV_ERR_INVALID_ARG; }
     if (r->persistent && r->wg_per_cu != 1) { *why = "the resident loop runs one workgroup per CU"; return PKV_ERR_INVALID_ARG; }
-    if (cfg->schedule != PKV_SCHEDULE_ATOMIC && cfg->schedule != PKV_SCHEDULE_STATIC) {
+    if (cfg->schedule != PKV_SCHEDULE_ATOMIC && cfg->schedule != PKV_SCHEDULE_STATIC &&
+        cfg->schedule != PKV_SCHEDULE_PAGES) {
         *why = "unknown schedule"; return PKV_ERR_INVALID_ARG;
     }
     if (r->persistent && cfg->schedule != PKV_SCHEDULE_ATOMIC) { *why = "the resident loop claims items atomically"; return PKV_ERR_INVALID_ARG; }
@@ -123,6 +124,8 @@ void compute_layout(const Resolved& r, pkv_layout* lay) {
     off = align256(off + 4ull * r.max_batch);
     lay->part_off_off = off;
     off = align256(off + 4ull * (r.max_batch + 1));
+    lay->row_len_off = off;
+    off = align256(off + 4ull * r.max_batch);
     lay->merge_rows_off = off;
     off = align256(off + 4ull * r.max_batch);
     lay->items_off = off;
@@ -134,6 +137,8 @@ void compute_layout(const Resolved& r, pkv_layout* lay) {
     off = align256(off + 4ull * r.max_items * r.g * layers);
     lay->arrive_off = off;
     off = align256(off + 4ull * r.max_batch * r.hkv * layers);
+    lay->cursor_off = off;
+    if (r.schedule == PKV_SCHEDULE_PAGES) off = align256(off + 4ull * kCursorStride * r.max_batch * r.hkv);
     lay->loop_off = off;
     if (r.persistent) off = align256(off + sizeof(LoopGlobal) + 2ull * loop_counter_bytes(r));
     lay->loop_mirror_off = off;
@@ -174,7 +179,7 @@ int fit_chunk(const Resolved& r, const int32_t* ctx_lens, int batch, int64_t max
 
 pkv_status plan_queue(const Resolved& r, const int32_t* ctx_lens, int32_t batch, QHdr* qh,
                       int32_t* n_chunks, int32_t* part_off, int32_t* merge_rows, Item* items,
-                      int32_t items_cap, pkv_queue_info* info, const char** why) {
+                      int32_t items_cap, pkv_queue_info* info, const char** why, int32_t* row_len) {
     *why = "";
     if (batch < 0 || batch > r.max_batch) { *why = "batch outside [0, max_batch]"; return PKV_ERR_CAPACITY; }
     if (batch > 0 && !ctx_lens) { *why = "null ctx_lens"; return PKV_ERR_INVALID_ARG; }
@@ -200,6 +205,7 @@ pkv_status plan_queue(const Resolved& r, const int32_t* ctx_lens, int32_t batch,
         const int64_t L = ctx_lens[b];
         const int32_t nc = L == 0 ? 0 : (split ? (int32_t)((L + chunk - 1) / chunk) : 1);
         n_chunks[b] = nc;
+        if (row_len) row_len[b] = (int32_t)L;
         part_off[b + 1] = part_off[b] + (nc > 1 ? nc : 0);
         n_items += (int64_t)nc * r.hkv;
         if (nc > 1) ++n_split_rows;

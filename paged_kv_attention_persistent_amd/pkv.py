@@ -27,7 +27,7 @@ PKV_ERR_TIMEOUT = -7
 
 PKV_POLICY_AUTO, PKV_POLICY_NO_SPLIT, PKV_POLICY_SPLIT = 0, 1, 2
 PKV_ORDER_CANONICAL, PKV_ORDER_LPT = 0, 1
-PKV_SCHEDULE_ATOMIC, PKV_SCHEDULE_STATIC = 0, 1
+PKV_SCHEDULE_ATOMIC, PKV_SCHEDULE_STATIC, PKV_SCHEDULE_PAGES = 0, 1, 2
 PKV_MERGE_FUSED, PKV_MERGE_SEPARATE = 0, 1
 PKV_KV_BF16, PKV_KV_F32 = 0, 1
 PKV_DEVERR_NONE, PKV_DEVERR_PAGE_OOB, PKV_DEVERR_BAD_ITEM = 0, 1, 2
@@ -85,9 +85,10 @@ class pkv_runtime_info(C.Structure):
 class pkv_layout(C.Structure):
     _fields_ = [("ctrl_off", C.c_uint64), ("queue_off", C.c_uint64),
                 ("n_chunks_off", C.c_uint64), ("part_off_off", C.c_uint64),
+                ("row_len_off", C.c_uint64),
                 ("merge_rows_off", C.c_uint64), ("items_off", C.c_uint64),
                 ("partial_o_off", C.c_uint64), ("partial_lse_off", C.c_uint64),
-                ("arrive_off", C.c_uint64), ("loop_off", C.c_uint64),
+                ("arrive_off", C.c_uint64), ("cursor_off", C.c_uint64), ("loop_off", C.c_uint64),
                 ("loop_mirror_off", C.c_uint64), ("sink_off", C.c_uint64),
                 ("total_bytes", C.c_uint64),
                 ("max_items", C.c_int32),

@@ -136,8 +136,9 @@ def test_config_validation():
     bad = [dict(num_q_heads=30), dict(head_dim=96), dict(page_size=32), dict(kv_chunk_tokens=100),
            dict(kv_chunk_tokens=-16),
            dict(num_pages=0), dict(wg_per_cu=9), dict(policy=7), dict(num_q_heads=64),
-           dict(merge_mode=2), dict(schedule=2), dict(persistent=1, schedule=1), dict(append=2),
-           dict(append=1), dict(kv_dtype=2), dict(kv_dtype=-1)]
+           dict(merge_mode=2), dict(persistent=1, schedule=1), dict(append=2),
+           dict(append=1), dict(kv_dtype=2), dict(kv_dtype=-1),
+           dict(schedule=3), dict(persistent=1, schedule=2)]
     base = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, num_pages=100, max_batch=4,
                 max_pages_per_seq=10, num_cus=256)
     for b in bad:
@@ -154,6 +155,21 @@ def test_config_validation():
     with pytest.raises(pkv.PkvError):
         pkv.pkv_workspace_size(c)
     assert pkv.pkv_workspace_size(pkv.make_config(**dict(base, persistent=1, kv_dtype=1))) > 0
+
+
+def test_page_claim_layout():
+    # the page-claim schedule adds one 128-byte cursor per (row, KV head);
+    # the queue and the other regions are unchanged
+    kw = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, num_pages=100, max_batch=4,
+              max_pages_per_seq=10, num_cus=256)
+    a = pkv.pkv_workspace_layout(pkv.make_config(**kw))
+    b = pkv.pkv_workspace_layout(pkv.make_config(schedule=pkv.PKV_SCHEDULE_PAGES, **kw))
+    assert a.loop_off - a.cursor_off == 0
+    assert b.loop_off - b.cursor_off == 4 * 8 * 128
+    assert b.total_bytes - a.total_bytes == 4 * 8 * 128
+    for f in ("queue_off", "n_chunks_off", "part_off_off", "row_len_off", "merge_rows_off", "items_off"):
+        assert getattr(a, f) == getattr(b, f)
+    assert a.part_off_off < a.row_len_off < a.merge_rows_off < a.items_off
 
 
 def test_f32_cache_plan_and_layout():

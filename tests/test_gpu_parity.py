@@ -90,7 +90,9 @@ class Run:
         hdr = ws[lay.queue_off:lay.queue_off + 20].cpu().view(torch.int32).numpy()
         nm = int(hdr[1])
         mr = ws[lay.merge_rows_off:lay.merge_rows_off + 4 * nm].cpu().view(torch.int32).numpy()
-        return {"items": items, "n_chunks": nch, "part_off": po, "merge_rows": mr, "hdr": hdr}
+        rl = ws[lay.row_len_off:lay.row_len_off + 4 * B].cpu().view(torch.int32).numpy()
+        return {"items": items, "n_chunks": nch, "part_off": po, "merge_rows": mr, "hdr": hdr,
+                "row_len": rl}
 
     def close(self):
         self.dec.close()
@@ -149,15 +151,19 @@ def lse_tol(wl):
     return LSE_F32 if wl.kv_dtype == "f32" else MAX_ABS
 
 
+SCHEDULES = {"atomic": pkv.PKV_SCHEDULE_ATOMIC, "pages": pkv.PKV_SCHEDULE_PAGES}
+
+
+@pytest.mark.parametrize("sched", list(SCHEDULES))
 @pytest.mark.parametrize("kv", KVS)
 @pytest.mark.parametrize("merge", [pkv.PKV_MERGE_FUSED, pkv.PKV_MERGE_SEPARATE],
                          ids=["fused_merge", "separate_merge"])
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
-def test_small_cases_full_compare(case, merge, kv):
+def test_small_cases_full_compare(case, merge, kv, sched):
     name, lens, hq, hkv, d, policy, chunk = case
-    say("case", name, "merge", merge, "kv", kv)
+    say("case", name, "merge", merge, "kv", kv, "schedule", sched)
     wl = workloads.custom(name, lens, hq, hkv, d, spare_pages=5, kv_dtype=kv)
-    run = Run(wl, policy=policy, kv_chunk_tokens=chunk, merge_mode=merge)
+    run = Run(wl, policy=policy, kv_chunk_tokens=chunk, merge_mode=merge, schedule=SCHEDULES[sched])
     ro, rl = oracle_full(wl)
     for call in range(2):                 # second call: counters and head re-armed
         o, l = run.decode()
@@ -192,14 +198,15 @@ FULL = {"long": [(0, 0), (0, 5)], "mixed": [(b, (3 * b) % 8) for b in range(8)],
         "short": [(0, 0), (17, 3), (63, 7)]}
 
 
+@pytest.mark.parametrize("sched", list(SCHEDULES))
 @pytest.mark.parametrize("kv", KVS)
 @pytest.mark.parametrize("merge", [pkv.PKV_MERGE_FUSED, pkv.PKV_MERGE_SEPARATE],
                          ids=["fused_merge", "separate_merge"])
 @pytest.mark.parametrize("name", ["long", "mixed", "short"])
-def test_full_size_sampled_units(name, merge, kv):
-    say("full", name, "kv", kv)
+def test_full_size_sampled_units(name, merge, kv, sched):
+    say("full", name, "kv", kv, "schedule", sched)
     wl = workloads.CONFIGS[name]().with_kv_dtype(kv)
-    run = Run(wl, poison=True, merge_mode=merge)
+    run = Run(wl, poison=True, merge_mode=merge, schedule=SCHEDULES[sched])
     o, l = run.decode()
     info = run.info
     ref = wq.build_queue(wl.ctx_lens, wl.num_kv_heads, run.dec.query()["num_cus"], 0)
@@ -268,6 +275,7 @@ def test_queue_bytes_on_device_match_oracle(name):
         assert np.array_equal(got["n_chunks"], ref["n_chunks"])
         assert np.array_equal(got["part_off"], ref["part_off"])
         assert np.array_equal(got["merge_rows"], ref["merge_rows"])
+        assert np.array_equal(got["row_len"], ref["row_len"])
         assert list(got["hdr"]) == [len(ref["items"]), len(ref["merge_rows"]), int(ref["split"]),
                                     ref["chunk_tokens"], wl.batch]
     run.close()
@@ -306,6 +314,8 @@ def test_device_queue_random_lengths_match_oracle():
             assert items == ref["items"].tobytes(), where
             nch = ws[lay.n_chunks_off:lay.n_chunks_off + 4 * B].cpu().view(torch.int32).numpy()
             assert np.array_equal(nch, ref["n_chunks"]), where
+            rl = ws[lay.row_len_off:lay.row_len_off + 4 * B].cpu().view(torch.int32).numpy()
+            assert np.array_equal(rl, ref["row_len"]), where
         finally:
             dec.close()
 
@@ -457,3 +467,44 @@ def test_f32_cache_is_read_at_full_precision():
     say(f"oracle LSE gap between the fp32 cache and its bf16 rounding: {gap:.3e}")
     assert gap > 5 * LSE_F32
     run.close()
+
+
+@pytest.mark.parametrize("merge", [pkv.PKV_MERGE_FUSED, pkv.PKV_MERGE_SEPARATE],
+                         ids=["fused_merge", "separate_merge"])
+def test_page_claims_with_idle_items_and_repeats(merge):
+    """Page-claim schedule where most items of a row find its pages already
+    claimed (16-token ranges over short rows: far more waves than page
+    groups), so their partial states are empty, and repeated calls, each of
+    which must start every cursor at zero again."""
+    wl = workloads.custom("claims_idle", [200, 17, 0, 96, 1000], 8, 2, 128, spare_pages=3)
+    run = Run(wl, policy=pkv.PKV_POLICY_SPLIT, kv_chunk_tokens=16, merge_mode=merge,
+              schedule=pkv.PKV_SCHEDULE_PAGES)
+    ro, rl = oracle_full(wl)
+    for call in range(12):
+        run.out.fill_(float("nan"))
+        run.lse.fill_(float("nan"))
+        o, l = run.decode()
+        check(o, l, ro, rl, f"idle items call {call}")
+    lay = run.dec.layout
+    cur = run.dec.workspace[lay.cursor_off:lay.cursor_off + 4 * 32 * len(wl.ctx_lens) * 2]
+    assert int(cur.cpu().view(torch.int32).abs().sum()) == 0       # every cursor re-armed
+    run.close()
+
+
+@pytest.mark.parametrize("kv", KVS)
+def test_page_claims_split_equals_unsplit(kv):
+    # the claimed page sets differ from call to call; the merged result must
+    # not: each call against the unsplit decode of the same rows
+    wl = workloads.custom("claims_vs_unsplit", [20000, 5000, 3, 70000], 8, 2, 128, spare_pages=2,
+                          kv_dtype=kv)
+    a = Run(wl, policy=pkv.PKV_POLICY_SPLIT, kv_chunk_tokens=1024, schedule=pkv.PKV_SCHEDULE_PAGES)
+    b = Run(wl, policy=pkv.PKV_POLICY_NO_SPLIT)
+    ob, lb = b.decode()
+    ro, rl = oracle_full(wl)
+    check(ob, lb, ro, rl, f"unsplit {kv}", lse_tol(wl))
+    for call in range(5):
+        oa, la = a.decode()
+        check(oa, la, ro, rl, f"page claims {kv} call {call}", lse_tol(wl))
+        check(oa, la, ob, lb, f"page claims vs unsplit {kv} call {call}", lse_tol(wl))
+    a.close()
+    b.close()
