@@ -398,11 +398,22 @@ def density_search(torch, pkv, workloads, periods_ms, max_sessions, steps, runs,
     return res
 
 
+def kernel_code_digest(path):
+    """sha256 prefix of a HIP source with its comments and whitespace removed:
+    it changes when the code changes, not when a comment does."""
+    import hashlib
+    import re
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = re.sub(r"\s+", " ", text).strip()
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
+
+
 def measured_traffic(root, kv="bf16"):
     """HBM bytes per decode launch of the long context from the committed
-    counter summary, if it was taken on the kernel source as it is now (else
+    counter summary, if it was taken on the kernel code as it is now (else
     None)."""
-    import hashlib
     import re
     name = "decode_kernel_long_context" + ("_fp32_cache" if kv == "f32" else "") + "_traffic.md"
     prof = os.path.join(root, "profiles", name)
@@ -410,10 +421,10 @@ def measured_traffic(root, kv="bf16"):
     try:
         text = open(prof).read()
         rec = json.loads(re.search(r"```json\n(.*?)\n```", text, re.S).group(1))
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        digest = kernel_code_digest(src)
     except Exception:
         return None
-    if rec.get("source_sha256_prefix") != sha:
+    if rec.get("kernel_code_sha256_prefix") != digest:
         return None
     return int(rec["traffic_bytes_per_launch"])
 

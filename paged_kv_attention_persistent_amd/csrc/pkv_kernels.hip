@@ -30,8 +30,10 @@
 //     to rounding because the final normalisation divides by the same sum;
 //   * pages are software-pipelined two ahead in registers (three tiles), so
 //     each wave keeps up to 16 KB of K/V loads in flight;
-//   * at the end of an item the 8 groups of a wave combine by xor shuffles and
-//     the 8 waves combine through LDS.
+//   * at the end of an item the 8 groups of a wave combine by DPP and
+//     row-swap permutes and the 8 waves combine through LDS.
+// An fp32 cache runs the same kernels on half-page tiles (8 rows of 512 B at
+// D = 128), with fp32 FMAs in place of the bf16 dot products.
 #include <float.h>
 #include <hip/hip_runtime.h>
 

@@ -236,3 +236,19 @@ def test_f32_stream_rounds_to_bf16_stream():
     sl = wl.with_kv_dtype("f32").pool_slabs("v", wl.block_table[0, :3], 1)
     full = wl.with_kv_dtype("f32").pool("v", "cpu", poison=False)
     assert torch.equal(sl, full[torch.as_tensor(wl.block_table[0, :3].astype(np.int64)), 1])
+
+
+def test_traffic_record_follows_kernel_code_not_comments(tmp_path):
+    # bench.py reports the committed traffic counters only while the kernel
+    # code they were taken on is unchanged; comments and layout do not count
+    import bench
+    a = tmp_path / "a.hip"
+    a.write_text("// note\nint f(int x) {\n  return x + 1; /* one */\n}\n")
+    b = tmp_path / "b.hip"
+    b.write_text("int f(int x) { return x + 1; }  // another note\n")
+    c = tmp_path / "c.hip"
+    c.write_text("int f(int x) { return x + 2; }\n")
+    assert bench.kernel_code_digest(a) == bench.kernel_code_digest(b) != bench.kernel_code_digest(c)
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    assert bench.measured_traffic(root) is None or bench.measured_traffic(root) > 536870912
