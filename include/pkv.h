@@ -344,6 +344,15 @@ PKV_API pkv_status pkv_plan_queue(const pkv_config* cfg, const int32_t* ctx_lens
                                   void* items, int32_t items_cap, int32_t* n_chunks,
                                   int32_t* part_off, int32_t* merge_rows, pkv_queue_info* info);
 
+/* Test hook: copy the device queue as the decode kernel reads it -- the
+ * workspace bytes from pkv_layout.queue_off up to the end of its items
+ * (header, n_chunks, part_off, row_len, merge_rows at their layout offsets,
+ * then n_items 16-byte items) -- to host memory host_dst of capacity bytes.
+ * Waits for the handle's stream first.  *written receives the bytes copied
+ * (at most capacity).  One-shot handles only (the resident loop keeps its
+ * queue in host memory). */
+PKV_API pkv_status pkv_queue_read(pkv_handle* h, void* host_dst, size_t capacity, size_t* written);
+
 /* Test hook: write the K and V rows that the decode kernel's own gather
  * reads for queue item item_index, in token order, to device buffers k_out and
  * v_out ([tok_end - tok_begin][D] of the cache's element type, kv_dtype).

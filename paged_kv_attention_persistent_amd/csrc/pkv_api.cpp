@@ -620,6 +620,27 @@ PKV_API pkv_status pkv_clear_error(pkv_handle* h) {
     return PKV_OK;
 }
 
+PKV_API pkv_status pkv_queue_read(pkv_handle* h, void* host_dst, size_t capacity, size_t* written) {
+    if (!h || !written) return PKV_ERR_INVALID_ARG;
+    *written = 0;
+    if (h->r.persistent) return fail(h, PKV_ERR_STATE, "pkv_queue_read needs a one-shot handle");
+    if (capacity > 0 && !host_dst) return fail(h, PKV_ERR_INVALID_ARG, "null host_dst");
+    hipError_t e = hipStreamSynchronize(h->stream);
+    if (e != hipSuccess) return hip_fail(h, e, "stream sync");
+    QHdr qh;
+    e = hipMemcpy(&qh, h->ws + h->lay.queue_off, sizeof(qh), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(h, e, "queue header read");
+    if (qh.n_items < 0 || qh.n_items > h->r.max_items) return fail(h, PKV_ERR_DEVICE_FAULT, "queue header out of range");
+    const size_t total = (h->lay.items_off - h->lay.queue_off) + 16ull * (size_t)qh.n_items;
+    const size_t n = total < capacity ? total : capacity;
+    if (n > 0) {
+        e = hipMemcpy(host_dst, h->ws + h->lay.queue_off, n, hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_fail(h, e, "queue read");
+    }
+    *written = n;
+    return PKV_OK;
+}
+
 PKV_API pkv_status pkv_debug_gather(pkv_handle* h, const pkv_tensors* t, int32_t item_index,
                                     void* k_out, void* v_out, void* stream) {
     if (!h) return PKV_ERR_INVALID_ARG;

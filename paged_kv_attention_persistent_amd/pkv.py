@@ -117,6 +117,7 @@ SIGNATURES = {
                                    C.POINTER(pkv_queue_info)]),
     "pkv_debug_gather": (C.c_int32, [C.c_void_p, C.POINTER(pkv_tensors), C.c_int32,
                                      C.c_void_p, C.c_void_p, C.c_void_p]),
+    "pkv_queue_read": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_size_t, C.POINTER(C.c_size_t)]),
     "pkv_set_trace": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_int32]),
     "pkv_loop_set_free_pages": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_int32]),
     "pkv_loop_free_pages": (C.c_int32, [C.c_void_p, C.POINTER(C.c_int32)]),
@@ -303,6 +304,15 @@ def pkv_debug_gather(handle: int, tensors: pkv_tensors, item_index: int, k_out, 
                                   C.c_void_p(k_out.data_ptr()), C.c_void_p(v_out.data_ptr()),
                                   C.c_void_p(_stream_ptr(stream))),
            "pkv_debug_gather", C.c_void_p(handle))
+
+
+def pkv_queue_read(handle: int, capacity: int) -> bytes:
+    """The device queue as the decode kernel reads it (see pkv.h)."""
+    buf = C.create_string_buffer(int(capacity))
+    n = C.c_size_t(0)
+    _check(lib().pkv_queue_read(C.c_void_p(handle), buf, int(capacity), C.byref(n)), "pkv_queue_read",
+           C.c_void_p(handle))
+    return buf.raw[:n.value]
 
 
 def pkv_loop_set_free_pages(handle: int, pages) -> None:

@@ -278,6 +278,13 @@ def test_queue_bytes_on_device_match_oracle(name):
         assert np.array_equal(got["row_len"], ref["row_len"])
         assert list(got["hdr"]) == [len(ref["items"]), len(ref["merge_rows"]), int(ref["split"]),
                                     ref["chunk_tokens"], wl.batch]
+        # the C-ABI read of the same queue: the workspace bytes, header through items
+        lay = run.dec.layout
+        raw = pkv.pkv_queue_read(run.dec.handle, 1 << 26)
+        assert len(raw) == lay.items_off - lay.queue_off + 16 * len(ref["items"])
+        assert raw == run.dec.workspace[lay.queue_off:lay.queue_off + len(raw)].cpu().numpy().tobytes()
+        assert raw[lay.items_off - lay.queue_off:] == ref["items"].tobytes()
+        assert len(pkv.pkv_queue_read(run.dec.handle, 100)) == 100          # capped by capacity
     run.close()
 
 
@@ -508,3 +515,39 @@ def test_page_claims_split_equals_unsplit(kv):
         check(oa, la, ob, lb, f"page claims vs unsplit {kv} call {call}", lse_tol(wl))
     a.close()
     b.close()
+
+
+@pytest.mark.parametrize("sched", list(SCHEDULES))
+@pytest.mark.parametrize("kv", KVS)
+def test_structured_cases_count_every_token(kv, sched):
+    """Closed forms on the GPU, strong enough to see one token too many or too
+    few.  With q = 0 every score is 0, so LSE = ln L_b to fp32 rounding (a few
+    1e-7 relative) while a dropped or repeated token moves it by about 1 / L_b
+    (2e-4 at 5000 tokens); with V[t][0] = (t mod 256) / 256 and V[t][1] = 0.375
+    (both bf16-exact), O[.][0] is the mean of the first column to bf16 rounding
+    and O[.][1] is 0.375 exactly.  Split and unsplit rows, partial pages, a
+    one-token row and an empty row."""
+    lens = [5000, 17, 1, 3000, 0, 4097, 256]
+    wl = workloads.custom("structured", lens, 8, 2, 128, spare_pages=3, kv_dtype=kv)
+    v = wl.pool("v", "cpu", poison=True)
+    for b, L in enumerate(lens):
+        t = np.arange(L)
+        pg = torch.as_tensor(wl.block_table[b, t // 16].astype(np.int64))
+        row = torch.as_tensor(t % 16)
+        v[pg, :, row, 0] = torch.as_tensor((t % 256) / 256.0, dtype=torch.float32).to(v.dtype)[:, None]
+        v[pg, :, row, 1] = 0.375
+    for policy, chunk in ((pkv.PKV_POLICY_SPLIT, 1024), (pkv.PKV_POLICY_NO_SPLIT, 0)):
+        run = Run(wl, policy=policy, kv_chunk_tokens=chunk, schedule=SCHEDULES[sched])
+        run.q.zero_()
+        run.v = v.to("cuda")
+        o, l = run.decode()
+        for b, L in enumerate(lens):
+            if L == 0:
+                assert np.all(o[b] == 0) and np.all(np.isneginf(l[b]))
+                continue
+            where = f"{kv} {sched} policy {policy} row {b} (L = {L})"
+            assert np.abs(l[b] - np.log(L)).max() <= 5e-6, where
+            exact = np.mean((np.arange(L) % 256) / 256.0)
+            assert np.abs(o[b, :, 0] - exact).max() <= 2.0 ** -8 * exact + 1e-6, where
+            assert np.all(o[b, :, 1] == 0.375), where
+        run.close()
