@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--workload", default="long", choices=["long", "mixed", "short", "tiny"])
     ap.add_argument("--others", default="mixed,short",
                     help="extra workloads measured in the same run ('' for none)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bounded oracle sample for cpu_baseline (0 disables)")
     ap.add_argument("--order", default="canonical", choices=["canonical", "lpt"])
     ap.add_argument("--wg-per-cu", type=int, default=0)
@@ -52,6 +52,10 @@ def parse():
     ap.add_argument("--loop-steps", type=int, default=200,
                     help="steps per run of the 56-session resident loop (0 skips the loop)")
     ap.add_argument("--loop-runs", type=int, default=3)
+    ap.add_argument("--no-tiny", action="store_true", help="skip the tiny configuration's latency")
+    ap.add_argument("--density-probe", action=argparse.BooleanOptionalAction, default=True,
+                    help="cadenced loop with session churn at a 10 ms beat: late steps at 56 sessions "
+                         "and the most sessions (up to 80) with no late step over 3 runs")
     ap.add_argument("--density", action="store_true",
                     help="cadenced loop with session churn: most sessions with no late step "
                          "at periods of 10 and 20 ms (bisection, 3 runs each)")
@@ -71,7 +75,7 @@ def parse():
 
 
 def measure(torch, pkv, workloads, name, steps, warmup, order, wg_per_cu, copies, gate, say,
-            merge="fused", schedule=0, kv="bf16"):
+            merge="fused", schedule=0, kv="bf16", chunk=0):
     wl = workloads.CONFIGS[name]().with_kv_dtype(kv)
     dev = "cuda"
     q = wl.q(dev)
@@ -85,7 +89,7 @@ def measure(torch, pkv, workloads, name, steps, warmup, order, wg_per_cu, copies
     cfg = pkv.make_config(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages, wl.batch,
                           wl.max_pages_per_seq, scale=wl.scale,
                           order=pkv.PKV_ORDER_LPT if order == "lpt" else pkv.PKV_ORDER_CANONICAL,
-                          wg_per_cu=wg_per_cu, schedule=schedule,
+                          wg_per_cu=wg_per_cu, schedule=schedule, kv_chunk_tokens=chunk,
                           kv_dtype=pkv.PKV_KV_F32 if kv == "f32" else pkv.PKV_KV_BF16,
                           merge_mode=pkv.PKV_MERGE_SEPARATE if merge == "separate" else pkv.PKV_MERGE_FUSED)
     stream = torch.cuda.current_stream()
@@ -131,31 +135,18 @@ def measure(torch, pkv, workloads, name, steps, warmup, order, wg_per_cu, copies
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(stop)
-    # Timed region 2: the same steps with HIP events recorded by the library
-    # right around the decode kernel on the launch stream (its own duration).
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    for a, b in ev:                       # torch creates the HIP events on first record
-        a.record(stream)
-        b.record(stream)
-    torch.cuda.synchronize()
-    for i in range(steps):
-        pkv.pkv_set_decode_events(dec.handle, ev[i][0], ev[i][1])
-        pkv.pkv_decode(dec.handle, tens[i % copies], stream)
-    torch.cuda.synchronize()
-    pkv.pkv_set_decode_events(dec.handle, None, None)
     st = dec.query()
-    kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
     ms_step = total_ms / steps
+    # With the fused merge a step is one launch of the decode kernel, so the
+    # step time of back-to-back launches (HIP events on the launch stream at
+    # the two ends of the timed region) is the kernel's average launch
+    # duration, launch gaps included.
     res = {
         "workload": name, "kv_dtype": kv, "kv_bytes": info.kv_bytes, "items": info.n_items,
         "chunk_tokens": info.chunk_tokens,
         "split": bool(info.split), "launches_per_step": info.launches_per_step,
         "partial_bytes": info.partial_bytes, "ms_per_step": ms_step,
         "gbs": info.kv_bytes / (ms_step * 1e-3) / 1e9,
-        "decode_ms_mean": float(kern_ms.mean()), "decode_ms_median": float(np.median(kern_ms)),
-        "decode_ms_p99": float(np.percentile(kern_ms, 99)),
-        "decode_gbs": info.kv_bytes / (kern_ms.mean() * 1e-3) / 1e9,
         "host_wall_ms_per_step": wall * 1e3 / steps, "grid": st["grid"], "num_cus": st["num_cus"],
         "batch": wl.batch, "ctx_lens_sum": int(wl.ctx_lens.sum()),
     }
@@ -285,7 +276,7 @@ def measure_loop(torch, pkv, workloads, steps, runs, gate, say, append=False, kv
     return res
 
 
-def density_search(torch, pkv, workloads, periods_ms, max_sessions, steps, runs, say):
+def density_search(torch, pkv, workloads, periods_ms, max_sessions, steps, runs, say, probe_sessions=None):
     """Cadenced session loop (WPK note: sessions served on a fixed beat, late
     beats counted, density = most sessions with none late).  Steps are
     published on a clock of period T; a step is late if it completes after its
@@ -293,7 +284,8 @@ def density_search(torch, pkv, workloads, periods_ms, max_sessions, steps, runs,
     (lifetimes U[40, 120] steps); when one leaves, the next joins the slot at a
     step boundary with a fresh context (drawn so that it fits the slot's
     pages).  For each T the largest session count with no late step over
-    `runs` runs is found by bisection."""
+    `runs` runs is found by bisection; with probe_sessions, that many sessions
+    are also run `runs` times at each T and their late steps counted."""
     from oracle import paged_attention as pa
     dev = "cuda"
     sl = workloads.session_loop(sessions=max_sessions, steps=steps, name="loop_density")
@@ -309,20 +301,7 @@ def density_search(torch, pkv, workloads, periods_ms, max_sessions, steps, runs,
     say(f"density inputs: {max_sessions} session slots, {2 * k.numel() * 2 / 1e9:.1f} GB of K/V, "
         f"{time.perf_counter() - t0:.1f} s")
     # per-slot session schedule: lengths at every step with joins and leaves
-    rng = np.random.default_rng([workloads.MEASURE_SEED, 9])
-    lens = np.zeros((steps, max_sessions), dtype=np.int32)
-    joins = 0
-    for s in range(max_sessions):
-        cap = int(sl.l0[s])                      # the slot's pages hold cap + steps tokens
-        t, L0 = 0, cap
-        while t < steps:
-            life = int(rng.integers(40, 121))
-            for u in range(t, min(steps, t + life)):
-                lens[u, s] = L0 + (u - t)
-            t += life
-            if t < steps:
-                L0 = int(rng.integers(min(2048, cap), cap + 1))
-                joins += 1
+    lens, joins = sl.churn_lens(workloads.MEASURE_SEED)
     S_all, H, D = sl.sessions, sl.num_q_heads, sl.head_dim
     strides = (S_all * H * D, sl.pages_per_layer * sl.num_kv_heads * 16 * D, S_all * sl.max_pages,
                S_all * H * D, S_all * H)
@@ -352,27 +331,43 @@ def density_search(torch, pkv, workloads, periods_ms, max_sessions, steps, runs,
         torch.cuda.synchronize()
         return late, np.array(lat) * 1e3
 
-    # parity of a churned step: a slot after a join reads its new, shorter context
-    _, _ = run(min(8, max_sessions), 0.0)
+    # parity of churned steps: a slot after a join reads its new, shorter context
+    n_chk = min(8, max_sessions)
+    _, _ = run(n_chk, 0.0)
     o = out.float().cpu().numpy()
     l = lse.cpu().numpy()
     G = H // sl.num_kv_heads
-    t_chk = steps - 1
-    for s in range(min(8, max_sessions)):
-        L = int(lens[t_chk, s])
-        npg = -(-L // 16)
-        pg = sl.block_tables[0, s, :npg]
-        ks = workloads.bits_u16(sl.slabs("k", 0, pg, 0))[:, None]
-        vs = workloads.bits_u16(sl.slabs("v", 0, pg, 0))[:, None]
-        qg = workloads.bits_u16(sl.query_unit(t_chk, 0, s))[None, :G]
-        ro, rl = pa.range_state(qg, ks, vs, np.arange(npg)[None], 0, 0, 0, L, sl.scale, 16)
-        err = np.abs(o[t_chk, 0, s, :G] - ro).max()
-        if not err <= 2e-2:
-            raise SystemExit(f"density loop parity failed for slot {s}: {err:.3e}")
+    for t_chk in (steps // 2, steps - 1):
+        for layer in (0, sl.layers - 1):
+            for s in range(n_chk):
+                for hk in (0, sl.num_kv_heads - 1):
+                    L = int(lens[t_chk, s])
+                    npg = -(-L // 16)
+                    pg = sl.block_tables[layer, s, :npg]
+                    ks = workloads.bits_u16(sl.slabs("k", layer, pg, hk))[:, None]
+                    vs = workloads.bits_u16(sl.slabs("v", layer, pg, hk))[:, None]
+                    qg = workloads.bits_u16(sl.query_unit(t_chk, layer, s))[None, hk * G:(hk + 1) * G]
+                    ro, rl = pa.range_state(qg, ks, vs, np.arange(npg)[None], 0, 0, 0, L, sl.scale, 16)
+                    err = np.abs(o[t_chk, layer, s, hk * G:(hk + 1) * G] - ro)
+                    lerr = np.abs(l[t_chk, layer, s, hk * G:(hk + 1) * G] - rl)
+                    if not (err.max() <= 2e-2 and err.mean() <= 2e-3 and lerr.max() <= 2e-2):
+                        raise SystemExit(f"density loop parity failed: step {t_chk} layer {layer} slot {s} "
+                                         f"head {hk}: {err.max():.3e} {lerr.max():.3e}")
     say(f"density loop parity passed ({joins} joins in the schedule)")
     res = {"max_sessions_tried": max_sessions, "steps_per_run": steps, "runs": runs,
            "session_lifetime_steps": [40, 120], "joins_per_run": joins, "periods": {}}
     for T in periods_ms:
+        if probe_sessions:
+            lates, p99s = [], []
+            for _ in range(runs):
+                late, lat = run(probe_sessions, T / 1e3)
+                lates.append(late)
+                p99s.append(float(np.percentile(lat, 99)))
+            res[f"probe_{probe_sessions}_sessions_T{T}ms"] = {"late_steps": int(sum(lates)),
+                                                              "steps": runs * steps,
+                                                              "p99_ms": round(max(p99s), 4)}
+            say(f"density probe T={T} ms: {probe_sessions} sessions -> {sum(lates)} late steps of "
+                f"{runs * steps}, p99 {max(p99s):.2f} ms")
         lo, hi, best = 1, max_sessions, 0
         best_p99 = None
         while lo <= hi:
@@ -523,8 +518,7 @@ def ablations(torch, pkv, workloads, args, say):
                                  ("pages", pkv.PKV_SCHEDULE_PAGES)):
                 r, _ = measure(torch, pkv, workloads, name, steps, args.warmup, args.order, args.wg_per_cu,
                                args.copies, not args.no_gate, say, args.merge, sched, kv=kv)
-                row[label] = {"gbs": round(r["gbs"], 1), "decode_gbs": round(r["decode_gbs"], 1),
-                              "decode_us": round(r["decode_ms_mean"] * 1e3, 2)}
+                row[label] = {"gbs": round(r["gbs"], 1), "us_per_step": round(r["ms_per_step"] * 1e3, 2)}
             key = name if kv == "bf16" else f"{name}_f32"
             res["schedule"][key] = row
             say(f"ablation {key}: atomic {row['atomic']['gbs']} GB/s, static {row['static']['gbs']} GB/s, "
@@ -542,42 +536,143 @@ def ablations(torch, pkv, workloads, args, say):
     return res
 
 
-def cpu_baseline(workloads, wl, seconds, say):
-    """The oracle as it stands, on whole (sequence, KV head) units of the same
-    workload, repeated pass after pass for about `seconds` of CPU time."""
+def _oracle_worker(args):
+    """One process of the CPU baseline: regenerate the slabs of its (sequence,
+    KV head) units (untimed), wait for the others, then run the float64
+    oracle over them pass after pass for `seconds` of wall time.  Returns
+    (K+V bytes of the units computed, seconds, units)."""
+    root, name, kv, units, seconds, barrier = args
+    if root not in sys.path:
+        sys.path.insert(0, root)
+    from threadpoolctl import threadpool_limits
+    import torch
+    torch.set_num_threads(1)                         # the input generator, too, on this core only
     from oracle import paged_attention as pa
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
+    from paged_kv_attention_persistent_amd import workloads
+    wl = workloads.CONFIGS[name]().with_kv_dtype(kv)
     qb = workloads.bits_u16(wl.q("cpu"))
     G = wl.num_q_heads // wl.num_kv_heads
-    units = [(b, h) for b in range(wl.batch) for h in range(wl.num_kv_heads)]
-    cache = {}
-    done_bytes, spent, n = 0, 0.0, 0
-    while n == 0 or spent < seconds:
-        b, hk = units[n % len(units)]
+    data = []
+    for b, hk in units:
         L = int(wl.ctx_lens[b])
         npg = -(-L // 16)
-        if (b, hk) not in cache:
-            pg = wl.block_table[b, :npg]
-            cache[(b, hk)] = (workloads.kv_host(wl.pool_slabs("k", pg, hk))[:, None],
-                              workloads.kv_host(wl.pool_slabs("v", pg, hk))[:, None])
-        ks, vs = cache[(b, hk)]
-        t0 = time.perf_counter()
+        pg = wl.block_table[b, :npg]
+        data.append((b, hk, L, npg, workloads.kv_host(wl.pool_slabs("k", pg, hk))[:, None],
+                     workloads.kv_host(wl.pool_slabs("v", pg, hk))[:, None]))
+    done, n = 0, 0
+    with threadpool_limits(limits=1):                # one core per process
+        b, hk, L, npg, ks, vs = data[0]              # untimed warm-up (first-touch of temporaries)
         pa.range_state(qb[b:b + 1, hk * G:(hk + 1) * G], ks, vs, np.arange(npg)[None], 0, 0, 0, L,
                        wl.scale, 16)
-        spent += time.perf_counter() - t0
-        done_bytes += L * wl.head_dim * wl.kv_elem_bytes * 2
-        n += 1
-    passes = n / len(units)
-    say(f"cpu baseline: {n} units ({passes:.2f} passes), {spent:.1f} s")
-    return {"value": done_bytes / spent / 1e9, "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{n} (sequence, KV head) units = {passes:.2f} passes over the {len(units)} units "
-                      f"of the '{wl.name}' workload ({done_bytes / 1e6:.1f} MB of K+V), float64 NumPy "
-                      f"oracle, inputs generated on the host and excluded from the time"}
+        barrier.wait()
+        t0 = time.perf_counter()
+        while n == 0 or time.perf_counter() - t0 < seconds:
+            b, hk, L, npg, ks, vs = data[n % len(data)]
+            pa.range_state(qb[b:b + 1, hk * G:(hk + 1) * G], ks, vs, np.arange(npg)[None], 0, 0, 0, L,
+                           wl.scale, 16)
+            done += L * wl.head_dim * wl.kv_elem_bytes * 2
+            n += 1
+        spent = time.perf_counter() - t0
+    return done, spent, n
+
+
+def cpu_baseline(workloads, wl, seconds, say):
+    """The float64 oracle as it stands on whole (sequence, KV head) units of
+    the same workload: one process per host core available to this process
+    (os.sched_getaffinity), each pinned to one BLAS thread and running its
+    share of the units pass after pass for `seconds`; then the same on one
+    core.  Throughput = K+V bytes of the units computed / wall seconds.  The
+    worker processes are started fresh (spawn), not forked from this one."""
+    import multiprocessing as mp
+    root = os.path.dirname(os.path.abspath(__file__))
+    units = [(b, h) for b in range(wl.batch) for h in range(wl.num_kv_heads)]
+    cores = len(os.sched_getaffinity(0))
+    ctx = mp.get_context("spawn")
+    res = {}
+    for label, n_proc in (("all", cores), ("one", 1)):
+        if n_proc == 1:
+            shares = [units[:1]]                     # one core: the first unit, pass after pass
+        else:
+            shares = [[units[(i + j * n_proc) % len(units)] for j in range(max(1, -(-len(units) // n_proc)))]
+                      for i in range(n_proc)]
+        with ctx.Manager() as mgr:
+            barrier = mgr.Barrier(n_proc)
+            with ctx.Pool(n_proc) as pool:
+                out = pool.map(_oracle_worker, [(root, wl.name if wl.name in workloads.CONFIGS else "long",
+                                                 wl.kv_dtype, sh, seconds, barrier) for sh in shares])
+        total = sum(o[0] for o in out)
+        wall = max(o[1] for o in out)
+        res[label] = {"gbs": total / wall / 1e9, "processes": n_proc, "units": sum(o[2] for o in out),
+                      "seconds": wall, "bytes": total}
+        say(f"cpu baseline ({n_proc} process{'es' if n_proc > 1 else ''}): {res[label]['gbs']:.2f} GB/s, "
+            f"{res[label]['units']} units in {wall:.1f} s")
+    a, o = res["all"], res["one"]
+    return {"value": round(a["gbs"], 4), "unit": "GB/s", "cores": a["processes"], "kind": "oracle",
+            "affinity_cores": cores, "one_core_value": round(o["gbs"], 4),
+            "sample": f"float64 NumPy oracle on whole (sequence, KV head) units of the '{wl.name}' workload "
+                      f"({len(units)} units of {int(wl.ctx_lens.max())} tokens max), {a['processes']} "
+                      f"processes x 1 BLAS thread for {a['seconds']:.1f} s: {a['units']} units, "
+                      f"{a['bytes'] / 1e9:.2f} GB of K+V; one core: {o['units']} units in {o['seconds']:.1f} s; "
+                      f"inputs regenerated in each process and excluded from the time"}
+
+
+def read_ceiling(torch, pkv, say, nbytes=2 << 30, reps=5):
+    """Measured HBM read ceiling: pkv_read_probe (non-temporal dwordx4 loads,
+    sequential) over `nbytes`, `reps` back-to-back launches timed by HIP
+    events on the launch stream, at 1, 2 and 3 workgroups per CU; the best."""
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(3 * cus * 256, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    best, best_grid = 0.0, 0
+    for per_cu in (1, 2, 3):
+        grid = per_cu * cus
+        for _ in range(2):
+            pkv.pkv_read_probe(src, nbytes, sink, grid, stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            pkv.pkv_read_probe(src, nbytes, sink, grid, stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        gbs = nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+        if gbs > best:
+            best, best_grid = gbs, grid
+    say(f"read ceiling: {best:.1f} GB/s ({nbytes >> 20} MiB, grid {best_grid})")
+    del src, sink
+    torch.cuda.empty_cache()
+    return best, best_grid
+
+
+def tiny_latency(torch, pkv, workloads, steps, say):
+    """The tiny configuration (64 KiB of K/V, cache-resident): device time per
+    call of back-to-back launches, and the host round trip of one call
+    (queue build + decode + synchronise)."""
+    r, wl = measure(torch, pkv, workloads, "tiny", steps, 10, "canonical", 0, 1, True, say)
+    q, k, v = wl.q("cuda"), wl.pool("k", "cuda", False), wl.pool("v", "cuda", False)
+    bt, lens = wl.block_table_t("cuda"), wl.ctx_lens_t("cuda")
+    out = torch.empty(wl.batch, wl.num_q_heads, wl.head_dim, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(wl.batch, wl.num_q_heads, dtype=torch.float32, device="cuda")
+    cfg = pkv.make_config(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages, wl.batch,
+                          wl.max_pages_per_seq, scale=wl.scale)
+    dec = pkv.PagedDecoder(cfg)
+    t = pkv.make_tensors(q, k, v, bt, lens, out, lse)
+    rt = []
+    for i in range(steps + 10):
+        a = time.perf_counter()
+        dec.build_queue(wl.ctx_lens)
+        pkv.pkv_decode(dec.handle, t, dec.stream)
+        torch.cuda.synchronize()
+        if i >= 10:
+            rt.append(time.perf_counter() - a)
+    dec.close()
+    rt = np.array(rt) * 1e6
+    say(f"tiny: {r['ms_per_step'] * 1e3:.2f} us per call back to back, host round trip "
+        f"p50 {np.median(rt):.1f} us")
+    return {"device_us_per_call": round(r["ms_per_step"] * 1e3, 3),
+            "host_round_trip_us_p50": round(float(np.median(rt)), 2),
+            "host_round_trip_us_p99": round(float(np.percentile(rt, 99)), 2),
+            "kv_bytes": r["kv_bytes"], "items": r["items"]}
 
 
 def profile_pass(torch, pkv, workloads, args, say):
@@ -642,17 +737,25 @@ def main():
     main_res, wl = measure(torch, pkv, workloads, args.workload, args.steps, args.warmup,
                            args.order, args.wg_per_cu, args.copies, not args.no_gate, say, args.merge,
                            sched, kv=args.kv)
-    say(f"{args.workload}: {main_res['gbs']:.1f} GB/s per step, decode kernel "
-        f"{main_res['decode_gbs']:.1f} GB/s ({main_res['decode_ms_mean'] * 1e3:.1f} us)")
+    say(f"{args.workload}: {main_res['gbs']:.1f} GB/s per step ({main_res['ms_per_step'] * 1e3:.2f} us, "
+        f"{main_res['launches_per_step']} launch per step)")
+    keys = ("gbs", "ms_per_step", "items", "split", "chunk_tokens", "kv_bytes", "launches_per_step")
     others = {}
     for name in [x for x in args.others.split(",") if x and x != args.workload]:
         r, _ = measure(torch, pkv, workloads, name, max(args.steps // 2, 10), args.warmup,
                        args.order, args.wg_per_cu, args.copies, not args.no_gate, say, args.merge, sched)
-        others[name] = {k: r[k] for k in ("gbs", "decode_gbs", "ms_per_step", "decode_ms_mean",
-                                          "items", "split", "chunk_tokens", "kv_bytes",
-                                          "launches_per_step")}
+        others[name] = {k: r[k] for k in keys}
         others[name]["pct_of_hbm_peak"] = 100.0 * r["gbs"] / HBM_PEAK_GBS
-        say(f"{name}: {r['gbs']:.1f} GB/s per step, decode {r['decode_gbs']:.1f} GB/s")
+        say(f"{name}: {r['gbs']:.1f} GB/s per step ({r['ms_per_step'] * 1e3:.2f} us, chunk {r['chunk_tokens']})")
+        if name == "mixed":
+            # the configuration's stated range length, beside the fitted one
+            r, _ = measure(torch, pkv, workloads, name, max(args.steps // 2, 10), args.warmup,
+                           args.order, args.wg_per_cu, args.copies, False, say, args.merge, sched, chunk=4096)
+            others["mixed_chunk4096"] = {k: r[k] for k in keys}
+            others["mixed_chunk4096"]["pct_of_hbm_peak"] = 100.0 * r["gbs"] / HBM_PEAK_GBS
+            say(f"mixed at chunk 4096: {r['gbs']:.1f} GB/s per step ({r['items']} items)")
+    if not args.no_tiny:
+        others["tiny"] = tiny_latency(torch, pkv, workloads, max(args.steps // 2, 10), say)
     f32 = {}
     if not args.no_f32:
         for name in ("long", "mixed", "short"):
@@ -661,14 +764,11 @@ def main():
             r, _ = measure(torch, pkv, workloads, name, max(args.steps // 2, 10), args.warmup,
                            args.order, args.wg_per_cu, args.copies, not args.no_gate, say, args.merge,
                            sched, kv="f32")
-            f32[name] = {k: r[k] for k in ("gbs", "decode_gbs", "ms_per_step", "decode_ms_mean",
-                                           "items", "chunk_tokens", "kv_bytes")}
+            f32[name] = {k: r[k] for k in keys if k != "split"}
             f32[name]["pct_of_hbm_peak"] = 100.0 * r["gbs"] / HBM_PEAK_GBS
-            f32[name]["decode_frac"] = r["decode_gbs"] / HBM_PEAK_GBS
             if name == "long":
                 f32[name]["traffic"] = measured_traffic(os.path.dirname(os.path.abspath(__file__)), "f32")
-            say(f"{name} (fp32 cache): {r['gbs']:.1f} GB/s per step, decode {r['decode_gbs']:.1f} GB/s "
-                f"({r['decode_ms_mean'] * 1e3:.1f} us)")
+            say(f"{name} (fp32 cache): {r['gbs']:.1f} GB/s per step ({r['ms_per_step'] * 1e3:.1f} us)")
     loop = loop_append = loop_f32 = None
     if args.loop_steps > 0:
         loop = measure_loop(torch, pkv, workloads, args.loop_steps, args.loop_runs,
@@ -680,11 +780,18 @@ def main():
             loop_f32 = measure_loop(torch, pkv, workloads, args.loop_steps, args.loop_runs,
                                     not args.no_gate, say, kv="f32")
     abl = ablations(torch, pkv, workloads, args, say) if args.ablations else None
-    density = density_search(torch, pkv, workloads, (10, 20), 160, 100, 3, say) if args.density else None
+    if args.density:
+        density = density_search(torch, pkv, workloads, (10, 20), 160, 100, 3, say, probe_sessions=56)
+    elif args.density_probe:
+        density = density_search(torch, pkv, workloads, (10,), 80, 100, 3, say, probe_sessions=56)
+    else:
+        density = None
+    ceiling, ceiling_grid = read_ceiling(torch, pkv, say)
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(workloads, wl, args.cpu_seconds, say)
-    achieved = main_res["decode_gbs"]
+    achieved = main_res["gbs"]
+    one_launch = main_res["launches_per_step"] == 1
     line = {
         "metric": METRIC,
         "value": round(main_res["gbs"], 2),
@@ -709,12 +816,19 @@ def main():
                   if args.workload == "long" else
                   {"workload": args.workload, "items": main_res["items"], "kv_dtype": args.kv,
                    "kv_bytes_per_step": main_res["kv_bytes"]},
+        # achieved: algorithmic K+V bytes per launch / the launch's average
+        # duration, from back-to-back launches timed by HIP events on the
+        # launch stream (one launch per step with the fused merge)
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__)), args.kv)
                      if args.workload == "long" else None,
                      "kernel": f"decode_kernel<128,4,{'KvF32' if args.kv == 'f32' else 'KvBf16'}>",
-                     "decode_us_mean": round(main_res["decode_ms_mean"] * 1e3, 3)},
+                     "kernel_us_mean": round(main_res["ms_per_step"] * 1e3, 3) if one_launch else None,
+                     "bytes_per_launch": main_res["kv_bytes"],
+                     "ceiling": {"value": round(ceiling, 1), "unit": "GB/s",
+                                 "kind": f"measured streaming read (pkv_read_probe, 2 GiB, grid {ceiling_grid})",
+                                 "frac": round(achieved / ceiling, 4)}},
         "cpu_baseline": cpu,
         "session_loop_p99_ms": loop["p99_ms"] if loop else None,
         "session_loop": loop,

@@ -229,7 +229,9 @@ typedef struct pkv_layout {
 
 typedef struct pkv_handle pkv_handle;
 
-/* Bytes of device workspace a handle with this config needs. */
+/* Bytes of device workspace a handle with this config needs (the caller
+ * allocates it: GPUOS page, section 4.3).  PKV_ERR_UNSUPPORTED or
+ * PKV_ERR_INVALID_ARG for a config pkv_create would refuse. */
 PKV_API pkv_status pkv_workspace_size(const pkv_config* cfg, size_t* bytes);
 
 /* Workspace layout of a config (pure host computation). */
@@ -250,31 +252,65 @@ PKV_API pkv_status pkv_workspace_layout(const pkv_config* cfg, pkv_layout* layou
  * Persistent Kernel note ("What a persistent kernel is", "Runtime and timing
  * boundary"); the host cannot run other kernels on the CUs meanwhile. */
 
-/* Create a handle on the current HIP device.  workspace: device memory of at
- * least pkv_workspace_size bytes, 256-byte aligned, owned by the caller and
- * kept alive until pkv_destroy.  stream: hipStream_t used for queue uploads
+/* Create a handle on the current HIP device: the runtime's initialisation
+ * call, in the shape of the host API that sets up the persistent executor
+ * and its queue on the GPUOS page ("GPUOS: A GPU Operating System Primitive
+ * for Transparent Operation Fusion", section 4.3 and Table 1, the init
+ * call), with memory that the framework already allocated (section 4.3,
+ * "Memory Management and Safety").  workspace: device memory of at least
+ * pkv_workspace_size bytes, 256-byte aligned, owned by the caller and kept
+ * alive until pkv_destroy.  stream: hipStream_t used for queue uploads
  * (0 = the null stream).  Initialises the workspace's control words
- * (asynchronously on stream). */
+ * (asynchronously on stream).  With persistent = 1 it also launches the
+ * resident kernel; PKV_ERR_UNSUPPORTED if its grid (wg_per_cu workgroups
+ * per CU) cannot be resident at once on this device.
+ *
+ * Streams.  One handle runs one piece of device work at a time.  The
+ * library orders its own launches across streams with events: a queue
+ * upload or device build waits for the previous decode (or gather) that read
+ * the queue, and a decode waits for the queue's upload and for the previous
+ * decode, whichever streams they ran on.  Calls on the handle's own stream
+ * are ordered by the stream alone. */
 PKV_API pkv_status pkv_create(const pkv_config* cfg, void* workspace, size_t workspace_bytes,
                               void* stream, pkv_handle** out);
 
 /* Build the compact work queue on the host from host context lengths
- * (int32 [batch]) and enqueue its upload on the handle's stream.  Returns
- * after the upload is enqueued; info (nullable) receives the counters. */
+ * (int32 [batch]) and enqueue its upload on the handle's stream: the queue
+ * of tasks for non-empty (row, KV head, range) intervals of the PersistentKV
+ * page ("PersistentKV: Page-Aware Decode Scheduling for Long-Context LLM
+ * Serving on Commodity GPUs", Methodology 1 "Compact Workqueue"), with the
+ * split decision of Methodology 2 "Calibrated Adaptive Policy" (pkv_config
+ * policy above).  Returns after the upload is enqueued; info (nullable)
+ * receives the counters.  Errors: PKV_ERR_CAPACITY if batch exceeds
+ * max_batch, a length exceeds max_pages_per_seq pages or the items exceed
+ * max_items (nothing is uploaded).  In the resident loop the queue goes to
+ * a host slot for the next step instead. */
 PKV_API pkv_status pkv_build_queue(pkv_handle* h, const int32_t* ctx_lens_host, int32_t batch,
                                    pkv_queue_info* info);
 
-/* Same queue, built on the device from device context lengths (int32
+/* Same queue (PersistentKV page, Methodology 1 "Compact Workqueue" and
+ * Methodology 2), built on the device from device context lengths (int32
  * [batch]) by one workgroup on stream; bit-identical to pkv_build_queue.
  * Supports PKV_ORDER_CANONICAL only.  The split decision is taken on the
- * device, so the host learns no counters. */
+ * device, so the host learns no counters.  A length outside
+ * [0, max_pages_per_seq * P] or too many items sets the device error word
+ * PKV_DEVERR_BAD_ITEM (detail: the row, or the item count) and leaves an
+ * empty queue; the next pkv_decode or pkv_query reports it. */
 PKV_API pkv_status pkv_build_queue_device(pkv_handle* h, const int32_t* ctx_lens_device,
                                           int32_t batch, void* stream);
 
-/* Enqueue the decode for the built queue on stream (async): the persistent
- * decode kernel, then, if any row is split or empty, the merge kernel.
- * Returns PKV_ERR_DEVICE_FAULT (and enqueues nothing) if an earlier call left
- * a device error word set. */
+/* Decode attention for the built queue (PersistentKV page, Methodology 1
+ * "Native Block-Table Decode Engine": K/V read in place through the block
+ * table, "Row-Local Bounds", and "Sequence Splitting" with the exact merge of
+ * partial states).  One-shot handles: enqueue on stream (async) the
+ * persistent decode kernel, whose workgroups pop queue items with one atomic
+ * each (GPUOS page, section 4.1 "Persistent Kernel Executor"), then, with a
+ * separate merge and any split or empty row, the merge kernel.  Resident
+ * loop: publish one step and block until it completes (below).  Returns
+ * PKV_ERR_DEVICE_FAULT (and enqueues nothing) if an earlier call left a
+ * device error word set; PKV_ERR_STATE before a queue is built;
+ * PKV_ERR_INVALID_ARG for null or misaligned tensors or a batch other than
+ * the built queue's. */
 PKV_API pkv_status pkv_decode(pkv_handle* h, const pkv_tensors* t, void* stream);
 
 /* Optional timing: hipEvent_t handles recorded on the decode stream right
@@ -323,14 +359,25 @@ PKV_API pkv_status pkv_copy_probe(void* dst, const void* src, size_t bytes, int3
 PKV_API pkv_status pkv_read_probe(const void* src, size_t bytes, void* sink, int32_t grid,
                                   void* stream);
 
-/* Read the control words (synchronises the device).  Returns
- * PKV_ERR_DEVICE_FAULT when the device error word is set. */
+/* Read the control words: the queue head, the items finished, the device
+ * error word and, for the resident loop, whether the kernel is alive and
+ * which step it completed -- the queue-inspection and liveness calls of the
+ * GPUOS page's host API (Table 1, peek_queue and worker_alive).  Synchronises
+ * the device for one-shot handles; reads host words only while a resident
+ * loop runs.  Returns PKV_ERR_DEVICE_FAULT when the device error word is
+ * set (info is filled in either way). */
 PKV_API pkv_status pkv_query(pkv_handle* h, pkv_runtime_info* info);
 
-/* Clear the device error word (synchronises the device). */
+/* Clear the device error word after a reported fault (synchronises the
+ * device), so that the handle may be used again (GPUOS page, section 5: a
+ * kill switch returns an error code to the host, which decides what next).
+ * PKV_ERR_STATE while a resident loop runs. */
 PKV_API pkv_status pkv_clear_error(pkv_handle* h);
 
-/* Destroy the handle (does not free the caller's workspace). */
+/* Destroy the handle, the shutdown call of the GPUOS page's host API
+ * (Table 1): for a resident loop, raise the exit flag and wait until the
+ * kernel has left; then free the library's host memory.  Does not free the
+ * caller's workspace. */
 PKV_API pkv_status pkv_destroy(pkv_handle* h);
 
 PKV_API const char* pkv_status_string(pkv_status s);

@@ -19,6 +19,92 @@
 
 using namespace pkv;
 
+namespace pkv {
+
+DecodeParams decode_params(const Resolved& r, const pkv_layout& lay, unsigned char* ws, const pkv_tensors* t,
+                           uint32_t* host_error) {
+    DecodeParams p;
+    memset(&p, 0, sizeof(p));
+    p.q = static_cast<const uint16_t*>(t ? t->q : nullptr);
+    p.k_pool = static_cast<const uint16_t*>(t ? t->k_pool : nullptr);
+    p.v_pool = static_cast<const uint16_t*>(t ? t->v_pool : nullptr);
+    p.block_table = t ? t->block_table : nullptr;
+    p.out = static_cast<uint16_t*>(t ? t->out : nullptr);
+    p.lse = t ? t->lse : nullptr;
+    p.ctrl = reinterpret_cast<Ctrl*>(ws + lay.ctrl_off);
+    p.qhdr = reinterpret_cast<const QHdr*>(ws + lay.queue_off);
+    p.n_chunks = reinterpret_cast<const int32_t*>(ws + lay.n_chunks_off);
+    p.part_off = reinterpret_cast<const int32_t*>(ws + lay.part_off_off);
+    p.merge_rows = reinterpret_cast<const int32_t*>(ws + lay.merge_rows_off);
+    p.items = reinterpret_cast<const Item*>(ws + lay.items_off);
+    p.partial_o = reinterpret_cast<float*>(ws + lay.partial_o_off);
+    p.sink = reinterpret_cast<const char*>(ws + lay.sink_off);
+    p.row_len = reinterpret_cast<const int32_t*>(ws + lay.row_len_off);
+    p.cursors = r.schedule == PKV_SCHEDULE_PAGES ? reinterpret_cast<uint32_t*>(ws + lay.cursor_off) : nullptr;
+    p.partial_lse = reinterpret_cast<float*>(ws + lay.partial_lse_off);
+    p.arrive = reinterpret_cast<uint32_t*>(ws + lay.arrive_off);
+    p.trace = nullptr;
+    p.trace_cap = 0;
+    p.head = &reinterpret_cast<Ctrl*>(ws + lay.ctrl_off)->head;
+    p.head_dim = r.d;
+    p.coherent_out = 0;
+    p.static_first = 1;
+    p.static_sched = r.schedule == PKV_SCHEDULE_STATIC ? 1 : 0;
+    p.coherent_in = 0;
+    p.host_error = host_error;
+    p.batch = t ? t->batch : 0;
+    p.bt_stride = (t && t->block_table_stride) ? t->block_table_stride : r.max_pages_per_seq;
+    p.num_pages = r.num_pages;
+    p.hq = r.hq;
+    p.hkv = r.hkv;
+    p.max_tokens = r.max_pages_per_seq * r.page;
+    p.max_items = r.max_items;
+    p.fused_merge = r.merge_mode == PKV_MERGE_FUSED ? 1 : 0;
+    p.scale_log2 = r.scale * 1.44269504088896340736f;
+    return p;
+}
+
+BuildParams build_params(const Resolved& r, const pkv_layout& lay, unsigned char* ws, const int32_t* ctx_lens,
+                         int32_t batch, uint32_t* host_error) {
+    BuildParams p;
+    memset(&p, 0, sizeof(p));
+    p.ctx_lens = ctx_lens;
+    p.qhdr = reinterpret_cast<QHdr*>(ws + lay.queue_off);
+    p.n_chunks = reinterpret_cast<int32_t*>(ws + lay.n_chunks_off);
+    p.part_off = reinterpret_cast<int32_t*>(ws + lay.part_off_off);
+    p.row_len = reinterpret_cast<int32_t*>(ws + lay.row_len_off);
+    p.merge_rows = reinterpret_cast<int32_t*>(ws + lay.merge_rows_off);
+    p.items = reinterpret_cast<Item*>(ws + lay.items_off);
+    p.ctrl = reinterpret_cast<Ctrl*>(ws + lay.ctrl_off);
+    p.host_error = host_error;
+    p.batch = batch;
+    p.hkv = r.hkv;
+    p.num_cus = r.num_cus;
+    p.chunk = r.chunk;
+    p.policy = r.policy;
+    p.max_items = r.max_items;
+    p.max_tokens = r.max_pages_per_seq * r.page;
+    return p;
+}
+
+pkv_status check_tensor_args(const Resolved& r, const pkv_tensors* t, const char** why) {
+    auto bad = [&](pkv_status s, const char* w) { *why = w; return s; };
+    auto aligned = [](const void* p, size_t a) { return ((uintptr_t)p % a) == 0; };
+    if (!t) return bad(PKV_ERR_INVALID_ARG, "null tensors");
+    if (!t->q || !t->k_pool || !t->v_pool || !t->block_table || !t->out || !t->lse)
+        return bad(PKV_ERR_INVALID_ARG, "null tensor pointer");
+    if (!aligned(t->q, 16) || !aligned(t->k_pool, 16) || !aligned(t->v_pool, 16) || !aligned(t->out, 16))
+        return bad(PKV_ERR_INVALID_ARG, "q, k_pool, v_pool and out must be 16-byte aligned");
+    if (!aligned(t->block_table, 4) || !aligned(t->lse, 4) || (t->ctx_lens && !aligned(t->ctx_lens, 4)))
+        return bad(PKV_ERR_INVALID_ARG, "block_table, ctx_lens and lse must be 4-byte aligned");
+    if (t->batch < 0 || t->batch > r.max_batch) return bad(PKV_ERR_CAPACITY, "batch outside [0, max_batch]");
+    if (t->block_table_stride < 0 || (t->block_table_stride > 0 && t->block_table_stride < r.max_pages_per_seq))
+        return bad(PKV_ERR_INVALID_ARG, "block_table_stride smaller than max_pages_per_seq");
+    return PKV_OK;
+}
+
+}  // namespace pkv
+
 struct pkv_handle {
     Resolved r;
     pkv_layout lay;
@@ -33,7 +119,10 @@ struct pkv_handle {
     bool staging_pending[2] = {false, false};
     int staging_next = 0;
     size_t staging_bytes = 0;
-    hipEvent_t upload_evt = nullptr;
+    hipEvent_t upload_evt = nullptr;    // marks the last write of the device queue (recorded on demand)
+    hipStream_t upload_stream = nullptr;
+    hipEvent_t consumed_evt = nullptr;  // marks the last kernel that read the queue (recorded on demand)
+    hipStream_t consume_stream = nullptr;
     // mapped host word mirrored by the kernels on a device fault
     uint32_t* host_err = nullptr;
     uint32_t* host_err_dev = nullptr;
@@ -75,45 +164,9 @@ pkv_status hip_fail(pkv_handle* h, hipError_t e, const char* what) {
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 DecodeParams make_params(const pkv_handle* h, const pkv_tensors* t) {
-    DecodeParams p;
-    memset(&p, 0, sizeof(p));
-    p.q = static_cast<const uint16_t*>(t ? t->q : nullptr);
-    p.k_pool = static_cast<const uint16_t*>(t ? t->k_pool : nullptr);
-    p.v_pool = static_cast<const uint16_t*>(t ? t->v_pool : nullptr);
-    p.block_table = t ? t->block_table : nullptr;
-    p.out = static_cast<uint16_t*>(t ? t->out : nullptr);
-    p.lse = t ? t->lse : nullptr;
-    p.ctrl = reinterpret_cast<Ctrl*>(h->ws + h->lay.ctrl_off);
-    p.qhdr = reinterpret_cast<const QHdr*>(h->ws + h->lay.queue_off);
-    p.n_chunks = reinterpret_cast<const int32_t*>(h->ws + h->lay.n_chunks_off);
-    p.part_off = reinterpret_cast<const int32_t*>(h->ws + h->lay.part_off_off);
-    p.merge_rows = reinterpret_cast<const int32_t*>(h->ws + h->lay.merge_rows_off);
-    p.items = reinterpret_cast<const Item*>(h->ws + h->lay.items_off);
-    p.partial_o = reinterpret_cast<float*>(h->ws + h->lay.partial_o_off);
-    p.sink = reinterpret_cast<const char*>(h->ws + h->lay.sink_off);
-    p.row_len = reinterpret_cast<const int32_t*>(h->ws + h->lay.row_len_off);
-    p.cursors = h->r.schedule == PKV_SCHEDULE_PAGES ? reinterpret_cast<uint32_t*>(h->ws + h->lay.cursor_off)
-                                                     : nullptr;
-    p.partial_lse = reinterpret_cast<float*>(h->ws + h->lay.partial_lse_off);
-    p.arrive = reinterpret_cast<uint32_t*>(h->ws + h->lay.arrive_off);
+    DecodeParams p = decode_params(h->r, h->lay, h->ws, t, h->host_err_dev);
     p.trace = h->trace;
     p.trace_cap = h->trace_cap;
-    p.head = &reinterpret_cast<Ctrl*>(h->ws + h->lay.ctrl_off)->head;
-    p.head_dim = h->r.d;
-    p.coherent_out = 0;
-    p.static_first = 1;
-    p.static_sched = h->r.schedule == PKV_SCHEDULE_STATIC ? 1 : 0;
-    p.coherent_in = 0;
-    p.host_error = h->host_err_dev;
-    p.batch = t ? t->batch : 0;
-    p.bt_stride = (t && t->block_table_stride) ? t->block_table_stride : h->r.max_pages_per_seq;
-    p.num_pages = h->r.num_pages;
-    p.hq = h->r.hq;
-    p.hkv = h->r.hkv;
-    p.max_tokens = h->r.max_pages_per_seq * h->r.page;
-    p.max_items = h->r.max_items;
-    p.fused_merge = h->r.merge_mode == PKV_MERGE_FUSED ? 1 : 0;
-    p.scale_log2 = h->r.scale * 1.44269504088896340736f;
     return p;
 }
 
@@ -248,19 +301,34 @@ pkv_status decode_loop(pkv_handle* h, const pkv_tensors* t) {
     return PKV_OK;
 }
 
+// Ordering of the handle's device work across streams.  The device queue (and
+// the control words) are written by a queue upload or the device builder and
+// read by the decode, merge and gather kernels; a write must not start before
+// the last reader on another stream has finished, and a reader must not
+// start before the last write.  The handle remembers the stream of the last
+// write and of the last reader.  Work on that same stream is ordered by the
+// stream; work on another stream first waits for an event recorded on the
+// remembered stream at that moment (it marks everything enqueued there so far,
+// which includes the write or the reader).  Events are recorded only when a
+// call on another stream needs them: an event record after every launch costs
+// the back-to-back launches of one stream several microseconds each.
+hipError_t after_upload(pkv_handle* h, hipStream_t s) {
+    if (s == h->upload_stream) return hipSuccess;
+    hipError_t e = hipEventRecord(h->upload_evt, h->upload_stream);
+    return e != hipSuccess ? e : hipStreamWaitEvent(s, h->upload_evt, 0);
+}
+hipError_t after_readers(pkv_handle* h, hipStream_t s) {
+    if (s == h->consume_stream) return hipSuccess;
+    hipError_t e = hipEventRecord(h->consumed_evt, h->consume_stream);
+    return e != hipSuccess ? e : hipStreamWaitEvent(s, h->consumed_evt, 0);
+}
+void mark_upload(pkv_handle* h, hipStream_t s) { h->upload_stream = s; }
+void mark_readers(pkv_handle* h, hipStream_t s) { h->consume_stream = s; }
+
 pkv_status check_tensors(pkv_handle* h, const pkv_tensors* t) {
-    if (!t) return fail(h, PKV_ERR_INVALID_ARG, "null tensors");
-    if (!t->q || !t->k_pool || !t->v_pool || !t->block_table || !t->out || !t->lse)
-        return fail(h, PKV_ERR_INVALID_ARG, "null tensor pointer");
-    if (!aligned(t->q, 16) || !aligned(t->k_pool, 16) || !aligned(t->v_pool, 16) || !aligned(t->out, 16))
-        return fail(h, PKV_ERR_INVALID_ARG, "q, k_pool, v_pool and out must be 16-byte aligned");
-    if (!aligned(t->block_table, 4) || !aligned(t->lse, 4) || (t->ctx_lens && !aligned(t->ctx_lens, 4)))
-        return fail(h, PKV_ERR_INVALID_ARG, "block_table, ctx_lens and lse must be 4-byte aligned");
-    if (t->batch < 0 || t->batch > h->r.max_batch) return fail(h, PKV_ERR_CAPACITY, "batch outside [0, max_batch]");
-    if (t->block_table_stride < 0 ||
-        (t->block_table_stride > 0 && t->block_table_stride < h->r.max_pages_per_seq))
-        return fail(h, PKV_ERR_INVALID_ARG, "block_table_stride smaller than max_pages_per_seq");
-    return PKV_OK;
+    const char* why = nullptr;
+    const pkv_status s = check_tensor_args(h->r, t, &why);
+    return s == PKV_OK ? s : fail(h, s, why);
 }
 
 }  // namespace
@@ -337,6 +405,17 @@ PKV_API pkv_status pkv_create(const pkv_config* cfg, void* workspace, size_t wor
     h->ws = static_cast<unsigned char*>(workspace);
     h->stream = static_cast<hipStream_t>(stream);
     h->grid = h->device_cus * h->r.wg_per_cu;
+    if (h->r.persistent) {
+        // The resident kernel's dependency waits assume that every workgroup
+        // of its grid is resident at once; refuse a build whose registers or
+        // LDS would not fit wg_per_cu workgroups on a CU.
+        int fit = 0;
+        if (resident_occupancy(h->r.d, h->r.g, h->r.kv_dtype, &fit) != 0 || fit < h->r.wg_per_cu) {
+            h->last_error = "resident kernel does not fit wg_per_cu workgroups per CU";
+            delete h;
+            return PKV_ERR_UNSUPPORTED;
+        }
+    }
     h->staging_bytes = h->lay.items_off - h->lay.queue_off + 16ull * h->r.max_items;
     for (int i = 0; i < 2; ++i) {
         if ((e = hipHostMalloc((void**)&h->staging[i], h->staging_bytes, hipHostMallocDefault)) != hipSuccess ||
@@ -347,6 +426,7 @@ PKV_API pkv_status pkv_create(const pkv_config* cfg, void* workspace, size_t wor
         memset(h->staging[i], 0, h->staging_bytes);
     }
     if ((e = hipEventCreateWithFlags(&h->upload_evt, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&h->consumed_evt, hipEventDisableTiming)) != hipSuccess ||
         (e = hipHostMalloc((void**)&h->host_err, 64, hipHostMallocMapped | hipHostMallocCoherent)) != hipSuccess ||
         (e = hipHostGetDevicePointer((void**)&h->host_err_dev, h->host_err, 0)) != hipSuccess) {
         pkv_destroy(h);
@@ -366,8 +446,9 @@ PKV_API pkv_status pkv_create(const pkv_config* cfg, void* workspace, size_t wor
     memset(qh, 0, sizeof(QHdr));
     e = hipMemcpyAsync(h->ws + h->lay.queue_off, qh, sizeof(QHdr), hipMemcpyHostToDevice, h->stream);
     if (e == hipSuccess) e = hipEventRecord(h->staging_evt[0], h->stream);
-    if (e == hipSuccess) e = hipEventRecord(h->upload_evt, h->stream);
     if (e != hipSuccess) { pkv_destroy(h); return PKV_ERR_HIP; }
+    mark_upload(h, h->stream);
+    mark_readers(h, h->stream);
     h->staging_pending[0] = true;
     h->staging_next = 1;
     if (h->r.persistent) {
@@ -424,10 +505,13 @@ PKV_API pkv_status pkv_build_queue(pkv_handle* h, const int32_t* ctx_lens_host, 
                               h->r.max_items, &qi, &why, row_len);
     if (s != PKV_OK) return fail(h, s, why);
     const size_t bytes = (h->lay.items_off - q0) + 16ull * qi.n_items;
+    // the previous queue may still be read by a decode on another stream
+    if ((e = after_readers(h, h->stream)) != hipSuccess) return hip_fail(h, e, "stream wait");
+    if ((e = after_upload(h, h->stream)) != hipSuccess) return hip_fail(h, e, "stream wait");
     if ((e = hipMemcpyAsync(h->ws + q0, st, bytes, hipMemcpyHostToDevice, h->stream)) != hipSuccess)
         return hip_fail(h, e, "queue upload");
     if ((e = hipEventRecord(h->staging_evt[i], h->stream)) != hipSuccess) return hip_fail(h, e, "event record");
-    if ((e = hipEventRecord(h->upload_evt, h->stream)) != hipSuccess) return hip_fail(h, e, "event record");
+    mark_upload(h, h->stream);
     h->staging_pending[i] = true;
     h->staging_next = 1 - i;
     h->built = true;
@@ -447,31 +531,14 @@ PKV_API pkv_status pkv_build_queue_device(pkv_handle* h, const int32_t* ctx_lens
         return fail(h, PKV_ERR_INVALID_ARG, "null or misaligned ctx_lens");
     if (h->r.order != PKV_ORDER_CANONICAL) return fail(h, PKV_ERR_UNSUPPORTED, "device builder: canonical order only");
     if (h->r.persistent) return fail(h, PKV_ERR_STATE, "the resident loop takes host-built queues");
-    BuildParams p;
-    memset(&p, 0, sizeof(p));
-    p.ctx_lens = ctx_lens_device;
-    p.qhdr = reinterpret_cast<QHdr*>(h->ws + h->lay.queue_off);
-    p.n_chunks = reinterpret_cast<int32_t*>(h->ws + h->lay.n_chunks_off);
-    p.part_off = reinterpret_cast<int32_t*>(h->ws + h->lay.part_off_off);
-    p.row_len = reinterpret_cast<int32_t*>(h->ws + h->lay.row_len_off);
-    p.merge_rows = reinterpret_cast<int32_t*>(h->ws + h->lay.merge_rows_off);
-    p.items = reinterpret_cast<Item*>(h->ws + h->lay.items_off);
-    p.ctrl = reinterpret_cast<Ctrl*>(h->ws + h->lay.ctrl_off);
-    p.host_error = h->host_err_dev;
-    p.batch = batch;
-    p.hkv = h->r.hkv;
-    p.num_cus = h->r.num_cus;
-    p.chunk = h->r.chunk;
-    p.policy = h->r.policy;
-    p.max_items = h->r.max_items;
-    p.max_tokens = h->r.max_pages_per_seq * h->r.page;
+    const BuildParams p = build_params(h->r, h->lay, h->ws, ctx_lens_device, batch, h->host_err_dev);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (s != h->stream && (e = hipStreamWaitEvent(s, h->upload_evt, 0)) != hipSuccess)
+    if ((e = after_upload(h, s)) != hipSuccess || (e = after_readers(h, s)) != hipSuccess)
         return hip_fail(h, e, "stream wait");
     int rc = launch_build_queue(p, s);
     if (rc != 0) return hip_fail(h, (hipError_t)rc, "build_queue launch");
-    if ((e = hipEventRecord(h->upload_evt, s)) != hipSuccess) return hip_fail(h, e, "event record");
+    mark_upload(h, s);
     h->built = true;
     h->built_on_device = true;
     h->batch = batch;
@@ -496,7 +563,9 @@ PKV_API pkv_status pkv_decode(pkv_handle* h, const pkv_tensors* t, void* stream)
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (st != h->stream && (e = hipStreamWaitEvent(st, h->upload_evt, 0)) != hipSuccess)
+    // after the queue's upload, and after the previous decode (the control
+    // words and partial states are shared by every launch of the handle)
+    if ((e = after_upload(h, st)) != hipSuccess || (e = after_readers(h, st)) != hipSuccess)
         return hip_fail(h, e, "stream wait");
     const DecodeParams p = make_params(h, t);
     if (h->ev_before && (e = hipEventRecord(h->ev_before, st)) != hipSuccess) return hip_fail(h, e, "event record");
@@ -508,6 +577,7 @@ PKV_API pkv_status pkv_decode(pkv_handle* h, const pkv_tensors* t, void* stream)
         rc = launch_merge(p, h->r.d, h->r.g, merge_rows, st);
         if (rc != 0) return hip_fail(h, (hipError_t)rc, "merge launch");
     }
+    mark_readers(h, st);
     return PKV_OK;
 }
 
@@ -625,8 +695,10 @@ PKV_API pkv_status pkv_queue_read(pkv_handle* h, void* host_dst, size_t capacity
     *written = 0;
     if (h->r.persistent) return fail(h, PKV_ERR_STATE, "pkv_queue_read needs a one-shot handle");
     if (capacity > 0 && !host_dst) return fail(h, PKV_ERR_INVALID_ARG, "null host_dst");
-    hipError_t e = hipStreamSynchronize(h->stream);
-    if (e != hipSuccess) return hip_fail(h, e, "stream sync");
+    // the last write, on whichever stream it was enqueued
+    hipError_t e = hipEventRecord(h->upload_evt, h->upload_stream);
+    if (e == hipSuccess) e = hipEventSynchronize(h->upload_evt);
+    if (e != hipSuccess) return hip_fail(h, e, "event sync");
     QHdr qh;
     e = hipMemcpy(&qh, h->ws + h->lay.queue_off, sizeof(qh), hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(h, e, "queue header read");
@@ -653,11 +725,12 @@ PKV_API pkv_status pkv_debug_gather(pkv_handle* h, const pkv_tensors* t, int32_t
     if (item_index < 0) return fail(h, PKV_ERR_INVALID_ARG, "negative item index");
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (st != h->stream && (e = hipStreamWaitEvent(st, h->upload_evt, 0)) != hipSuccess)
+    if ((e = after_upload(h, st)) != hipSuccess || (e = after_readers(h, st)) != hipSuccess)
         return hip_fail(h, e, "stream wait");
     const DecodeParams p = make_params(h, t);
     int rc = launch_debug_gather(p, h->r.d, h->r.kv_dtype, item_index, k_out, v_out, st);
     if (rc != 0) return hip_fail(h, (hipError_t)rc, "gather launch");
+    mark_readers(h, st);
     return PKV_OK;
 }
 
@@ -670,6 +743,7 @@ PKV_API pkv_status pkv_destroy(pkv_handle* h) {
         if (h->staging[i]) (void)hipHostFree(h->staging[i]);
     }
     if (h->upload_evt) (void)hipEventDestroy(h->upload_evt);
+    if (h->consumed_evt) (void)hipEventDestroy(h->consumed_evt);
     if (h->host_err) (void)hipHostFree(h->host_err);
     delete h;
     return PKV_OK;

@@ -219,6 +219,14 @@ struct BuildParams {
     int32_t max_tokens;
 };
 
+// Kernel parameters over a workspace laid out by compute_layout (pkv_api.cpp).
+DecodeParams decode_params(const Resolved& r, const pkv_layout& lay, unsigned char* ws, const pkv_tensors* t,
+                           uint32_t* host_error);
+BuildParams build_params(const Resolved& r, const pkv_layout& lay, unsigned char* ws, const int32_t* ctx_lens,
+                         int32_t batch, uint32_t* host_error);
+// Validation of the caller's tensors against a config; PKV_OK or an error with *why.
+pkv_status check_tensor_args(const Resolved& r, const pkv_tensors* t, const char** why);
+
 // Launch wrappers (pkv_kernels.hip).  Return a hipError_t as int.
 int launch_init_ctrl(Ctrl* ctrl, uint32_t* arrive, int n_arrive, void* stream);
 int launch_zero(void* p, size_t bytes, void* stream);
@@ -231,5 +239,7 @@ bool supported_shape(int head_dim, int group);
 int launch_copy_probe(void* dst, const void* src, size_t bytes, int grid, void* stream);
 int launch_read_probe(const void* src, size_t bytes, void* sink, int grid, void* stream);
 int launch_resident(const LoopParams& lp, int head_dim, int group, int kv_dtype, int grid, void* stream);
+// Workgroups of the resident kernel that fit on one CU at once (registers, LDS, waves).
+int resident_occupancy(int head_dim, int group, int kv_dtype, int* blocks);
 
 }  // namespace pkv

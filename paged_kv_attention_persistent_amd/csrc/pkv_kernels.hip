@@ -1675,6 +1675,19 @@ int launch_resident(const LoopParams& lp, int head_dim, int group, int kv_dtype,
     PKV_DISPATCH(launch_resident_t, head_dim, group, lp, kv_dtype, grid, (hipStream_t)stream);
 }
 
+template <int D, int G>
+int resident_occupancy_t(int kv_dtype, int* blocks) {
+    *blocks = 0;
+    hipError_t e = kv_dtype == PKV_KV_F32
+        ? hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, resident_kernel<D, G, KvF32>, kThreads, 0)
+        : hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, resident_kernel<D, G, KvBf16>, kThreads, 0);
+    return (int)e;
+}
+
+int resident_occupancy(int head_dim, int group, int kv_dtype, int* blocks) {
+    PKV_DISPATCH(resident_occupancy_t, head_dim, group, kv_dtype, blocks);
+}
+
 int launch_decode(const DecodeParams& p, int head_dim, int group, int kv_dtype, int grid, void* stream) {
     PKV_DISPATCH(launch_decode_t, head_dim, group, p, kv_dtype, grid, (hipStream_t)stream);
 }

@@ -412,6 +412,34 @@ class SessionLoop:
         return int(self.ctx_lens(t).astype(np.int64).sum()) * self.layers * self.num_kv_heads \
             * self.head_dim * self.kv_elem_bytes * 2
 
+    def churn_lens(self, seed: int, life=(40, 120), join_lo: int = 2048, idle_prob: float = 0.0,
+                   idle=(1, 2)):
+        """Session churn over the slots (the Wave Persistent Kernel note's
+        sessions joining and leaving at step boundaries): each slot hosts a
+        sequence of sessions with lifetimes U[life] steps; when one leaves,
+        the slot may stay empty (context 0) for U[idle] steps with probability
+        idle_prob, then the next session joins with a fresh context drawn
+        from [min(join_lo, L0_s), L0_s], so that it fits the pages the slot
+        owns (L0_s + steps tokens).  The slot's first session is the loop's
+        own (context L0_s + t).  Returns (lens int32 [steps][sessions], joins)."""
+        rng = np.random.default_rng([seed, 9])
+        lens = np.zeros((self.steps, self.sessions), dtype=np.int32)
+        joins = 0
+        for s in range(self.sessions):
+            cap = int(self.l0[s])
+            t, L0 = 0, cap
+            while t < self.steps:
+                n = int(rng.integers(life[0], life[1] + 1))
+                for u in range(t, min(self.steps, t + n)):
+                    lens[u, s] = L0 + (u - t)
+                t += n
+                if t < self.steps and idle_prob > 0 and rng.random() < idle_prob:
+                    t += int(rng.integers(idle[0], idle[1] + 1))      # the slot stays empty
+                if t < self.steps:
+                    L0 = int(rng.integers(min(join_lo, cap), cap + 1))
+                    joins += 1
+        return lens, joins
+
     def pools(self, which: str, device) -> torch.Tensor:
         """[layers][pages][Hkv][P][D] of kv_dtype (one stream per tensor name).
         With append, rows that hold no token before step 0 are NaN."""

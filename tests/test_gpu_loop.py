@@ -266,3 +266,69 @@ def test_loop_append_errors():
         assert e.value.status == pkv.PKV_ERR_STATE
     finally:
         lp.close()
+
+
+def oracle_unit_len(sl, t, layer, s, hk, L):
+    """The oracle over the first L tokens of a slot's pages (a session that
+    joined the slot reads the slot's cache from token 0)."""
+    G = sl.num_q_heads // sl.num_kv_heads
+    if L == 0:
+        return np.zeros((G, sl.head_dim)), np.full(G, -np.inf)
+    npg = -(-L // 16)
+    pages = sl.block_tables[layer, s, :npg]
+    ks = workloads.kv_host(sl.slabs("k", layer, pages, hk))[:, None]
+    vs = workloads.kv_host(sl.slabs("v", layer, pages, hk))[:, None]
+    qg = workloads.bits_u16(sl.query_unit(t, layer, s))[None, hk * G:(hk + 1) * G]
+    return pa.range_state(qg, ks, vs, np.arange(npg)[None], 0, 0, 0, L, sl.scale, 16)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "f32"])
+@pytest.mark.parametrize("variant", ["nosplit", "split"])
+def test_loop_session_churn_every_output(variant, kv):
+    """Sessions leave and join at step boundaries (the Wave Persistent Kernel
+    note, "Runtime and timing boundary"): a slot is reset to a new, shorter
+    context, or stays empty for a step or two, and the resident kernel keeps
+    running.  Every output of every step, layer and slot against the oracle
+    over the slot's first L tokens; empty slots must hold the neutral state."""
+    say("churn", variant, kv)
+    sl = workloads.session_loop(seed=31, sessions=6, layers=2, steps=30, lo=1, hi=150,
+                                num_q_heads=8, num_kv_heads=2, name="loop_churn", kv_dtype=kv)
+    lens, joins = sl.churn_lens(seed=32, life=(2, 7), join_lo=1, idle_prob=0.3)
+    assert joins >= 10 and (lens == 0).any()
+    shorter = sum(int(lens[t, s] < lens[t - 1, s]) for t in range(1, sl.steps) for s in range(sl.sessions))
+    assert shorter >= 5                                     # slots re-used with shorter contexts
+    kw = dict(policy=pkv.PKV_POLICY_NO_SPLIT) if variant == "nosplit" else \
+        dict(policy=pkv.PKV_POLICY_SPLIT, kv_chunk_tokens=32)
+    lp = Loop(sl, **kw)
+    try:
+        for t in range(sl.steps):
+            lp.dec.build_queue(lens[t])
+            pkv.pkv_decode(lp.dec.handle, lp.tensors(t), lp.stream)
+        st = lp.dec.query()
+        assert st["loop_out_epoch"] == sl.steps and st["loop_alive"] == 1
+    finally:
+        lp.close()
+    G = sl.num_q_heads // sl.num_kv_heads
+    o = lp.out.float().cpu().numpy().astype(np.float64)
+    l = lp.lse.cpu().numpy().astype(np.float64)
+    errs, lerrs = [], []
+    for t in range(sl.steps):
+        for layer in range(sl.layers):
+            for s in range(sl.sessions):
+                for hk in range(sl.num_kv_heads):
+                    L = int(lens[t, s])
+                    got_o = o[t, layer, s, hk * G:(hk + 1) * G]
+                    got_l = l[t, layer, s, hk * G:(hk + 1) * G]
+                    if L == 0:
+                        assert np.all(got_o == 0) and np.all(np.isneginf(got_l)), (t, layer, s)
+                        continue
+                    ro, rl = oracle_unit_len(sl, t, layer, s, hk, L)
+                    assert np.all(np.isfinite(got_o)), (t, layer, s, hk)
+                    errs.append(np.abs(got_o - ro).ravel())
+                    lerrs.append(np.abs(got_l - rl))
+    err = np.concatenate(errs)
+    lerr = np.concatenate(lerrs)
+    say(f"churn {variant} {kv}: {joins} joins, {len(errs)} units: max_abs={err.max():.3e} "
+        f"mean_abs={err.mean():.3e} lse_max={lerr.max():.3e}")
+    assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS
+    assert lerr.max() <= (1e-4 if kv == "f32" else MAX_ABS)

@@ -5,9 +5,12 @@ element within max-abs 2e-2 and mean-abs 2e-3 of the oracle, compared in
 float64 after widening the kernel's bf16 output; the same bounds apply to the
 fp32 LSE.  Queue bytes and gathered K/V bits must match exactly.
 
-Small cases compare every output; full-size workloads compare sampled
-(sequence, KV head) units, each recomputed by the oracle from pages
-regenerated on the CPU by the seeded generator.
+Every case compares every output: small cases, the full-size workloads
+(each (sequence, KV head) of the long context, the mixed batch and the
+many-short batch, with the oracle run once per workload and cache type on
+pools copied back from the seeded generator), and structured cases whose
+answer is known in closed form (q = 0 token counting, scores that force the
+online-softmax rescale).
 
 The same cases run with an fp32 KV cache (kv_dtype F32: the fp32 attention
 cache of the Wave Persistent Kernel note).  There the gathered K/V bits must
@@ -194,31 +197,243 @@ def test_tiny_workload_and_repeat_calls():
 
 # ------------------------------------------------------ full-size cases ----
 
-FULL = {"long": [(0, 0), (0, 5)], "mixed": [(b, (3 * b) % 8) for b in range(8)],
-        "short": [(0, 0), (17, 3), (63, 7)]}
+_ORACLE_CACHE = {}
+
+
+def host_inputs(run):
+    """The run's query and pools as host arrays (bf16 bits / fp32 values),
+    copied back from the device: they are the seeded generator's output
+    (its CPU and GPU bits are identical, tested below), not the HIP path's."""
+    return (workloads.bits_u16(run.q), workloads.kv_host(run.k.cpu()),
+            workloads.kv_host(run.v.cpu()))
+
+
+def oracle_every_unit(wl, run):
+    """The oracle over every (sequence, KV head) of a full-size workload,
+    computed once per (workload, cache type) and shared by the tests below."""
+    key = (wl.name, wl.kv_dtype)
+    if key not in _ORACLE_CACHE:
+        q, k, v = host_inputs(run)
+        say(f"oracle over every unit of {wl.name} ({wl.kv_dtype}): {wl.batch * wl.num_kv_heads} units")
+        _ORACLE_CACHE.clear()                 # one workload's pools at a time in host memory
+        _ORACLE_CACHE[key] = (pa.decode_attention(q, k, v, wl.block_table, wl.ctx_lens, wl.scale,
+                                                  wl.page_size), (q, k, v))
+    return _ORACLE_CACHE[key]
+
+
+COMBOS = [(merge, sched) for merge in (pkv.PKV_MERGE_FUSED, pkv.PKV_MERGE_SEPARATE)
+          for sched in SCHEDULES]
+
+
+@pytest.mark.parametrize("kv", KVS)
+@pytest.mark.parametrize("name", ["long", "mixed", "short"])
+def test_full_size_every_unit(name, kv):
+    """Every output of the full-size workloads against the oracle, for both
+    merges and both schedules (the oracle is computed once per workload)."""
+    wl = workloads.CONFIGS[name]().with_kv_dtype(kv)
+    run = Run(wl, poison=True)
+    (ro, rl), _ = oracle_every_unit(wl, run)
+    cus = run.dec.query()["num_cus"]
+    ref = wq.build_queue(wl.ctx_lens, wl.num_kv_heads, cus, 0)
+    run.close()
+    for merge, sched in COMBOS:
+        run = Run(wl, poison=True, merge_mode=merge, schedule=SCHEDULES[sched])
+        o, l = run.decode()
+        info = run.info
+        assert info.n_items == len(ref["items"]) and bool(info.split) == ref["split"]
+        check(o, l, ro, rl, f"{name} {kv} merge {merge} {sched}: all {wl.batch * wl.num_kv_heads} units",
+              lse_tol(wl))
+        run.close()
+
+
+@pytest.mark.parametrize("kv", KVS)
+def test_full_size_long_context_counts_every_token(kv):
+    """The long context at full size (131072 tokens, 32 ranges merged across
+    256 workgroups) with q = 0 on all 32 heads: every score is 0, so
+    LSE = ln 131072 to fp32 rounding, where one lost or repeated token moves
+    it by 7.6e-6 and one page by 1.2e-4; O is the exact mean of each V column
+    (bf16 rounding of an fp32 sum of unit-weight rows), V column 0 is set to
+    (t mod 256) / 256 and column 1 to 0.375, so O[.][1] must be 0.375 bit for
+    bit.  Both merges and both schedules."""
+    wl = workloads.CONFIGS["long"]().with_kv_dtype(kv)
+    L = int(wl.ctx_lens[0])
+    t = np.arange(L)
+    pg = torch.as_tensor(wl.block_table[0, t // 16].astype(np.int64))
+    row = torch.as_tensor(t % 16)
+    v = wl.pool("v", "cpu", poison=True)
+    v[pg, :, row, 0] = torch.as_tensor((t % 256) / 256.0, dtype=torch.float32).to(v.dtype)[:, None]
+    v[pg, :, row, 1] = 0.375
+    vh = workloads.kv_host(v)
+    q0 = np.zeros((1, wl.num_q_heads, wl.head_dim), dtype=np.uint16)       # +0.0 bits
+    G = wl.num_q_heads // wl.num_kv_heads
+    kz = np.zeros((1, wl.num_kv_heads, 16, wl.head_dim), dtype=vh.dtype)    # unused: q = 0
+    mean = np.zeros((wl.num_q_heads, wl.head_dim))
+    for hk in range(wl.num_kv_heads):
+        # q = 0: the oracle's state is the plain mean of the valid V rows
+        kk = np.broadcast_to(kz, (wl.num_pages, wl.num_kv_heads, 16, wl.head_dim))
+        o, lse = pa.range_state(q0, kk, vh, wl.block_table, 0, hk, 0, L, wl.scale, 16)
+        assert np.all(o[:, 1] == 0.375)
+        assert np.allclose(lse, np.log(L), rtol=0, atol=1e-12)
+        mean[hk * G:(hk + 1) * G] = o
+    vd = v.to("cuda")
+    for merge, sched in COMBOS:
+        run = Run(wl, poison=True, merge_mode=merge, schedule=SCHEDULES[sched])
+        run.q.zero_()
+        run.v = vd
+        o, l = run.decode()
+        where = f"long {kv} merge {merge} {sched}"
+        say(f"{where}: max |LSE - ln L| = {np.abs(l[0] - np.log(L)).max():.2e}, "
+            f"max |O - mean| = {np.abs(o[0] - mean).max():.2e}")
+        assert np.abs(l[0] - np.log(L)).max() <= 5e-6, where
+        assert np.all(o[0, :, 1] == 0.375), where
+        assert np.all(np.abs(o[0] - mean) <= 2.0 ** -8 * np.abs(mean) + 1e-5), where
+        run.close()
+
+
+@pytest.mark.parametrize("kv", KVS)
+@pytest.mark.parametrize("name", ["long", "short"])
+def test_full_size_gather_bits_match_oracle(name, kv):
+    """The decode kernel's own gather on items of the full-size queues, bit
+    for bit against the oracle's gather: the first, the last and items spread
+    over the queue (both ends of every sampled row)."""
+    wl = workloads.CONFIGS[name]().with_kv_dtype(kv)
+    run = Run(wl, poison=True)
+    run.dec.build_queue(wl.ctx_lens)
+    items, *_ = pkv.pkv_plan_queue(run.cfg, wl.ctx_lens)
+    _, k, v = host_inputs(run)
+    pick = sorted(set([0, len(items) - 1] + list(range(0, len(items), max(1, len(items) // 24)))))
+    for i in pick:
+        it = items[i]
+        n = int(it["tok_end"] - it["tok_begin"])
+        ko = torch.zeros(n, wl.head_dim, dtype=wl.kv_torch_dtype, device="cuda")
+        vo = torch.zeros_like(ko)
+        pkv.pkv_debug_gather(run.dec.handle, run.tensors(), int(i), ko, vo, run.dec.stream)
+        torch.cuda.synchronize()
+        args = (wl.block_table, int(it["seq"]), int(it["kv_head"]), int(it["tok_begin"]),
+                int(it["tok_end"]), 16)
+        rk, rv = pa.gather_tokens(k, *args), pa.gather_tokens(v, *args)
+        gk, gv = workloads.kv_host(ko), workloads.kv_host(vo)
+        assert gk.dtype == rk.dtype and gk.tobytes() == rk.tobytes(), f"{name} K item {i}"
+        assert gv.dtype == rv.dtype and gv.tobytes() == rv.tobytes(), f"{name} V item {i}"
+    say(f"{name} {kv}: gather of {len(pick)} of {len(items)} items bit-exact")
+    run.close()
+
+
+# ------------------------------------------ online-softmax rescale cases ----
+
+def _sign_pattern(d):
+    """A fixed +-1 vector (bf16-exact): q = s_h u and K_t = r_t u make every
+    dot product an exact sum of equal terms, D r_t s_h."""
+    return np.where((np.arange(d) * 7 + 3) % 5 < 2, 1.0, -1.0)
+
+
+def scored_workload(kind, kv, d=128, hq=8, hkv=2, lens=None):
+    """Inputs whose scores force the running maximum up after the first tile.
+
+    rising: K_t = r_t u with r_t = alpha * frac((t + 1) / period) rounded to
+    bf16, per row a different period (the whole row, one 1024-token range,
+    300 tokens), so scores climb by up to ~65 log2 units inside every range
+    and every 8-lane group's tokens, in steps that exceed the lazy-rescale
+    threshold many times.  peaked: random K, and one token per row with
+    K = kappa u scoring ~30 nats (~43 log2 units above the rest) for the
+    group's first head: on the last valid row of a partial last page, at the
+    first token of a middle range, or mid-row.  The query heads of a group are
+    u scaled by 1, 1/2, 3/4 and 5/4."""
+    if lens is None:
+        lens = [5000, 4099, 1030, 17, 2049, 300]
+    wl = workloads.custom(f"scores_{kind}", lens, hq, hkv, d, spare_pages=3, kv_dtype=kv)
+    G = hq // hkv
+    u = _sign_pattern(d)
+    hs = np.array([1.0, 0.5, 0.75, 1.25])[np.arange(G) % 4]
+    q = np.zeros((wl.batch, hq, d), dtype=np.float32)
+    for h in range(hq):
+        q[:, h] = u * hs[h % G]
+    k = wl.pool("k", "cpu", poison=True)
+    base = float(wl.scale * d)                      # score of r_t = 1 for s_h = 1, nats
+    for b, L in enumerate(lens):
+        if L == 0:
+            continue
+        t = np.arange(L)
+        pg = torch.as_tensor(wl.block_table[b, t // 16].astype(np.int64))
+        row = torch.as_tensor(t % 16)
+        if kind == "rising":
+            period = [L, 1024, 300][b % 3]
+            r = (45.0 / base) * (((t % period) + 1) / period)
+            kt = torch.as_tensor(r[:, None] * u[None, :], dtype=torch.float32)
+            kt = kt.to(torch.bfloat16).to(k.dtype)          # bf16-exact in both caches
+            k[pg, :, row, :] = kt[:, None, :]
+        else:
+            peak = {0: L - 1, 1: 2048, 2: L - 1, 3: 16, 4: 1024, 5: L // 2}[b % 6]
+            peak = min(peak, L - 1)
+            kt = torch.as_tensor((30.0 / base) * u, dtype=torch.float32).to(torch.bfloat16).to(k.dtype)
+            k[int(wl.block_table[b, peak // 16]), :, peak % 16, :] = kt
+    qt = torch.as_tensor(q).to(torch.bfloat16)
+    return wl, qt, k
 
 
 @pytest.mark.parametrize("sched", list(SCHEDULES))
 @pytest.mark.parametrize("kv", KVS)
-@pytest.mark.parametrize("merge", [pkv.PKV_MERGE_FUSED, pkv.PKV_MERGE_SEPARATE],
-                         ids=["fused_merge", "separate_merge"])
-@pytest.mark.parametrize("name", ["long", "mixed", "short"])
-def test_full_size_sampled_units(name, merge, kv, sched):
-    say("full", name, "kv", kv, "schedule", sched)
-    wl = workloads.CONFIGS[name]().with_kv_dtype(kv)
-    run = Run(wl, poison=True, merge_mode=merge, schedule=SCHEDULES[sched])
-    o, l = run.decode()
-    info = run.info
-    ref = wq.build_queue(wl.ctx_lens, wl.num_kv_heads, run.dec.query()["num_cus"], 0)
-    assert info.n_items == len(ref["items"]) and bool(info.split) == ref["split"]
-    qb = workloads.bits_u16(run.q)
-    G = wl.num_q_heads // wl.num_kv_heads
-    for b, hk in FULL[name]:
-        ro, rl = oracle_unit(wl, qb, b, hk)
-        check(o[b, hk * G:(hk + 1) * G], l[b, hk * G:(hk + 1) * G], ro, rl, f"{name} {kv} b={b} hk={hk}",
-              lse_tol(wl))
-    # every output finite: no stray read of a poisoned slot anywhere
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+@pytest.mark.parametrize("kind", ["rising", "peaked"])
+def test_online_softmax_rescale_cases(kind, kv, sched):
+    """Scores that rise past the running maximum inside a range, on a state
+    that already holds tokens, so that the lazy rescale of l and acc runs
+    (PersistentKV page, Methodology 1 "Sequence Splitting": the partial
+    online-softmax state).  Every output against the oracle, split (both
+    merges) and unsplit, D = 128 / G = 4 and D = 64 / G = 8."""
+    for d, hq, hkv, lens in ((128, 8, 2, None), (64, 16, 2, [3000, 700, 33])):
+        wl, q, k = scored_workload(kind, kv, d, hq, hkv, lens)
+        ro, rl = pa.decode_attention(workloads.bits_u16(q), workloads.kv_host(k),
+                                     workloads.kv_host(wl.pool("v", "cpu", poison=True)),
+                                     wl.block_table, wl.ctx_lens, wl.scale, wl.page_size)
+        say(f"{kind} d={d}: oracle LSE range {rl.min():.2f} .. {rl.max():.2f}")
+        kd = k.to("cuda")
+        qd = q.to("cuda")
+        for policy, chunk, merge in ((pkv.PKV_POLICY_SPLIT, 1024, pkv.PKV_MERGE_FUSED),
+                                     (pkv.PKV_POLICY_SPLIT, 1024, pkv.PKV_MERGE_SEPARATE),
+                                     (pkv.PKV_POLICY_NO_SPLIT, 0, pkv.PKV_MERGE_FUSED)):
+            run = Run(wl, policy=policy, kv_chunk_tokens=chunk, merge_mode=merge,
+                      schedule=SCHEDULES[sched])
+            run.k, run.q = kd, qd
+            o, l = run.decode()
+            check(o, l, ro, rl, f"{kind} {kv} {sched} d={d} policy {policy} merge {merge}", lse_tol(wl))
+            run.close()
+
+
+# ------------------------------------------------ streams and ordering ----
+
+def test_queue_rebuilds_and_decodes_on_other_streams_stay_ordered():
+    """Queue builds (host uploads on the handle's stream, device builds on a
+    third stream) alternate with decodes on a second stream, with no host
+    synchronisation in between: each decode must read the queue built just
+    before it, and no build may overwrite a queue a decode still reads."""
+    base = [60000, 300, 41, 5000, 0, 777]
+    wl = workloads.custom("streams", base, 8, 2, 128, spare_pages=2)
+    run = Run(wl, poison=True, policy=pkv.PKV_POLICY_SPLIT, kv_chunk_tokens=1024)
+    s_dec, s_build = torch.cuda.Stream(), torch.cuda.Stream()
+    rng = np.random.default_rng(5)
+    plans, outs, dev_lens = [], [], []
+    for i in range(10):
+        lens = np.minimum(rng.integers(0, 4 * np.asarray(base) // 3 + 1), base).astype(np.int32)
+        lens[0] = base[0] - 997 * i                 # a long row keeps every decode busy
+        plans.append(lens)
+        dev_lens.append(torch.as_tensor(lens).to("cuda"))
+        outs.append((torch.full_like(run.out, float("nan")), torch.full_like(run.lse, float("nan"))))
+    torch.cuda.synchronize()                        # inputs in place; no host sync from here on
+    for i, lens in enumerate(plans):
+        if i % 2 == 0:
+            run.dec.build_queue(lens)
+        else:
+            pkv.pkv_build_queue_device(run.dec.handle, dev_lens[i], s_build)
+        o, lse = outs[i]
+        t = pkv.make_tensors(run.q, run.k, run.v, run.bt, run.lens, o, lse)
+        pkv.pkv_decode(run.dec.handle, t, s_dec)
+    torch.cuda.synchronize()
+    assert run.dec.query()["error_code"] == 0
+    q, k, v = host_inputs(run)
+    for i, (lens, (o, lse)) in enumerate(zip(plans, outs)):
+        ro, rl = pa.decode_attention(q, k, v, wl.block_table, lens, wl.scale, 16)
+        check(o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+              ro, rl, f"call {i} ({'host' if i % 2 == 0 else 'device'} build)")
     run.close()
 
 
