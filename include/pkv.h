@@ -407,6 +407,28 @@ PKV_API pkv_status pkv_queue_read(pkv_handle* h, void* host_dst, size_t capacity
 PKV_API pkv_status pkv_debug_gather(pkv_handle* h, const pkv_tensors* t, int32_t item_index,
                                     void* k_out, void* v_out, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * one-shot decode of pkv_build_queue_device + pkv_decode in one call, with
+ * no handle and no workspace.  Its scratch (control words, queue, partial
+ * states, counters) is a fixed 16 MiB array in the library's device memory,
+ * one per device, held until the process ends; configs whose workspace
+ * (pkv_workspace_size) exceeds 16 MiB get PKV_ERR_CAPACITY.  Enqueues on
+ * stream, in order: a clear of the scratch's control words, the device queue
+ * builder over ctx_lens_device (int32 [batch], device memory), the decode
+ * kernel and, with a separate merge, the merge kernel.  Allocates nothing
+ * (no hipMalloc, no library allocation, no memset).  cfg as for pkv_create
+ * (persistent = 0 and the canonical order only, else PKV_ERR_UNSUPPORTED;
+ * batch <= 4096); t as for pkv_decode, with t->batch == batch.  error_word
+ * (nullable; device or mapped host memory, 4-byte aligned, owned by the
+ * caller) receives a PKV_DEVERR_* code when the device finds a block-table
+ * entry outside the pool or a bad length; the library never clears it.
+ * Every call on a device shares that device's scratch and leaves it in
+ * place: calls that overlap on one device (other streams, other threads)
+ * race and must be ordered by the caller. */
+PKV_API pkv_status pkv_decode_noalloc(const pkv_config* cfg, const int32_t* ctx_lens_device, int32_t batch,
+                                      const pkv_tensors* t, uint32_t* error_word, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpkv.so")
-SOURCES = ["pkv_kernels.hip", "pkv_api.cpp", "queue_plan.cpp"]
+SOURCES = ["pkv_kernels.hip", "pkv_api.cpp", "queue_plan.cpp", "pkv_noalloc.hip"]
 ARCH = "gfx950"
 
 

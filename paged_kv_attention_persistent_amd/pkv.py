@@ -123,6 +123,8 @@ SIGNATURES = {
     "pkv_loop_free_pages": (C.c_int32, [C.c_void_p, C.POINTER(C.c_int32)]),
     "pkv_copy_probe": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int32, C.c_void_p]),
     "pkv_read_probe": (C.c_int32, [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int32, C.c_void_p]),
+    "pkv_decode_noalloc": (C.c_int32, [C.POINTER(pkv_config), C.c_void_p, C.c_int32,
+                                       C.POINTER(pkv_tensors), C.c_void_p, C.c_void_p]),
 }
 
 _LIB = None
@@ -345,6 +347,15 @@ def pkv_read_probe(src, nbytes: int, sink, grid: int = 0, stream=None) -> None:
     """sink: a device int32 tensor of at least grid * 256 elements."""
     _check(lib().pkv_read_probe(C.c_void_p(src.data_ptr()), int(nbytes), C.c_void_p(sink.data_ptr()),
                                 int(grid), C.c_void_p(_stream_ptr(stream))), "pkv_read_probe")
+
+
+def pkv_decode_noalloc(cfg: pkv_config, ctx_lens_dev, tensors: pkv_tensors, error_word=None,
+                       stream=None) -> None:
+    """Decode with the library's static scratch (no workspace, no handle)."""
+    ew = C.c_void_p(error_word.data_ptr()) if error_word is not None else C.c_void_p(None)
+    _check(lib().pkv_decode_noalloc(C.byref(cfg), C.c_void_p(ctx_lens_dev.data_ptr()),
+                                    int(ctx_lens_dev.numel()), C.byref(tensors), ew,
+                                    C.c_void_p(_stream_ptr(stream))), "pkv_decode_noalloc")
 
 
 class PagedDecoder:
