@@ -405,12 +405,18 @@ def kernel_code_digest(path):
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
-def measured_traffic(root, kv="bf16"):
-    """HBM bytes per decode launch of the long context from the committed
-    counter summary, if it was taken on the kernel code as it is now (else
-    None)."""
+PROFILE_NAMES = {"long": "decode_kernel_long_context", "mixed": "decode_kernel_mixed_batch",
+                 "short": "decode_kernel_many_short"}
+
+
+def measured_traffic(root, workload="long", kv="bf16"):
+    """HBM bytes per decode launch of a workload from its committed counter
+    summary, if the counters were taken on the kernel code as it is now
+    (else None)."""
     import re
-    name = "decode_kernel_long_context" + ("_fp32_cache" if kv == "f32" else "") + "_traffic.md"
+    if workload not in PROFILE_NAMES:
+        return None
+    name = PROFILE_NAMES[workload] + ("_fp32_cache" if kv == "f32" else "") + "_traffic.md"
     prof = os.path.join(root, "profiles", name)
     src = os.path.join(root, "paged_kv_attention_persistent_amd", "csrc", "pkv_kernels.hip")
     try:
@@ -746,6 +752,7 @@ def main():
                        args.order, args.wg_per_cu, args.copies, not args.no_gate, say, args.merge, sched)
         others[name] = {k: r[k] for k in keys}
         others[name]["pct_of_hbm_peak"] = 100.0 * r["gbs"] / HBM_PEAK_GBS
+        others[name]["traffic"] = measured_traffic(os.path.dirname(os.path.abspath(__file__)), name)
         say(f"{name}: {r['gbs']:.1f} GB/s per step ({r['ms_per_step'] * 1e3:.2f} us, chunk {r['chunk_tokens']})")
         if name == "mixed":
             # the configuration's stated range length, beside the fitted one
@@ -766,8 +773,7 @@ def main():
                            sched, kv="f32")
             f32[name] = {k: r[k] for k in keys if k != "split"}
             f32[name]["pct_of_hbm_peak"] = 100.0 * r["gbs"] / HBM_PEAK_GBS
-            if name == "long":
-                f32[name]["traffic"] = measured_traffic(os.path.dirname(os.path.abspath(__file__)), "f32")
+            f32[name]["traffic"] = measured_traffic(os.path.dirname(os.path.abspath(__file__)), name, "f32")
             say(f"{name} (fp32 cache): {r['gbs']:.1f} GB/s per step ({r['ms_per_step'] * 1e3:.1f} us)")
     loop = loop_append = loop_f32 = None
     if args.loop_steps > 0:
@@ -821,8 +827,8 @@ def main():
         # launch stream (one launch per step with the fused merge)
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__)), args.kv)
-                     if args.workload == "long" else None,
+                     "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__)), args.workload,
+                                                 args.kv),
                      "kernel": f"decode_kernel<128,4,{'KvF32' if args.kv == 'f32' else 'KvBf16'}>",
                      "kernel_us_mean": round(main_res["ms_per_step"] * 1e3, 3) if one_launch else None,
                      "bytes_per_launch": main_res["kv_bytes"],
