@@ -35,7 +35,8 @@ Readings taken where the page is silent:
 * Ranges are fixed chunks from token 0: chunk c covers
   [c * C, min(L_b, (c + 1) * C)).
 * Item encoding, 16 bytes little-endian:
-  u32 seq, u16 kv_head, u16 chunk, u32 tok_begin, u32 tok_end.
+  u32 seq, u16 kv_head, u16 chunk, u32 tok_begin, u32 tok_end.  A row that
+  would need more than 65535 ranges cannot be encoded and is an error.
 * n_chunks[b] = 0 for an empty row, ceil(L_b / C) for a split row, else 1.
 * part_off[b] is the exclusive prefix sum over rows of n_chunks[b] counted
   only where n_chunks[b] > 1 (rows that need a merge own partial slots);
@@ -131,6 +132,8 @@ def build_queue(ctx_lens, num_kv_heads: int, num_cus: int, chunk_tokens: int,
             n_chunks[b] = -(-L // chunk_tokens)          # ceil(L / C)
         else:
             n_chunks[b] = 1
+        if n_chunks[b] > 65535:                          # the item's range index is 16 bits
+            raise ValueError(f"row {b} needs {n_chunks[b]} ranges; an item encodes at most 65535")
 
     part_off = np.zeros(bsz + 1, dtype=np.int32)
     for b in range(bsz):

@@ -203,7 +203,9 @@ pkv_status plan_queue(const Resolved& r, const int32_t* ctx_lens, int32_t batch,
     part_off[0] = 0;
     for (int b = 0; b < batch; ++b) {
         const int64_t L = ctx_lens[b];
-        const int32_t nc = L == 0 ? 0 : (split ? (int32_t)((L + chunk - 1) / chunk) : 1);
+        const int64_t nc64 = L == 0 ? 0 : (split ? (L + chunk - 1) / chunk : 1);
+        if (nc64 > 65535) { *why = "a row needs more than 65535 ranges (16-bit range index)"; return PKV_ERR_CAPACITY; }
+        const int32_t nc = (int32_t)nc64;
         n_chunks[b] = nc;
         if (row_len) row_len[b] = (int32_t)L;
         part_off[b + 1] = part_off[b] + (nc > 1 ? nc : 0);

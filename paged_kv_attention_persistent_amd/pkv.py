@@ -14,7 +14,9 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libpkv.so")
+# PKV_LIBRARY names another build of the same library to load instead of the
+# in-tree one (a sanitizer build, for instance); it must exist like the default.
+LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(HERE, "libpkv.so")
 
 PKV_OK = 0
 PKV_ERR_INVALID_ARG = -1

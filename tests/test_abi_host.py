@@ -252,3 +252,19 @@ def test_traffic_record_follows_kernel_code_not_comments(tmp_path):
     import os
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     assert bench.measured_traffic(root) is None or bench.measured_traffic(root) > 536870912
+
+
+def test_configs_whose_rows_could_need_more_than_65535_ranges_are_refused():
+    # the item's range index is a 16-bit field: a config is refused when its
+    # longest row at its range length would need more than 65535 ranges
+    cfg = pkv.make_config(4, 1, 128, 64, 1, 65535, policy=pkv.PKV_POLICY_SPLIT, kv_chunk_tokens=16,
+                          num_cus=256, max_items=70000)
+    items, n_chunks, *_ = pkv.pkv_plan_queue(cfg, [65535 * 16])
+    assert n_chunks[0] == 65535 and int(items["chunk"].max()) == 65534
+    ref = wq.build_queue([65535 * 16], 1, 256, 16, wq.POLICY_SPLIT)
+    assert items.tobytes() == ref["items"].tobytes()
+    big = pkv.make_config(4, 1, 128, 64, 1, 65536, policy=pkv.PKV_POLICY_SPLIT, kv_chunk_tokens=16,
+                          num_cus=256, max_items=70000)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_workspace_size(big)
+    assert e.value.status == pkv.PKV_ERR_CAPACITY

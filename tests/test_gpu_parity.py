@@ -604,6 +604,31 @@ def test_bad_block_table_entry_is_reported_not_read():
     run.close()
 
 
+def test_device_builder_reports_bad_lengths_in_the_error_word():
+    """The device queue builder checks every length before it writes a queue:
+    a length beyond max_pages_per_seq pages sets PKV_DEVERR_BAD_ITEM with the
+    row as detail and leaves an empty queue (nothing is read: the builder
+    touches only the lengths); pkv_query reports it and pkv_clear_error makes
+    the handle usable again."""
+    cfg = pkv.make_config(4, 1, 128, 64, 4, 100, policy=pkv.PKV_POLICY_SPLIT, kv_chunk_tokens=256,
+                          num_cus=256)
+    dec = pkv.PagedDecoder(cfg)
+    for lens, row in (([5, 100 * 16 + 1, 7], 1), ([3, 9, 1600, -1], 3)):
+        dec.build_queue_device(torch.as_tensor(np.asarray(lens, dtype=np.int32)).cuda())
+        torch.cuda.synchronize()
+        st = dec.query(raise_on_fault=False)
+        assert st["status"] == pkv.PKV_ERR_DEVICE_FAULT, lens
+        assert st["error_code"] == pkv.PKV_DEVERR_BAD_ITEM and st["error_detail"] == row, (lens, st)
+        assert st["n_items"] == 0
+        pkv.pkv_clear_error(dec.handle)
+    lens = [5, 100 * 16, 7, 0]
+    dec.build_queue_device(torch.as_tensor(np.asarray(lens, dtype=np.int32)).cuda())
+    torch.cuda.synchronize()
+    st = dec.query()
+    assert st["error_code"] == 0 and st["n_items"] == len(wq.build_queue(lens, 1, 256, 256, 2)["items"])
+    dec.close()
+
+
 def test_argument_errors_enqueue_nothing():
     wl = workloads.tiny()
     run = Run(wl)

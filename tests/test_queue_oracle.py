@@ -185,3 +185,11 @@ def test_fit_mode_brute_force_small_grids():
                 assert len(got) <= max(max(1, cus // hkv) * hkv, sum(1 for L in lens if L) * hkv)
                 if C > 1024:  # chosen by the bound, not the floor: one page less would not fit
                     assert sum(-(-(-(-L // 16)) // (C // 16 - 1)) for L in lens) > max(1, cus // hkv)
+
+
+def test_a_row_needing_more_than_65535_ranges_is_an_error():
+    # the item's range index is a 16-bit field: 65535 ranges encode, 65536 do not
+    ok = wq.build_queue([65535 * 16], 1, 256, 16, wq.POLICY_SPLIT)
+    assert ok["n_chunks"][0] == 65535 and int(ok["items"]["chunk"].max()) == 65534
+    with pytest.raises(ValueError):
+        wq.build_queue([65535 * 16 + 1], 1, 256, 16, wq.POLICY_SPLIT)
