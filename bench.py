@@ -44,9 +44,10 @@ def parse():
     ap.add_argument("--order", default="canonical", choices=["canonical", "lpt"])
     ap.add_argument("--wg-per-cu", type=int, default=0)
     ap.add_argument("--merge", default="fused", choices=["fused", "separate"])
-    ap.add_argument("--schedule", default="atomic", choices=["atomic", "static", "pages"],
+    ap.add_argument("--schedule", default="atomic", choices=["atomic", "static", "pages", "steal"],
                     help="item assignment of the one-shot launches (pages: split rows' pages "
-                         "claimed from a shared cursor)")
+                         "claimed from a shared cursor; steal: a quarter of each range in a "
+                         "pool the row's waves drain)")
     ap.add_argument("--copies", type=int, default=2)
     ap.add_argument("--no-gate", action="store_true")
     ap.add_argument("--loop-steps", type=int, default=200,
@@ -512,8 +513,8 @@ def measure_bucketed(torch, pkv, workloads, name, steps, warmup, say):
 
 
 def ablations(torch, pkv, workloads, args, say):
-    """Scheduling ablations (static vs atomic item assignment vs page claims;
-    exact-length bucketed launches vs the compact queue) on the one-shot
+    """Scheduling ablations (static vs atomic item assignment vs page claims vs
+    the steal pool; exact-length bucketed launches vs the compact queue) on the one-shot
     workloads, with both cache types for the assignment."""
     res = {"schedule": {}, "bucketed": {}}
     steps = max(args.steps // 2, 10)
@@ -521,14 +522,14 @@ def ablations(torch, pkv, workloads, args, say):
         for name in ("long", "mixed", "short"):
             row = {}
             for label, sched in (("atomic", pkv.PKV_SCHEDULE_ATOMIC), ("static", pkv.PKV_SCHEDULE_STATIC),
-                                 ("pages", pkv.PKV_SCHEDULE_PAGES)):
+                                 ("pages", pkv.PKV_SCHEDULE_PAGES), ("steal", pkv.PKV_SCHEDULE_STEAL)):
                 r, _ = measure(torch, pkv, workloads, name, steps, args.warmup, args.order, args.wg_per_cu,
                                args.copies, not args.no_gate, say, args.merge, sched, kv=kv)
                 row[label] = {"gbs": round(r["gbs"], 1), "us_per_step": round(r["ms_per_step"] * 1e3, 2)}
             key = name if kv == "bf16" else f"{name}_f32"
             res["schedule"][key] = row
             say(f"ablation {key}: atomic {row['atomic']['gbs']} GB/s, static {row['static']['gbs']} GB/s, "
-                f"page claims {row['pages']['gbs']} GB/s")
+                f"page claims {row['pages']['gbs']} GB/s, steal pool {row['steal']['gbs']} GB/s")
     for name in ("mixed", "short"):
         r, _ = measure(torch, pkv, workloads, name, steps, args.warmup, args.order, args.wg_per_cu,
                        args.copies, False, say, args.merge)
@@ -697,7 +698,7 @@ def profile_pass(torch, pkv, workloads, args, say):
                           wl.max_pages_per_seq, scale=wl.scale,
                           kv_dtype=pkv.PKV_KV_F32 if args.kv == "f32" else pkv.PKV_KV_BF16,
                           schedule={"atomic": pkv.PKV_SCHEDULE_ATOMIC, "static": pkv.PKV_SCHEDULE_STATIC,
-                                    "pages": pkv.PKV_SCHEDULE_PAGES}[args.schedule],
+                                    "pages": pkv.PKV_SCHEDULE_PAGES, "steal": pkv.PKV_SCHEDULE_STEAL}[args.schedule],
                           merge_mode=pkv.PKV_MERGE_SEPARATE if args.merge == "separate" else pkv.PKV_MERGE_FUSED)
     dec = pkv.PagedDecoder(cfg)
     info = dec.build_queue(wl.ctx_lens)
@@ -739,7 +740,7 @@ def main():
         profile_pass(torch, pkv, workloads, args, say)
         return
     sched = {"atomic": pkv.PKV_SCHEDULE_ATOMIC, "static": pkv.PKV_SCHEDULE_STATIC,
-             "pages": pkv.PKV_SCHEDULE_PAGES}[args.schedule]
+             "pages": pkv.PKV_SCHEDULE_PAGES, "steal": pkv.PKV_SCHEDULE_STEAL}[args.schedule]
     main_res, wl = measure(torch, pkv, workloads, args.workload, args.steps, args.warmup,
                            args.order, args.wg_per_cu, args.copies, not args.no_gate, say, args.merge,
                            sched, kv=args.kv)

@@ -96,9 +96,20 @@ enum { PKV_ORDER_CANONICAL = 0, PKV_ORDER_LPT = 1 };
  * 48 KiB of K+V at D = 128) from a cursor shared by the row's items, so
  * faster workgroups take more of the row; each item still yields one partial
  * state and the merge is the same exact merge (over disjoint page sets).
- * Outputs agree with the other schedules to rounding, not bit for bit.  The
- * resident loop always claims items (ATOMIC). */
-enum { PKV_SCHEDULE_ATOMIC = 0, PKV_SCHEDULE_STATIC = 1, PKV_SCHEDULE_PAGES = 2 };
+ * Outputs agree with the other schedules to rounding, not bit for bit.
+ * STEAL: items are claimed as in ATOMIC and each item of a split (row, KV
+ * head) reads its own range, except the first quarter of every range
+ * (rounded down to whole rounds of 8 waves x 3 pages, full pages only): those
+ * pages form the row's shared pool, which the waves of the row's items drain
+ * 3 pages per claim once their own pages are done (wave w takes the pool
+ * pages congruent to w modulo 8, from a cursor per (row, KV head, wave)), so
+ * the row's items end close together whichever XCD runs them.  The pages are
+ * still read once each and merged exactly; outputs agree with the other
+ * schedules to rounding.  The PersistentKV page names work assignment as a
+ * deciding variable beside the attention arithmetic (Technical Summary,
+ * "Significance and Claims"); these schedules are measured as an ablation.  The resident loop always claims
+ * items (ATOMIC). */
+enum { PKV_SCHEDULE_ATOMIC = 0, PKV_SCHEDULE_STATIC = 1, PKV_SCHEDULE_PAGES = 2, PKV_SCHEDULE_STEAL = 3 };
 
 /* Element type of the KV cache.  BF16: 2-byte values.  F32: 4-byte values,
  * as in the fp32 attention cache of the text-to-speech model on the WPK note
@@ -217,7 +228,8 @@ typedef struct pkv_layout {
     uint64_t partial_lse_off;   /* fp32 [layers][max_items][G], natural-log partial LSE */
     uint64_t arrive_off;        /* uint32 [layers][max_batch][Hkv] arrival counters of the fused merge */
     uint64_t cursor_off;        /* PKV_SCHEDULE_PAGES: uint32 page cursors, one 128-byte line per
-                                   (row, KV head); empty otherwise */
+                                   (row, KV head); PKV_SCHEDULE_STEAL: one per (row, KV head,
+                                   wave), 8 waves; empty otherwise */
     uint64_t loop_off;          /* resident loop: control mirror and two slots of step counters */
     uint64_t loop_mirror_off;   /* resident loop: device copies of the two host queue slots */
     uint64_t sink_off;          /* 4 KiB read by the gather's look-ahead past the end of a

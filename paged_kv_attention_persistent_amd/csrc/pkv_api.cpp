@@ -40,7 +40,9 @@ DecodeParams decode_params(const Resolved& r, const pkv_layout& lay, unsigned ch
     p.partial_o = reinterpret_cast<float*>(ws + lay.partial_o_off);
     p.sink = reinterpret_cast<const char*>(ws + lay.sink_off);
     p.row_len = reinterpret_cast<const int32_t*>(ws + lay.row_len_off);
-    p.cursors = r.schedule == PKV_SCHEDULE_PAGES ? reinterpret_cast<uint32_t*>(ws + lay.cursor_off) : nullptr;
+    p.cursors = (r.schedule == PKV_SCHEDULE_PAGES || r.schedule == PKV_SCHEDULE_STEAL)
+                    ? reinterpret_cast<uint32_t*>(ws + lay.cursor_off) : nullptr;
+    p.steal = r.schedule == PKV_SCHEDULE_STEAL ? 1 : 0;
     p.partial_lse = reinterpret_cast<float*>(ws + lay.partial_lse_off);
     p.arrive = reinterpret_cast<uint32_t*>(ws + lay.arrive_off);
     p.trace = nullptr;
@@ -438,8 +440,9 @@ PKV_API pkv_status pkv_create(const pkv_config* cfg, void* workspace, size_t wor
                               h->r.max_batch * h->r.hkv * h->r.num_layers, h->stream);
     if (rc == 0 && h->r.persistent)
         rc = launch_zero(h->ws + h->lay.loop_off, sizeof(LoopGlobal) + 2 * loop_counter_bytes(h->r), h->stream);
-    if (rc == 0 && h->r.schedule == PKV_SCHEDULE_PAGES)     // cursors start at zero; the merge re-arms them
-        rc = launch_zero(h->ws + h->lay.cursor_off, 4ull * kCursorStride * h->r.max_batch * h->r.hkv, h->stream);
+    if (rc == 0 && (h->r.schedule == PKV_SCHEDULE_PAGES || h->r.schedule == PKV_SCHEDULE_STEAL))
+        // cursors start at zero; the merge re-arms them
+        rc = launch_zero(h->ws + h->lay.cursor_off, h->lay.loop_off - h->lay.cursor_off, h->stream);
     if (rc != 0) { pkv_destroy(h); return PKV_ERR_HIP; }
     // an empty queue until the first build
     QHdr* qh = reinterpret_cast<QHdr*>(h->staging[0]);

@@ -174,8 +174,9 @@ struct DecodeParams {
     float scale_log2;           // scale * log2(e)
     const char* sink;           // kSinkBytes the look-ahead reads past a window's end
     const int32_t* row_len;     // [batch] tokens per row (the queue's copy of ctx_lens)
-    uint32_t* cursors;          // page-claim schedule: [max_batch][Hkv] cursors, kCursorStride apart
+    uint32_t* cursors;          // page-claim and steal schedules: [max_batch][Hkv] cursors, kCursorStride apart
                                 // (null: split items read their own token range)
+    int32_t steal;              // 1: the first pages of every split item go to its row's shared pool
 };
 
 // Resident-loop kernel parameters: the per-step constant part of the decode

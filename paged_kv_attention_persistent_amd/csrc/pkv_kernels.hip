@@ -561,6 +561,151 @@ __device__ __forceinline__ void run_claimed(const DecodeParams& P, const u32x4 (
     __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
+// Steal schedule.  Every item of a split (row, KV head) reads the pages of
+// its range past the first pool_share() of them itself, in the fixed
+// round-robin order (wave w takes every kWaves-th page); the first
+// pool_share() pages of all the row's items form the row's shared pool, which
+// the waves of the row's items drain once their own pages are done.  Wave w
+// of any item takes only pool pages congruent to w modulo kWaves, claimed
+// kPoolClaim at a time from a cursor of its own (one per row, KV head and
+// wave index, so no cursor sees more than a few hundred claims), and a wave
+// that finishes early claims more, so the row's items end within a few
+// microseconds of each other instead of following the speed of the XCD each
+// one runs on.  Claimed pages fold into the wave's running state, so an item
+// still yields one partial state and the merge is unchanged.
+// The pool holds full pages only: the row's partial last page stays in the
+// last item's own pages.
+constexpr int kPoolEighths = 2;                 // pool share of a full item, in eighths
+constexpr int kPoolClaim = 3;                   // pages per claim (whole rotations of three tiles)
+constexpr int kPoolStep = kPoolClaim * kWaves;  // pool pages per claim round of the 8 waves
+
+// Pages at the start of an item that belong to the row's pool: cp is the
+// queue's range length in pages, n the item's own page count.
+__device__ __forceinline__ int pool_share(int cp, int n, bool last) {
+    const int k = ((cp * kPoolEighths / 8) / kPoolStep) * kPoolStep;
+    if (!last) return n < k ? 0 : k;             // (a full item has n = cp pages)
+    const int kl = ((n - 1) / kPoolStep) * kPoolStep;   // keep the last page in the item
+    return kl < k ? kl : k;
+}
+
+// One claim on a wave's pool cursor (lane 0's atomic; the result is read
+// later, with readfirstlane, so its round trip overlaps other work).
+__device__ __forceinline__ uint32_t pool_claim(uint32_t* cursor, int lane) {
+    uint32_t v = 0;
+    if (lane == 0) {
+        // a lane-private copy of the address keeps this a one-lane atomic
+        __attribute__((address_space(1))) uint32_t* cp = (__attribute__((address_space(1))) uint32_t*)cursor;
+        __asm__ volatile("" : "+v"(cp));
+        v = __hip_atomic_fetch_add(cp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return v;
+}
+
+// first: this wave's first claim, made when the item started.
+template <int D, int G, typename KV>
+__device__ __forceinline__ void run_pool(const DecodeParams& P, const u32x4 (&qv)[G][D / 64],
+                                         State<D, G>& st, uint32_t* cursor, uint32_t first, const int32_t* bt0,
+                                         int cp, int nch, uint32_t len, int w, int hk, int lane, int r, int p) {
+    constexpr int TPP = KV::kTilesPerPage;
+    constexpr int TPG = kPoolClaim * TPP;        // tiles per claim
+    constexpr int kTileRows = kPageSize / TPP;
+    constexpr uint64_t kSlabBytes = (uint64_t)kPageSize * D * KV::kBytes;
+    constexpr uint64_t kTileBytes = kSlabBytes / TPP;
+    static_assert(TPG % 3 == 0, "a claim is whole rotations of three tiles");
+    const char* kbase = reinterpret_cast<const char*>(P.k_pool);
+    const char* vbase = reinterpret_cast<const char*>(P.v_pool);
+    const uint64_t head_off = (uint64_t)hk * kSlabBytes;
+    const uint64_t page_stride = (uint64_t)P.hkv * kSlabBytes;
+    const float c = P.scale_log2;
+    const int n_row = (int)((len + kPageSize - 1) / kPageSize);
+    // claims: gpi per full item, then those of the last item
+    const int gpi = pool_share(cp, cp, false) / kPoolStep;
+    const int n_last = n_row - (nch - 1) * cp;
+    const uint32_t ng = n_last > 0 ? (uint32_t)((nch - 1) * gpi + pool_share(cp, n_last, true) / kPoolStep) : 0u;
+
+    // Page ids of claim v: wave-uniform scalar loads through the constant
+    // address space (the block table does not change during the launch, and
+    // a wait for a scalar load does not hold the vector loads in flight).
+    typedef const __attribute__((address_space(4))) int32_t cint;
+    cint* cbt = (cint*)(uintptr_t)bt0;
+    struct Ids { int32_t id[kPoolClaim]; };
+    auto claim_ids = [&](uint32_t v) -> Ids {
+        Ids o;
+        const int ci = (int)(v / (uint32_t)gpi), j = (int)(v % (uint32_t)gpi);
+        const int base = ci * cp + j * kPoolStep + w;
+#pragma unroll
+        for (int i = 0; i < kPoolClaim; ++i) o.id[i] = cbt[base + i * kWaves];
+        return o;
+    };
+    // Pages outside the pool read page 0 instead; the first one is reported
+    // after the loop.  Branch-free, so that the wait for the ids sits where
+    // they are first used.
+    int32_t bad = -1;
+    auto check = [&](Ids& o) {
+#pragma unroll
+        for (int i = 0; i < kPoolClaim; ++i) {
+            const bool oob = (uint32_t)o.id[i] >= (uint32_t)P.num_pages;
+            bad = (oob && bad < 0) ? o.id[i] : bad;
+            o.id[i] = oob ? 0 : o.id[i];
+        }
+    };
+    const LaneOff full = lane_offsets<D, KV>(r, p, kTileRows);
+    auto issue = [&](Tile<D, KV>& T, const Ids& o, int t, bool ok) {
+        const char* ks = P.sink;
+        const char* vs = P.sink;
+        if (ok) {
+            const uint64_t so = (uint64_t)(uint32_t)o.id[t / TPP] * page_stride + head_off +
+                                (uint64_t)(t % TPP) * kTileBytes;
+            ks = kbase + so;
+            vs = vbase + so;
+        }
+        LaneOff o_ = full;
+        __asm__ volatile("" : "+v"(o_.o0), "+v"(o_.o1));
+        load_tile<D, KV>(T, ks, vs, o_);
+    };
+
+    const uint32_t v0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)first);
+    if (v0 >= ng) return;
+    Ids cur = claim_ids(v0);
+    uint32_t cv = pool_claim(cursor, lane);               // the claim after this one
+    check(cur);
+    Tile<D, KV> A, B, C;
+    issue(A, cur, 0, true);
+    issue(B, cur, 1, true);
+    issue(C, cur, 2, true);
+    for (;;) {
+        // the claim made one claim ago: its round trip overlapped the tiles
+        // issued since, so reading it does not wait for them
+        const uint32_t vn = (uint32_t)__builtin_amdgcn_readfirstlane((int)cv);
+        const bool more = vn < ng;
+        Ids nxt = cur;
+        if (more) {
+            nxt = claim_ids(vn);
+            cv = pool_claim(cursor, lane);                // the claim after next
+        }
+#pragma unroll
+        for (int rnd = 0; rnd < TPG / 3; ++rnd) {
+            const int t = 3 * rnd;
+            consume_tile<D, G, KV, false>(A, qv, st, c, r, kTileRows);
+            if (rnd == TPG / 3 - 1) {
+                // keep the ids' first use (and the wait for them) after the tile
+                __builtin_amdgcn_sched_barrier(0);
+                check(nxt);
+            }
+            if (t + 3 < TPG) issue(A, cur, t + 3, true); else issue(A, nxt, t + 3 - TPG, more);
+            consume_tile<D, G, KV, false>(B, qv, st, c, r, kTileRows);
+            if (t + 4 < TPG) issue(B, cur, t + 4, true); else issue(B, nxt, t + 4 - TPG, more);
+            consume_tile<D, G, KV, false>(C, qv, st, c, r, kTileRows);
+            if (t + 5 < TPG) issue(C, cur, t + 5, true); else issue(C, nxt, t + 5 - TPG, more);
+        }
+        if (!more) break;
+        cur = nxt;
+    }
+    // the look-ahead past the last claim (sink reads) and the spare claim
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (bad >= 0 && lane == 0) report(P.ctrl, P.host_error, PKV_DEVERR_PAGE_OOB, (uint32_t)bad);
+}
+
 template <int D, int G>
 struct Smem {
     float acc[kWaves][G * D];
@@ -611,6 +756,14 @@ __device__ __forceinline__ void store_lse(const DecodeParams& P, int b, size_t h
 // Ranges are read 32 at a time, all loads of a block issued together; blocks
 // after the first fold in by rescaling (the same identity, applied twice).
 // Each thread merges two adjacent dims of one head.
+// The page cursors of a (row, KV head): one for the page-claim schedule, one
+// per wave index for the steal schedule.
+__device__ __forceinline__ void rearm_cursors(const DecodeParams& P, int b, int hk) {
+    const int n = P.steal ? kWaves : 1;
+    uint32_t* c = P.cursors + ((size_t)b * P.hkv + hk) * n * kCursorStride;
+    for (int i = 0; i < n; ++i) atomicExch(c + (size_t)i * kCursorStride, 0u);
+}
+
 template <int D, int G, int NT, bool COHERENT>
 __device__ void merge_row(const DecodeParams& P, int b, int hk, int nc, int base, int tid) {
     constexpr int CB = 32;
@@ -709,7 +862,9 @@ __device__ __forceinline__ ItemRef read_item(const DecodeParams& P, uint32_t idx
     return it;
 }
 
-template <int D, int G, typename KV>
+// ONE_SHOT: compiled for the one-shot decode kernel, which alone takes the
+// page-claim and steal schedules (the resident loop claims whole items).
+template <int D, int G, typename KV, bool ONE_SHOT>
 __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, const ItemRef& it, uint32_t& nxt) {
     constexpr int NPC = D / 64;
     const int tid = threadIdx.x;
@@ -728,7 +883,6 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, const ItemRe
     }
     const int n_pages = (int)((te - tb + kPageSize - 1) / kPageSize);
     const int first_page = (int)(tb / kPageSize);
-    const int nw = n_pages > w ? (n_pages - w + kWaves - 1) / kWaves : 0;
 
     // q as packed bf16, in the dims this lane's cache words hold: qv[g][k]
     // pairs with word k (bf16) or words 2k, 2k + 1 (fp32, two halves)
@@ -773,12 +927,25 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, const ItemRe
         for (int e = 0; e < D / 8; ++e) st.acc[g][e] = 0.0f;
     }
 
-    const WaveItem wi{tb, te, w, hk};
-    const int32_t* bt_row = P.block_table + (size_t)b * P.bt_stride + first_page + w;
-    if (P.cursors && it.nch > 1) {                // page-claim schedule: the row's pages are shared
+    if (ONE_SHOT && P.cursors && it.nch > 1 && !P.steal) {   // page-claim schedule: the row's pages are shared
         run_claimed<D, G, KV>(P, qv, st, P.cursors + ((size_t)b * P.hkv + hk) * kCursorStride,
                               P.block_table + (size_t)b * P.bt_stride, it.len, hk, lane, r, p);
     } else {
+        // steal schedule: the item's first pages belong to the row's pool
+        const bool pool = ONE_SHOT && P.steal && it.nch > 1;
+        int cp = 0, skip = 0;
+        if (pool) {
+            cp = __builtin_amdgcn_readfirstlane(P.qhdr->chunk_tokens) / kPageSize;
+            skip = pool_share(cp, n_pages, it.chunk == it.nch - 1);
+        }
+        const int nb = n_pages - skip;
+        const int nw = nb > w ? (nb - w + kWaves - 1) / kWaves : 0;
+        const WaveItem wi{tb + (uint32_t)skip * kPageSize, te, w, hk};
+        const int32_t* bt_row = P.block_table + (size_t)b * P.bt_stride + first_page + skip + w;
+        uint32_t* cursor = pool ? P.cursors + (((size_t)b * P.hkv + hk) * kWaves + w) * kCursorStride : nullptr;
+        // the first pool claim is made now, so its result is back by the time
+        // this wave's own pages are done
+        const uint32_t first_claim = pool ? pool_claim(cursor, lane) : 0u;
         for (int wb = 0; wb < nw; wb += 64) {
             const int n = nw - wb < 64 ? nw - wb : 64;
             int32_t btv = 0;
@@ -796,6 +963,9 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, const ItemRe
             }
             run_window<D, G, KV>(P, qv, st, btv, n, wb, wi, r, p);
         }
+        if (pool)
+            run_pool<D, G, KV>(P, qv, st, cursor, first_claim, P.block_table + (size_t)b * P.bt_stride, cp, it.nch,
+                               it.len, w, hk, lane, r, p);
     }
     // Claim the next item only now, near the end of this one: a claim made
     // earlier would hold an item this workgroup cannot start while another
@@ -900,8 +1070,8 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, const ItemRe
             if (tid == 0) {
                 atomicExch(&P.arrive[(size_t)b * P.hkv + hk], 0u);
                 // every item of the row has arrived, so no wave claims from
-                // its cursor any more: the next launch starts it at zero
-                if (P.cursors) atomicExch(P.cursors + ((size_t)b * P.hkv + hk) * kCursorStride, 0u);
+                // its cursors any more: the next launch starts them at zero
+                if (P.cursors) rearm_cursors(P, b, hk);
             }
         }
     }
@@ -941,7 +1111,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
         uint32_t nxt = 0;
         uint64_t t_start = 0;
         if (P.trace) t_start = wall_clock64();
-        process_item<D, G, KV>(P, sm, read_item(P, idx), nxt);
+        process_item<D, G, KV, true>(P, sm, read_item(P, idx), nxt);
         ++done_here;
         if (P.trace && tid == 0 && idx < (uint32_t)P.trace_cap) {
             const uint64_t t_end = wall_clock64();
@@ -1265,7 +1435,7 @@ __global__ __launch_bounds__(kThreads) void resident_kernel(LoopParams L) {
                 if (L.append && it.ok && it.chunk == it.nch - 1)
                     append_token<D, KV>(Q, grants, it, new_k + layer * ls_new * KV::kBytes,
                                         new_v + layer * ls_new * KV::kBytes, tid);
-                process_item<D, G, KV>(Q, sm, it, nxt);
+                process_item<D, G, KV, false>(Q, sm, it, nxt);
             } else {
                 // rows with no tokens take the neutral state, in every layer;
                 // thread 0 finds them (64 merge rows at a time), all threads write
@@ -1351,7 +1521,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
     if (nc == 1 || (P.part_off[b] + nc) * P.hkv > P.max_items) return;
     merge_row<D, G, 256, false>(P, b, hk, nc, P.part_off[b], threadIdx.x);
     // the decode kernel has finished: its page cursor starts the next launch at zero
-    if (P.cursors && threadIdx.x == 0) P.cursors[((size_t)b * P.hkv + hk) * kCursorStride] = 0u;
+    if (P.cursors && threadIdx.x == 0) rearm_cursors(P, b, hk);
 }
 
 // Device queue builder: the same bytes as the host builder, from device

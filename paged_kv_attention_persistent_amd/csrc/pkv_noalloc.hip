@@ -73,8 +73,8 @@ extern "C" PKV_API pkv_status pkv_decode_noalloc(const pkv_config* cfg, const in
     const DecodeParams p = decode_params(r, lay, ws, t, error_word);
     const BuildParams bp = build_params(r, lay, ws, ctx_lens_device, batch, error_word);
     int rc = launch_init_ctrl(p.ctrl, p.arrive, r.max_batch * r.hkv * r.num_layers, stream);
-    if (rc == 0 && r.schedule == PKV_SCHEDULE_PAGES)
-        rc = launch_zero(ws + lay.cursor_off, 4ull * kCursorStride * r.max_batch * r.hkv, stream);
+    if (rc == 0 && (r.schedule == PKV_SCHEDULE_PAGES || r.schedule == PKV_SCHEDULE_STEAL))
+        rc = launch_zero(ws + lay.cursor_off, lay.loop_off - lay.cursor_off, stream);
     if (rc == 0) rc = launch_build_queue(bp, stream);
     if (rc == 0) rc = launch_decode(p, r.d, r.g, r.kv_dtype, cus * r.wg_per_cu, stream);
     if (rc == 0 && r.merge_mode == PKV_MERGE_SEPARATE && batch > 0) rc = launch_merge(p, r.d, r.g, batch, stream);

@@ -86,7 +86,7 @@ pkv_status resolve_config(const pkv_config* cfg, int device_cus, Resolved* r, co
     if (r->timeout_ms < 1 || r->timeout_ms > 3600000) { *why = "timeout_ms must be 1..3600000"; return PKV_ERR_INVALID_ARG; }
     if (r->persistent && r->wg_per_cu != 1) { *why = "the resident loop runs one workgroup per CU"; return PKV_ERR_INVALID_ARG; }
     if (cfg->schedule != PKV_SCHEDULE_ATOMIC && cfg->schedule != PKV_SCHEDULE_STATIC &&
-        cfg->schedule != PKV_SCHEDULE_PAGES) {
+        cfg->schedule != PKV_SCHEDULE_PAGES && cfg->schedule != PKV_SCHEDULE_STEAL) {
         *why = "unknown schedule"; return PKV_ERR_INVALID_ARG;
     }
     if (r->persistent && cfg->schedule != PKV_SCHEDULE_ATOMIC) { *why = "the resident loop claims items atomically"; return PKV_ERR_INVALID_ARG; }
@@ -138,7 +138,9 @@ void compute_layout(const Resolved& r, pkv_layout* lay) {
     lay->arrive_off = off;
     off = align256(off + 4ull * r.max_batch * r.hkv * layers);
     lay->cursor_off = off;
+    // one cursor per (row, KV head), or per (row, KV head, wave) for the steal schedule
     if (r.schedule == PKV_SCHEDULE_PAGES) off = align256(off + 4ull * kCursorStride * r.max_batch * r.hkv);
+    if (r.schedule == PKV_SCHEDULE_STEAL) off = align256(off + 4ull * kCursorStride * r.max_batch * r.hkv * kWaves);
     lay->loop_off = off;
     if (r.persistent) off = align256(off + sizeof(LoopGlobal) + 2ull * loop_counter_bytes(r));
     lay->loop_mirror_off = off;

@@ -29,7 +29,7 @@ PKV_ERR_TIMEOUT = -7
 
 PKV_POLICY_AUTO, PKV_POLICY_NO_SPLIT, PKV_POLICY_SPLIT = 0, 1, 2
 PKV_ORDER_CANONICAL, PKV_ORDER_LPT = 0, 1
-PKV_SCHEDULE_ATOMIC, PKV_SCHEDULE_STATIC, PKV_SCHEDULE_PAGES = 0, 1, 2
+PKV_SCHEDULE_ATOMIC, PKV_SCHEDULE_STATIC, PKV_SCHEDULE_PAGES, PKV_SCHEDULE_STEAL = 0, 1, 2, 3
 PKV_MERGE_FUSED, PKV_MERGE_SEPARATE = 0, 1
 PKV_KV_BF16, PKV_KV_F32 = 0, 1
 PKV_DEVERR_NONE, PKV_DEVERR_PAGE_OOB, PKV_DEVERR_BAD_ITEM = 0, 1, 2

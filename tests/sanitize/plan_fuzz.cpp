@@ -137,7 +137,7 @@ static int fuzz(unsigned seed, int trials) {
         c.merge_mode = uni(0, 1);
         c.persistent = rng() % 4 == 0;
         c.num_layers = c.persistent ? uni(1, 4) : 0;
-        c.schedule = c.persistent ? 0 : uni(0, 2);
+        c.schedule = c.persistent ? 0 : uni(0, 3);
         c.kv_dtype = uni(0, 1);
         Resolved r;
         const char* why = nullptr;

@@ -138,7 +138,8 @@ def test_config_validation():
            dict(num_pages=0), dict(wg_per_cu=9), dict(policy=7), dict(num_q_heads=64),
            dict(merge_mode=2), dict(persistent=1, schedule=1), dict(append=2),
            dict(append=1), dict(kv_dtype=2), dict(kv_dtype=-1),
-           dict(schedule=3), dict(persistent=1, schedule=2)]
+           dict(schedule=4), dict(schedule=-1), dict(persistent=1, schedule=2),
+           dict(persistent=1, schedule=3)]
     base = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, num_pages=100, max_batch=4,
                 max_pages_per_seq=10, num_cus=256)
     for b in bad:
@@ -167,8 +168,11 @@ def test_page_claim_layout():
     assert a.loop_off - a.cursor_off == 0
     assert b.loop_off - b.cursor_off == 4 * 8 * 128
     assert b.total_bytes - a.total_bytes == 4 * 8 * 128
+    # the steal schedule: one 128-byte cursor per (row, KV head, wave), 8 waves
+    c = pkv.pkv_workspace_layout(pkv.make_config(schedule=pkv.PKV_SCHEDULE_STEAL, **kw))
+    assert c.loop_off - c.cursor_off == 4 * 8 * 128 * 8
     for f in ("queue_off", "n_chunks_off", "part_off_off", "row_len_off", "merge_rows_off", "items_off"):
-        assert getattr(a, f) == getattr(b, f)
+        assert getattr(a, f) == getattr(b, f) == getattr(c, f)
     assert a.part_off_off < a.row_len_off < a.merge_rows_off < a.items_off
 
 

@@ -154,7 +154,7 @@ def lse_tol(wl):
     return LSE_F32 if wl.kv_dtype == "f32" else MAX_ABS
 
 
-SCHEDULES = {"atomic": pkv.PKV_SCHEDULE_ATOMIC, "pages": pkv.PKV_SCHEDULE_PAGES}
+SCHEDULES = {"atomic": pkv.PKV_SCHEDULE_ATOMIC, "pages": pkv.PKV_SCHEDULE_PAGES, "steal": pkv.PKV_SCHEDULE_STEAL}
 
 
 @pytest.mark.parametrize("sched", list(SCHEDULES))
@@ -755,6 +755,74 @@ def test_page_claims_split_equals_unsplit(kv):
         check(oa, la, ob, lb, f"page claims vs unsplit {kv} call {call}", lse_tol(wl))
     a.close()
     b.close()
+
+
+# Rows for the steal schedule at 2048-token ranges (128 pages): every full
+# range gives its first 24 pages to the row's pool (a quarter of the range,
+# rounded down to whole claim rounds of 8 waves x 3 pages); the last range
+# gives min(24, its pages - 1 rounded down to 24), so a last range of one
+# token or one page gives none, and one of 98 pages gives 24.
+STEAL_LENS = [20000, 6149, 4096, 2049, 0, 300, 16 * 128 * 3 + 16 * 25 + 7]
+
+
+@pytest.mark.parametrize("kv", KVS)
+@pytest.mark.parametrize("merge", [pkv.PKV_MERGE_FUSED, pkv.PKV_MERGE_SEPARATE],
+                         ids=["fused_merge", "separate_merge"])
+def test_steal_pool_against_oracle_and_repeats(merge, kv):
+    """Steal schedule on rows whose ranges share a pool: every output against
+    the oracle on repeated calls (the claimed pool pages differ from call to
+    call; every cursor must start each call at zero again), and against the
+    unsplit decode of the same rows."""
+    wl = workloads.custom("steal_pool", STEAL_LENS, 8, 2, 128, spare_pages=3, kv_dtype=kv)
+    run = Run(wl, policy=pkv.PKV_POLICY_SPLIT, kv_chunk_tokens=2048, merge_mode=merge,
+              schedule=pkv.PKV_SCHEDULE_STEAL)
+    flat = Run(wl, policy=pkv.PKV_POLICY_NO_SPLIT)
+    ob, lb = flat.decode()
+    ro, rl = oracle_full(wl)
+    check(ob, lb, ro, rl, f"unsplit {kv}", lse_tol(wl))
+    for call in range(6):
+        run.out.fill_(float("nan"))
+        run.lse.fill_(float("nan"))
+        o, l = run.decode()
+        check(o, l, ro, rl, f"steal {kv} merge {merge} call {call}", lse_tol(wl))
+        check(o, l, ob, lb, f"steal vs unsplit {kv} merge {merge} call {call}", lse_tol(wl))
+        assert np.all(o[4] == 0) and np.all(np.isneginf(l[4]))
+    lay = run.dec.layout
+    cur = run.dec.workspace[lay.cursor_off:lay.loop_off]
+    assert int(cur.cpu().view(torch.int32).abs().sum()) == 0       # every cursor re-armed
+    assert run.dec.query()["error_code"] == 0
+    run.close()
+    flat.close()
+
+
+@pytest.mark.parametrize("kv", KVS)
+def test_steal_pool_counts_every_token(kv):
+    """The closed forms of the structured cases (q = 0: LSE = ln L_b, V column
+    means, 0.375 bit for bit) under the steal schedule with pools in use: a
+    pool page read twice or never moves LSE by about 16 / L_b."""
+    wl = workloads.custom("steal_structured", STEAL_LENS, 8, 2, 128, spare_pages=3, kv_dtype=kv)
+    v = wl.pool("v", "cpu", poison=True)
+    for b, L in enumerate(STEAL_LENS):
+        t = np.arange(L)
+        pg = torch.as_tensor(wl.block_table[b, t // 16].astype(np.int64))
+        row = torch.as_tensor(t % 16)
+        v[pg, :, row, 0] = torch.as_tensor((t % 256) / 256.0, dtype=torch.float32).to(v.dtype)[:, None]
+        v[pg, :, row, 1] = 0.375
+    run = Run(wl, policy=pkv.PKV_POLICY_SPLIT, kv_chunk_tokens=2048, schedule=pkv.PKV_SCHEDULE_STEAL)
+    run.q.zero_()
+    run.v = v.to("cuda")
+    for call in range(3):
+        o, l = run.decode()
+        for b, L in enumerate(STEAL_LENS):
+            if L == 0:
+                assert np.all(o[b] == 0) and np.all(np.isneginf(l[b]))
+                continue
+            where = f"steal {kv} call {call} row {b} (L = {L})"
+            assert np.abs(l[b] - np.log(L)).max() <= 5e-6, where
+            exact = np.mean((np.arange(L) % 256) / 256.0)
+            assert np.abs(o[b, :, 0] - exact).max() <= 2.0 ** -8 * exact + 1e-6, where
+            assert np.all(o[b, :, 1] == 0.375), where
+    run.close()
 
 
 @pytest.mark.parametrize("sched", list(SCHEDULES))
