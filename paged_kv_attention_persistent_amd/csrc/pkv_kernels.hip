@@ -43,6 +43,7 @@ namespace pkv {
 namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kTau = 8.0f;               // lazy-rescale threshold, log2 units
@@ -278,24 +279,40 @@ __device__ __forceinline__ void consume_tile(const Tile<D, KV>& t, const u32x4 (
             st.m[g] = mn;
         }
     }
+    // bf16 cache: the lane's two token rows (8 apart) hold the same dims, so
+    // P.V runs as v_dot2 over the row pair: each dim's two V values form one
+    // bf16 pair (a byte permute, shared by all heads) and each head's two
+    // weights another (rounded to nearest even, one conversion), accumulated
+    // in fp32.  The softmax sum l keeps the unrounded fp32 weights.
+    uint32_t vp[NPC][4][2];
+    if constexpr (KV::kBytes == 2) {
+#pragma unroll
+        for (int k = 0; k < NPC; ++k) {
+            const uint32_t a0[4] = {v[0][k].x, v[0][k].y, v[0][k].z, v[0][k].w};
+            const uint32_t a1[4] = {v[1][k].x, v[1][k].y, v[1][k].z, v[1][k].w};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                vp[k][w][0] = __builtin_amdgcn_perm(a1[w], a0[w], 0x05040100u);   // low dims of both rows
+                vp[k][w][1] = __builtin_amdgcn_perm(a1[w], a0[w], 0x07060302u);   // high dims of both rows
+            }
+        }
+    }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         if constexpr (KV::kBytes == 2) {
             const float p0 = __builtin_amdgcn_exp2f(s[0][g] - st.m[g]);
             const float p1 = __builtin_amdgcn_exp2f(s[1][g] - st.m[g]);
             st.l[g] += p0 + p1;
+            const uint32_t pp = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{p0, p1}, bf16x2_t));
 #pragma unroll
-            for (int k = 0; k < NPC; ++k) {
-                const uint32_t a0[4] = {v[0][k].x, v[0][k].y, v[0][k].z, v[0][k].w};
-                const uint32_t a1[4] = {v[1][k].x, v[1][k].y, v[1][k].z, v[1][k].w};
+            for (int k = 0; k < NPC; ++k)
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     float& lo = st.acc[g][k * 8 + 2 * w];
                     float& hi = st.acc[g][k * 8 + 2 * w + 1];
-                    lo = fmaf(p1, bf16_lo(a1[w]), fmaf(p0, bf16_lo(a0[w]), lo));
-                    hi = fmaf(p1, bf16_hi(a1[w]), fmaf(p0, bf16_hi(a0[w]), hi));
+                    lo = dot2(vp[k][w][0], pp, lo);
+                    hi = dot2(vp[k][w][1], pp, hi);
                 }
-            }
         } else {
             const float p0 = __builtin_amdgcn_exp2f(s[0][g] - st.m[g]);
             st.l[g] += p0;
