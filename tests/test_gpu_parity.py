@@ -757,6 +757,59 @@ def test_page_claims_split_equals_unsplit(kv):
     b.close()
 
 
+# ------------------------------------------------ seeded random sweep ----
+
+def _random_case(rng, i):
+    """One configuration drawn over everything the library accepts at small
+    size: head_dim, group size (8 only at head_dim 64), KV heads, ragged lengths (empty rows, one
+    token, page boundaries, long rows), policy, range length, queue order,
+    merge, schedule and cache type."""
+    d = int(rng.choice([64, 128]))
+    g = int(rng.choice([1, 2, 4, 8] if d == 64 else [1, 2, 4]))     # group 8 is built for head_dim 64
+    hkv = int(rng.choice([1, 2, 4]))
+    b = int(rng.integers(1, 7))
+    pool = [0, 1, 15, 16, 17, 255, 256, 257, 1023, 2049, 3000, 4097, 9000, 20000]
+    lens = [int(rng.choice(pool)) if rng.random() < 0.5 else int(rng.integers(1, 12000)) for _ in range(b)]
+    policy = int(rng.choice([pkv.PKV_POLICY_AUTO, pkv.PKV_POLICY_SPLIT, pkv.PKV_POLICY_NO_SPLIT]))
+    chunk = int(rng.choice([0, 0, 16, 256, 1024, 2048]))
+    cfg = dict(policy=policy, kv_chunk_tokens=chunk,
+               order=int(rng.choice([pkv.PKV_ORDER_CANONICAL, pkv.PKV_ORDER_LPT])),
+               merge_mode=int(rng.choice([pkv.PKV_MERGE_FUSED, pkv.PKV_MERGE_SEPARATE])),
+               schedule=int(rng.choice([pkv.PKV_SCHEDULE_ATOMIC, pkv.PKV_SCHEDULE_STATIC,
+                                        pkv.PKV_SCHEDULE_PAGES, pkv.PKV_SCHEDULE_STEAL])),
+               num_cus=int(rng.choice([0, 0, 8, 64])))
+    kv = str(rng.choice(KVS))
+    return f"random_{i}", lens, g * hkv, hkv, d, kv, cfg
+
+
+@pytest.mark.parametrize("block", range(4))
+def test_seeded_random_configurations_against_oracle(block):
+    """Forty seeded random configurations (ten per block), every output
+    against the oracle on two calls in a row, and the host queue's split
+    decision and item count against the oracle's queue (num_cus = 0 is the
+    device's CU count)."""
+    rng = np.random.default_rng([20260623, block])
+    cus_dev = torch.cuda.get_device_properties(0).multi_processor_count
+    for i in range(10):
+        name, lens, hq, hkv, d, kv, cfg = _random_case(rng, 10 * block + i)
+        say(name, "lens", lens, "hq", hq, "hkv", hkv, "d", d, "kv", kv, cfg)
+        wl = workloads.custom(name, lens, hq, hkv, d, spare_pages=3, kv_dtype=kv)
+        cus = cfg.pop("num_cus") or cus_dev
+        run = Run(wl, num_cus=cus, **cfg)
+        ro, rl = oracle_full(wl)
+        ref = wq.build_queue(lens, hkv, cus, cfg["kv_chunk_tokens"], cfg["policy"], cfg["order"])
+        for call in range(2):
+            run.out.fill_(float("nan"))
+            run.lse.fill_(float("nan"))
+            o, l = run.decode()
+            assert run.info.n_items == len(ref["items"]) and bool(run.info.split) == ref["split"], name
+            check(o, l, ro, rl, f"{name} call {call}", lse_tol(wl))
+            for bb, L in enumerate(lens):
+                if L == 0:
+                    assert np.all(o[bb] == 0) and np.all(np.isneginf(l[bb])), name
+        run.close()
+
+
 # Rows for the steal schedule at 2048-token ranges (128 pages): every full
 # range gives its first 24 pages to the row's pool (a quarter of the range,
 # rounded down to whole claim rounds of 8 waves x 3 pages); the last range
