@@ -757,6 +757,54 @@ def test_page_claims_split_equals_unsplit(kv):
     b.close()
 
 
+# ------------------------------------------------------ maximum size ----
+
+@pytest.mark.parametrize("kv", KVS)
+def test_million_token_context(kv):
+    """Maximum-size case: one context of 1,048,571 tokens (65,536 pages, the
+    last one partial; 4.3 GB of bf16 K+V, 8.6 GB fp32) in fitted ranges of
+    32,768 tokens merged across 256 workgroups.  (1) q = 0 counts every token
+    under the atomic and steal schedules: LSE = ln L to fp32 rounding (one
+    page more or less moves it by 1.5e-5), V column 1 = 0.375 bit for bit and
+    column 0 = (t mod 256) / 256 to its exact mean within bf16 rounding;
+    (2) the generator's q: every query head of the last KV head against the
+    oracle."""
+    L = 1_048_571
+    wl = workloads.long_context(ctx=L).with_kv_dtype(kv)
+    run = Run(wl, poison=True)
+    say(f"million-token context ({kv}): {wl.num_pages} pages")
+    o, l = run.decode()
+    info = run.info
+    assert info.split and info.n_items == 256 and info.chunk_tokens == 32768
+    hk = wl.num_kv_heads - 1
+    G = wl.num_q_heads // wl.num_kv_heads
+    ro, rl = oracle_unit(wl, workloads.bits_u16(run.q), 0, hk)
+    check(o[0:1, hk * G:(hk + 1) * G], l[0:1, hk * G:(hk + 1) * G], ro[None], rl[None],
+          f"million {kv}: KV head {hk} against the oracle", lse_tol(wl))
+    run.close()
+    del run
+    torch.cuda.empty_cache()
+    exact = np.mean((np.arange(L) % 256) / 256.0)
+    for sched in (pkv.PKV_SCHEDULE_ATOMIC, pkv.PKV_SCHEDULE_STEAL):
+        run = Run(wl, poison=True, schedule=sched)
+        t = torch.arange(L, device="cuda")
+        pg = torch.as_tensor(wl.block_table[0].astype(np.int64), device="cuda")[t // 16]
+        row = t % 16
+        run.v[pg, :, row, 0] = ((t % 256).float() / 256.0).to(run.v.dtype)[:, None]
+        run.v[pg, :, row, 1] = 0.375
+        run.q.zero_()
+        o, l = run.decode()
+        where = f"million {kv} schedule {sched}"
+        say(f"{where}: max |LSE - ln L| = {np.abs(l[0] - np.log(L)).max():.2e}, "
+            f"max |O0 - mean| = {np.abs(o[0, :, 0] - exact).max():.2e}")
+        assert np.abs(l[0] - np.log(L)).max() <= 5e-6, where
+        assert np.all(o[0, :, 1] == 0.375), where
+        assert np.abs(o[0, :, 0] - exact).max() <= 2.0 ** -8 * exact + 1e-6, where
+        run.close()
+        del run, t, pg, row
+        torch.cuda.empty_cache()
+
+
 # ------------------------------------------------ seeded random sweep ----
 
 def _random_case(rng, i):
