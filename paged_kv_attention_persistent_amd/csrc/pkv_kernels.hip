@@ -28,12 +28,16 @@
 //     lazy rescale: the running max is raised only when a score exceeds it by
 //     more than 2^8, so the accumulator rescale is rare; results are exact up
 //     to rounding because the final normalisation divides by the same sum;
+//   * P.V for a bf16 cache is v_dot2 over the lane's two token rows (each
+//     dim's two V values and each head's two weights as bf16 pairs, fp32
+//     accumulate);
 //   * pages are software-pipelined two ahead in registers (three tiles), so
 //     each wave keeps up to 16 KB of K/V loads in flight;
 //   * at the end of an item the 8 groups of a wave combine by DPP and
 //     row-swap permutes and the 8 waves combine through LDS.
 // An fp32 cache runs the same kernels on half-page tiles (8 rows of 512 B at
-// D = 128), with fp32 FMAs in place of the bf16 dot products.
+// D = 128), with fp32 FMAs in place of the bf16 dot products and fp32
+// weights in P.V.
 #include <float.h>
 #include <hip/hip_runtime.h>
 
@@ -201,9 +205,11 @@ struct State {
 };
 
 // q.K, online-softmax update and P.V for one tile.  q stays packed bf16 in
-// registers; for a bf16 cache two K rows meet it in v_dot2 (fp32 accumulate),
-// for an fp32 cache each q pair is widened to fp32 on the fly (exact) and
-// multiplied with full-precision K.  The accumulator is fp32 either way.
+// registers; for a bf16 cache K pairs meet it in v_dot2 (fp32 accumulate) and
+// P.V runs as v_dot2 over the lane's two token rows with the weights rounded
+// to bf16; for an fp32 cache each q pair is widened to fp32 on the fly
+// (exact), multiplied with full-precision K, and P.V is fp32 FMA with fp32
+// weights.  The accumulator and the softmax sum are fp32 either way.
 template <int D, int G, typename KV, bool MASKED>
 __device__ __forceinline__ void consume_tile(const Tile<D, KV>& t, const u32x4 (&qv)[G][D / 64],
                                              State<D, G>& st, float c, int r, int valid) {
