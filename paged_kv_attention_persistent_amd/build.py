@@ -55,5 +55,27 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+CLIENT_SRC = os.path.join(ROOT, "tests", "c_abi", "pkv_c_client.c")
+CLIENT = os.path.join(ROOT, "_build", "pkv_c_client")
+
+
+def build_c_client(verbose: bool = False) -> str:
+    """Compile the plain-C consumer of the C ABI (tests/c_abi) with the host C
+    compiler, linked against libpkv.so next to this file and the HIP runtime."""
+    os.makedirs(os.path.dirname(CLIENT), exist_ok=True)
+    rocm = os.path.dirname(os.path.dirname(hipcc()))
+    cmd = [shutil.which("gcc") or "gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"), CLIENT_SRC,
+           "-o", CLIENT, "-L", HERE, "-lpkv", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../paged_kv_attention_persistent_amd", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"gcc failed ({res.returncode}):\n{res.stderr}")
+    return CLIENT
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_c_client(verbose=True))

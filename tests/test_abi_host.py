@@ -272,3 +272,15 @@ def test_configs_whose_rows_could_need_more_than_65535_ranges_are_refused():
     with pytest.raises(pkv.PkvError) as e:
         pkv.pkv_workspace_size(big)
     assert e.value.status == pkv.PKV_ERR_CAPACITY
+
+
+def test_plain_c_client_compiles_against_the_header():
+    # include/pkv.h is plain C: the C consumer of the ABI (tests/c_abi) builds
+    # with gcc -std=c11 -Wall -Wextra and links against libpkv.so and the HIP
+    # runtime (it runs on the GPU in tests/test_gpu_c_abi.py)
+    import shutil
+    from paged_kv_attention_persistent_amd import build as b
+    if not shutil.which("gcc") or not os.path.exists("/opt/rocm/include/hip/hip_runtime_api.h"):
+        pytest.skip("gcc or the HIP runtime headers are missing")
+    exe = b.build_c_client()
+    assert os.path.exists(exe) and os.access(exe, os.X_OK)
