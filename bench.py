@@ -69,15 +69,31 @@ def parse():
                     help="KV-cache element type of the main workload (and of --profile-pass)")
     ap.add_argument("--no-f32", action="store_true",
                     help="skip the fp32 KV-cache measurements (long, mixed and short workloads, session loop)")
+    ap.add_argument("--seed", type=int, default=None,
+                    help="seed of the synthetic one-shot workloads (default: the measurement seed "
+                         "20260623; the session loops keep theirs)")
+    ap.add_argument("--config", default="",
+                    help="JSON object of pkv_config fields applied to every one-shot configuration "
+                         "measured, e.g. '{\"kv_chunk_tokens\": 4096, \"order\": 1}'")
     ap.add_argument("--profile-pass", action="store_true",
                     help="for hardware-counter runs: a few untimed decode steps of the workload, "
                          "then a 1 GiB copy probe of known size (the counter reference)")
     return ap.parse_args()
 
 
+# Run settings from the command line (main): the workload seed and the
+# pkv_config overrides of --config.
+RUN = {"seed": None, "config": {}}
+
+
+def workload(workloads, name, seed=None):
+    seed = RUN["seed"] if seed is None else seed
+    return workloads.CONFIGS[name]() if seed is None else workloads.CONFIGS[name](seed)
+
+
 def measure(torch, pkv, workloads, name, steps, warmup, order, wg_per_cu, copies, gate, say,
             merge="fused", schedule=0, kv="bf16", chunk=0):
-    wl = workloads.CONFIGS[name]().with_kv_dtype(kv)
+    wl = workload(workloads, name).with_kv_dtype(kv)
     dev = "cuda"
     q = wl.q(dev)
     pools = []
@@ -87,12 +103,14 @@ def measure(torch, pkv, workloads, name, steps, warmup, order, wg_per_cu, copies
     lens = wl.ctx_lens_t(dev)
     out = torch.empty(wl.batch, wl.num_q_heads, wl.head_dim, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(wl.batch, wl.num_q_heads, dtype=torch.float32, device=dev)
+    kw = dict(order=pkv.PKV_ORDER_LPT if order == "lpt" else pkv.PKV_ORDER_CANONICAL,
+              wg_per_cu=wg_per_cu, schedule=schedule, kv_chunk_tokens=chunk,
+              kv_dtype=pkv.PKV_KV_F32 if kv == "f32" else pkv.PKV_KV_BF16,
+              merge_mode=pkv.PKV_MERGE_SEPARATE if merge == "separate" else pkv.PKV_MERGE_FUSED)
+    kw["scale"] = wl.scale
+    kw.update(RUN["config"])
     cfg = pkv.make_config(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages, wl.batch,
-                          wl.max_pages_per_seq, scale=wl.scale,
-                          order=pkv.PKV_ORDER_LPT if order == "lpt" else pkv.PKV_ORDER_CANONICAL,
-                          wg_per_cu=wg_per_cu, schedule=schedule, kv_chunk_tokens=chunk,
-                          kv_dtype=pkv.PKV_KV_F32 if kv == "f32" else pkv.PKV_KV_BF16,
-                          merge_mode=pkv.PKV_MERGE_SEPARATE if merge == "separate" else pkv.PKV_MERGE_FUSED)
+                          wl.max_pages_per_seq, **kw)
     stream = torch.cuda.current_stream()
     dec = pkv.PagedDecoder(cfg, stream=stream)
     info = dec.build_queue(wl.ctx_lens)
@@ -442,7 +460,7 @@ def measure_bucketed(torch, pkv, workloads, name, steps, warmup, say):
     one stream.  Returns the step rate and the launches and partial-state bytes
     per step."""
     from oracle import paged_attention as pa
-    wl = workloads.CONFIGS[name]()
+    wl = workload(workloads, name)
     dev = "cuda"
     lens = np.asarray(wl.ctx_lens)
     order = np.argsort(lens, kind="stable")
@@ -552,7 +570,7 @@ def _oracle_worker(args):
     KV head) units (untimed), wait for the others, then run the float64
     oracle over them pass after pass for `seconds` of wall time.  Returns
     (K+V bytes of the units computed, seconds, units)."""
-    root, name, kv, units, seconds, barrier = args
+    root, name, kv, seed, units, seconds, barrier = args
     if root not in sys.path:
         sys.path.insert(0, root)
     from threadpoolctl import threadpool_limits
@@ -560,7 +578,7 @@ def _oracle_worker(args):
     torch.set_num_threads(1)                         # the input generator, too, on this core only
     from oracle import paged_attention as pa
     from paged_kv_attention_persistent_amd import workloads
-    wl = workloads.CONFIGS[name]().with_kv_dtype(kv)
+    wl = (workloads.CONFIGS[name]() if seed is None else workloads.CONFIGS[name](seed)).with_kv_dtype(kv)
     qb = workloads.bits_u16(wl.q("cpu"))
     G = wl.num_q_heads // wl.num_kv_heads
     data = []
@@ -610,7 +628,7 @@ def cpu_baseline(workloads, wl, seconds, say):
             barrier = mgr.Barrier(n_proc)
             with ctx.Pool(n_proc) as pool:
                 out = pool.map(_oracle_worker, [(root, wl.name if wl.name in workloads.CONFIGS else "long",
-                                                 wl.kv_dtype, sh, seconds, barrier) for sh in shares])
+                                                 wl.kv_dtype, RUN["seed"], sh, seconds, barrier) for sh in shares])
         total = sum(o[0] for o in out)
         wall = max(o[1] for o in out)
         res[label] = {"gbs": total / wall / 1e9, "processes": n_proc, "units": sum(o[2] for o in out),
@@ -665,7 +683,7 @@ def tiny_latency(torch, pkv, workloads, steps, say):
     out = torch.empty(wl.batch, wl.num_q_heads, wl.head_dim, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(wl.batch, wl.num_q_heads, dtype=torch.float32, device="cuda")
     cfg = pkv.make_config(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages, wl.batch,
-                          wl.max_pages_per_seq, scale=wl.scale)
+                          wl.max_pages_per_seq, **{"scale": wl.scale, **RUN["config"]})
     dec = pkv.PagedDecoder(cfg)
     t = pkv.make_tensors(q, k, v, bt, lens, out, lse)
     rt = []
@@ -691,19 +709,20 @@ def profile_pass(torch, pkv, workloads, args, say):
     workload (alternating two pool copies), then one copy probe moving
     exactly 1 GiB (read 1 GiB, write 1 GiB), whose counter readings give the
     scale from counter units to bytes."""
-    wl = workloads.CONFIGS[args.workload]().with_kv_dtype(args.kv)
+    wl = workload(workloads, args.workload).with_kv_dtype(args.kv)
     dev = "cuda"
     q = wl.q(dev)
     pools = [(wl.pool("k", dev, False), wl.pool("v", dev, False)) for _ in range(2)]
     bt, lens = wl.block_table_t(dev), wl.ctx_lens_t(dev)
     out = torch.empty(wl.batch, wl.num_q_heads, wl.head_dim, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(wl.batch, wl.num_q_heads, dtype=torch.float32, device=dev)
+    kw = dict(scale=wl.scale, kv_dtype=pkv.PKV_KV_F32 if args.kv == "f32" else pkv.PKV_KV_BF16,
+              schedule={"atomic": pkv.PKV_SCHEDULE_ATOMIC, "static": pkv.PKV_SCHEDULE_STATIC,
+                        "pages": pkv.PKV_SCHEDULE_PAGES, "steal": pkv.PKV_SCHEDULE_STEAL}[args.schedule],
+              merge_mode=pkv.PKV_MERGE_SEPARATE if args.merge == "separate" else pkv.PKV_MERGE_FUSED)
+    kw.update(RUN["config"])
     cfg = pkv.make_config(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages, wl.batch,
-                          wl.max_pages_per_seq, scale=wl.scale,
-                          kv_dtype=pkv.PKV_KV_F32 if args.kv == "f32" else pkv.PKV_KV_BF16,
-                          schedule={"atomic": pkv.PKV_SCHEDULE_ATOMIC, "static": pkv.PKV_SCHEDULE_STATIC,
-                                    "pages": pkv.PKV_SCHEDULE_PAGES, "steal": pkv.PKV_SCHEDULE_STEAL}[args.schedule],
-                          merge_mode=pkv.PKV_MERGE_SEPARATE if args.merge == "separate" else pkv.PKV_MERGE_FUSED)
+                          wl.max_pages_per_seq, **kw)
     dec = pkv.PagedDecoder(cfg)
     info = dec.build_queue(wl.ctx_lens)
     tens = [pkv.make_tensors(q, k, v, bt, lens, out, lse) for k, v in pools]
@@ -739,6 +758,10 @@ def main():
 
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
+    RUN["seed"] = args.seed
+    RUN["config"] = json.loads(args.config) if args.config else {}
+    if not isinstance(RUN["config"], dict):
+        raise SystemExit("--config takes a JSON object of pkv_config fields")
     pkv.lib()
     if args.profile_pass:
         profile_pass(torch, pkv, workloads, args, say)
@@ -823,7 +846,9 @@ def main():
                    "launches_per_step": main_res["launches_per_step"],
                    "kv_bytes_per_step": main_res["kv_bytes"], "grid": main_res["grid"],
                    "order": args.order, "merge": args.merge, "schedule": args.schedule,
-                   "kv_dtype": args.kv}
+                   "kv_dtype": args.kv,
+                   "seed": workloads.MEASURE_SEED if args.seed is None else args.seed,
+                   **({"config_overrides": RUN["config"]} if RUN["config"] else {})}
                   if args.workload == "long" else
                   {"workload": args.workload, "items": main_res["items"], "kv_dtype": args.kv,
                    "kv_bytes_per_step": main_res["kv_bytes"]},

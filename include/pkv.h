@@ -132,6 +132,16 @@ enum {
     PKV_DEVERR_BAD_ITEM = 2     /* item fields out of range; detail = item index */
 };
 
+/* Environment overrides.  Wherever the library resolves a configuration
+ * (pkv_workspace_size, pkv_workspace_layout, pkv_create, pkv_plan_queue,
+ * pkv_decode_noalloc) these variables, when set and not empty, replace the
+ * matching fields before validation, for experiments without rebuilding the
+ * caller: PKV_POLICY = auto | split | nosplit (policy), PKV_CHUNK_TOKENS
+ * (kv_chunk_tokens), PKV_WG_PER_CU (wg_per_cu), PKV_SCHEDULE = atomic |
+ * static | pages | steal (schedule).  A value that does not parse gives
+ * PKV_ERR_INVALID_ARG naming the variable; a parsed value is checked like
+ * the field itself.  Set them the same for every call of one handle's
+ * lifetime: the workspace size depends on them. */
 typedef struct pkv_config {
     uint32_t struct_size;       /* sizeof(pkv_config): ABI version check */
     int32_t num_q_heads;        /* Hq */

@@ -35,7 +35,8 @@ def command(out: str = LIB, extra=()) -> list:
             "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", os.path.join(ROOT, "include"),
-            *[os.path.join(CSRC, s) for s in SOURCES], "-o", out, *extra]
+            *[os.path.join(CSRC, s) for s in SOURCES], "-o", out,
+            "-L", os.path.join(os.path.dirname(os.path.dirname(hipcc())), "lib"), "-lrocprofiler-sdk-roctx", *extra]
 
 
 def build(verbose: bool = False) -> str:

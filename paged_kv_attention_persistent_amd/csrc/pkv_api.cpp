@@ -8,6 +8,7 @@
 // code, in the spirit of that page's kill switches (section 5, "returning an
 // error code to the host").
 #include <hip/hip_runtime.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
 #include <string.h>
 
 #include <chrono>
@@ -20,6 +21,9 @@
 using namespace pkv;
 
 namespace pkv {
+
+ApiRange::ApiRange(const char* name) { roctxRangePushA(name); }
+ApiRange::~ApiRange() { roctxRangePop(); }
 
 DecodeParams decode_params(const Resolved& r, const pkv_layout& lay, unsigned char* ws, const pkv_tensors* t,
                            uint32_t* host_error) {
@@ -388,6 +392,7 @@ PKV_API pkv_status pkv_plan_queue(const pkv_config* cfg, const int32_t* ctx_lens
 
 PKV_API pkv_status pkv_create(const pkv_config* cfg, void* workspace, size_t workspace_bytes,
                               void* stream, pkv_handle** out) {
+    const ApiRange range_("pkv_create");
     if (!out) return PKV_ERR_INVALID_ARG;
     *out = nullptr;
     pkv_handle* h = new (std::nothrow) pkv_handle();
@@ -464,6 +469,7 @@ PKV_API pkv_status pkv_create(const pkv_config* cfg, void* workspace, size_t wor
 
 PKV_API pkv_status pkv_build_queue(pkv_handle* h, const int32_t* ctx_lens_host, int32_t batch,
                                    pkv_queue_info* info) {
+    const ApiRange range_("pkv_build_queue");
     if (!h) return PKV_ERR_INVALID_ARG;
     if (batch < 0 || batch > h->r.max_batch) return fail(h, PKV_ERR_CAPACITY, "batch outside [0, max_batch]");
     if (batch > 0 && !ctx_lens_host) return fail(h, PKV_ERR_INVALID_ARG, "null ctx_lens");
@@ -527,6 +533,7 @@ PKV_API pkv_status pkv_build_queue(pkv_handle* h, const int32_t* ctx_lens_host, 
 
 PKV_API pkv_status pkv_build_queue_device(pkv_handle* h, const int32_t* ctx_lens_device, int32_t batch,
                                           void* stream) {
+    const ApiRange range_("pkv_build_queue_device");
     if (!h) return PKV_ERR_INVALID_ARG;
     if (batch < 0 || batch > h->r.max_batch) return fail(h, PKV_ERR_CAPACITY, "batch outside [0, max_batch]");
     if (batch > 4096) return fail(h, PKV_ERR_UNSUPPORTED, "device builder supports batch <= 4096");
@@ -550,6 +557,7 @@ PKV_API pkv_status pkv_build_queue_device(pkv_handle* h, const int32_t* ctx_lens
 }
 
 PKV_API pkv_status pkv_decode(pkv_handle* h, const pkv_tensors* t, void* stream) {
+    const ApiRange range_("pkv_decode");
     if (!h) return PKV_ERR_INVALID_ARG;
     if (!h->built) return fail(h, PKV_ERR_STATE, "pkv_decode before pkv_build_queue");
     pkv_status s = check_tensors(h, t);
@@ -738,6 +746,7 @@ PKV_API pkv_status pkv_debug_gather(pkv_handle* h, const pkv_tensors* t, int32_t
 }
 
 PKV_API pkv_status pkv_destroy(pkv_handle* h) {
+    const ApiRange range_("pkv_destroy");
     if (!h) return PKV_ERR_INVALID_ARG;
     stop_loop(h);
     if (h->stream || h->staging[0]) (void)hipStreamSynchronize(h->stream);

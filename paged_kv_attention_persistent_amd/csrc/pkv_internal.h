@@ -221,6 +221,15 @@ struct BuildParams {
 };
 
 // Kernel parameters over a workspace laid out by compute_layout (pkv_api.cpp).
+// A roctx range around a C-ABI call (seen by rocprofv3 --marker-trace);
+// defined in pkv_api.cpp.
+struct ApiRange {
+    explicit ApiRange(const char* name);
+    ~ApiRange();
+    ApiRange(const ApiRange&) = delete;
+    ApiRange& operator=(const ApiRange&) = delete;
+};
+
 DecodeParams decode_params(const Resolved& r, const pkv_layout& lay, unsigned char* ws, const pkv_tensors* t,
                            uint32_t* host_error);
 BuildParams build_params(const Resolved& r, const pkv_layout& lay, unsigned char* ws, const int32_t* ctx_lens,

@@ -45,6 +45,7 @@ using namespace pkv;
 extern "C" PKV_API pkv_status pkv_decode_noalloc(const pkv_config* cfg, const int32_t* ctx_lens_device,
                                                  int32_t batch, const pkv_tensors* t, uint32_t* error_word,
                                                  void* stream) {
+    const ApiRange range_("pkv_decode_noalloc");
     if (!cfg || !t) return PKV_ERR_INVALID_ARG;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices ||

@@ -11,6 +11,7 @@
 // becomes the no-split route; the threshold is the occupancy rule
 // B * Hkv < CUs with some row longer than one range.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -20,10 +21,59 @@
 
 namespace pkv {
 
-pkv_status resolve_config(const pkv_config* cfg, int device_cus, Resolved* r, const char** why) {
+namespace {
+
+// Environment overrides of a few config fields, for experiments without
+// rebuilding the caller: PKV_POLICY (auto | split | nosplit),
+// PKV_CHUNK_TOKENS (kv_chunk_tokens), PKV_WG_PER_CU (wg_per_cu) and
+// PKV_SCHEDULE (atomic | static | pages | steal).  An empty variable is
+// unset; a value that does not parse is refused naming the variable (the
+// overridden fields are then checked like any config).
+bool env_int(const char* name, int32_t* out, const char** why) {
+    const char* v = getenv(name);
+    if (!v || !*v) return true;
+    char* end = nullptr;
+    const long x = strtol(v, &end, 10);
+    if (*end || x < INT32_MIN || x > INT32_MAX) { *why = name; return false; }
+    *out = (int32_t)x;
+    return true;
+}
+
+bool env_choice(const char* name, const char* const* names, int n, int32_t* out, const char** why) {
+    const char* v = getenv(name);
+    if (!v || !*v) return true;
+    for (int i = 0; i < n; ++i)
+        if (!strcmp(v, names[i])) { *out = i; return true; }
+    *why = name;
+    return false;
+}
+
+pkv_status apply_env(pkv_config* c, const char** why) {
+    static const char* const policies[] = {"auto", "nosplit", "split"};      // PKV_POLICY_* order
+    static const char* const schedules[] = {"atomic", "static", "pages", "steal"};
+    const char* bad = nullptr;
+    if (!env_choice("PKV_POLICY", policies, 3, &c->policy, &bad) ||
+        !env_int("PKV_CHUNK_TOKENS", &c->kv_chunk_tokens, &bad) ||
+        !env_int("PKV_WG_PER_CU", &c->wg_per_cu, &bad) ||
+        !env_choice("PKV_SCHEDULE", schedules, 4, &c->schedule, &bad)) {
+        *why = !strcmp(bad, "PKV_POLICY") ? "PKV_POLICY must be auto, split or nosplit"
+             : !strcmp(bad, "PKV_SCHEDULE") ? "PKV_SCHEDULE must be atomic, static, pages or steal"
+             : !strcmp(bad, "PKV_CHUNK_TOKENS") ? "PKV_CHUNK_TOKENS is not an integer"
+                                                : "PKV_WG_PER_CU is not an integer";
+        return PKV_ERR_INVALID_ARG;
+    }
+    return PKV_OK;
+}
+
+}  // namespace
+
+pkv_status resolve_config(const pkv_config* user_cfg, int device_cus, Resolved* r, const char** why) {
     *why = "";
-    if (!cfg || !r) { *why = "null config"; return PKV_ERR_INVALID_ARG; }
-    if (cfg->struct_size != sizeof(pkv_config)) { *why = "pkv_config.struct_size mismatch"; return PKV_ERR_INVALID_ARG; }
+    if (!user_cfg || !r) { *why = "null config"; return PKV_ERR_INVALID_ARG; }
+    if (user_cfg->struct_size != sizeof(pkv_config)) { *why = "pkv_config.struct_size mismatch"; return PKV_ERR_INVALID_ARG; }
+    pkv_config env_cfg = *user_cfg;
+    if (apply_env(&env_cfg, why) != PKV_OK) return PKV_ERR_INVALID_ARG;
+    const pkv_config* cfg = &env_cfg;
     for (int i = 0; i < 2; ++i)
         if (cfg->reserved[i]) { *why = "reserved config fields must be zero"; return PKV_ERR_INVALID_ARG; }
     if (cfg->num_q_heads <= 0 || cfg->num_kv_heads <= 0 || cfg->num_q_heads % cfg->num_kv_heads) {

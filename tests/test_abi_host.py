@@ -284,3 +284,37 @@ def test_plain_c_client_compiles_against_the_header():
         pytest.skip("gcc or the HIP runtime headers are missing")
     exe = b.build_c_client()
     assert os.path.exists(exe) and os.access(exe, os.X_OK)
+
+
+def test_environment_overrides(monkeypatch):
+    # PKV_POLICY / PKV_CHUNK_TOKENS / PKV_WG_PER_CU / PKV_SCHEDULE override the
+    # config wherever the library resolves it; bad values are refused loudly
+    for name in ("PKV_POLICY", "PKV_CHUNK_TOKENS", "PKV_WG_PER_CU", "PKV_SCHEDULE"):
+        monkeypatch.delenv(name, raising=False)
+    cfg = pkv.make_config(32, 8, 128, 8192, 1, 8192, num_cus=256)
+    lens = [131072]
+    *_, info = pkv.pkv_plan_queue(cfg, lens)
+    assert info.split == 1 and info.chunk_tokens == 4096 and info.n_items == 256
+    monkeypatch.setenv("PKV_POLICY", "nosplit")
+    *_, info = pkv.pkv_plan_queue(cfg, lens)
+    assert info.split == 0 and info.n_items == 8
+    monkeypatch.setenv("PKV_POLICY", "split")
+    monkeypatch.setenv("PKV_CHUNK_TOKENS", "8192")
+    *_, info = pkv.pkv_plan_queue(cfg, lens)
+    assert info.split == 1 and info.chunk_tokens == 8192 and info.n_items == 128
+    monkeypatch.setenv("PKV_CHUNK_TOKENS", "")                 # empty: unset
+    *_, info = pkv.pkv_plan_queue(cfg, lens)
+    assert info.chunk_tokens == 4096
+    monkeypatch.setenv("PKV_SCHEDULE", "steal")
+    steal = pkv.pkv_workspace_layout(cfg)
+    monkeypatch.delenv("PKV_SCHEDULE")
+    plain = pkv.pkv_workspace_layout(cfg)
+    assert steal.loop_off - steal.cursor_off == 4 * 32 * 8 * 8 and plain.loop_off == plain.cursor_off
+    for name, value in (("PKV_POLICY", "sometimes"), ("PKV_CHUNK_TOKENS", "4k"), ("PKV_CHUNK_TOKENS", "100"),
+                        ("PKV_WG_PER_CU", "9"), ("PKV_SCHEDULE", "random")):
+        monkeypatch.setenv(name, value)
+        with pytest.raises(pkv.PkvError):
+            pkv.pkv_plan_queue(cfg, lens)
+        monkeypatch.delenv(name)
+    *_, info = pkv.pkv_plan_queue(cfg, lens)
+    assert info.split == 1 and info.chunk_tokens == 4096

@@ -90,7 +90,7 @@ def test_host_library_under_asan_ubsan_passes_the_abi_tests(tmp_path):
     cmd = [HIPCC, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC", "-shared",
            "-fvisibility=hidden", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
            "-Xarch_host", "-fno-omit-frame-pointer", "-shared-libsan", "-I", os.path.join(ROOT, "include"), *srcs,
-           "-o", lib]
+           "-o", lib, "-L/opt/rocm/lib", "-lrocprofiler-sdk-roctx"]
     r = run(cmd)
     assert r.returncode == 0, r.stderr
     out = run(["nm", "-D", lib]).stdout
