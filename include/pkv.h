@@ -335,8 +335,10 @@ PKV_API pkv_status pkv_build_queue_device(pkv_handle* h, const int32_t* ctx_lens
  * the built queue's. */
 PKV_API pkv_status pkv_decode(pkv_handle* h, const pkv_tensors* t, void* stream);
 
-/* Optional timing: hipEvent_t handles recorded on the decode stream right
- * before and right after the persistent decode kernel (not the merge).  Pass
+/* Optional timing: hipEvent_t handles (the caller's, created and destroyed by
+ * the caller) recorded on the decode stream right before and right after
+ * each one-shot decode kernel (not the separate merge; the resident loop
+ * records neither).  PKV_ERR_INVALID_ARG when exactly one is null.  Pass
  * nulls to stop recording. */
 PKV_API pkv_status pkv_set_decode_events(pkv_handle* h, void* before, void* after);
 
@@ -360,11 +362,17 @@ PKV_API pkv_status pkv_loop_set_free_pages(pkv_handle* h, const int32_t* pages, 
 PKV_API pkv_status pkv_loop_free_pages(const pkv_handle* h, int32_t* n);
 
 /* Optional per-item trace (diagnostics): when buf (device memory, 32 bytes x
- * capacity) is set, every decode launch writes, for each item it runs,
- * uint64 {item index | workgroup << 32, start clock, end clock,
- * hardware id | XCC id << 32} at slot item index (items at or beyond
- * capacity are not traced).  Clocks are the 100 MHz device wall clock.
- * Pass null to stop tracing. */
+ * capacity) is set, every one-shot decode launch (the resident loop records
+ * none) writes four uint64 words per record, at slots below capacity only:
+ *   item i, at slot i:             {i | workgroup << 32, start clock,
+ *                                   end clock, hardware id | XCC id << 32};
+ *   workgroup w, at slot n_items + w: {w | w << 32 | 1 << 63, clock at entry,
+ *                                   clock when its first item starts,
+ *                                   hardware id | XCC id << 32}.
+ * Clocks are the 100 MHz device wall clock.  Slots at or beyond capacity and
+ * slots of items that did not run are left as they were.  PKV_ERR_INVALID_ARG
+ * for a buffer not 8-byte aligned or a capacity <= 0 with a buffer.  Pass
+ * null to stop tracing. */
 PKV_API pkv_status pkv_set_trace(pkv_handle* h, void* buf, int32_t capacity);
 
 /* Streaming copy of `bytes` (a multiple of 16) from src to dst on stream,
