@@ -87,7 +87,10 @@ enum { PKV_ORDER_CANONICAL = 0, PKV_ORDER_LPT = 1 };
 
 /* Item-to-workgroup assignment in one-shot launches.  ATOMIC (default): the
  * PersistentKV page's work queue -- workgroup g runs item g first, then claims
- * further items with an atomic counter as it finishes.  STATIC: the WPK note's
+ * further items with an atomic counter as it finishes (no claims at all when
+ * the queue has no more items than workgroups: the first round covers it).
+ * Consecutive launches of a handle use two such counters in turn, each
+ * launch clearing the other's for the next.  STATIC: the WPK note's
  * compiled schedule -- workgroup g runs items g, g + grid, g + 2 grid, ...
  * with no claims.  Every item is computed the same way in both, so outputs
  * are identical; only the time differs (a scheduling ablation).  PAGES: items
@@ -212,8 +215,9 @@ typedef struct pkv_runtime_info {
     uint32_t error_detail;
     uint32_t queue_head;        /* next item index the kernel would pop (0 when idle) */
     uint32_t n_items;           /* items of the current queue */
-    uint32_t items_done;        /* items finished since create (wraps) */
-    uint32_t decode_calls;      /* pkv_decode calls since create */
+    uint32_t items_done;        /* items run by one-shot decode launches since create,
+                                   counted as each starts (wraps) */
+    uint32_t decode_calls;      /* one-shot decode launches since create */
     int32_t grid;               /* persistent workgroups per decode launch */
     int32_t num_cus;            /* CUs of the device */
     uint32_t loop_out_epoch;    /* resident loop: last completed step (0 before the first) */

@@ -51,7 +51,9 @@ DecodeParams decode_params(const Resolved& r, const pkv_layout& lay, unsigned ch
     p.arrive = reinterpret_cast<uint32_t*>(ws + lay.arrive_off);
     p.trace = nullptr;
     p.trace_cap = 0;
-    p.head = &reinterpret_cast<Ctrl*>(ws + lay.ctrl_off)->head;
+    p.head = &reinterpret_cast<Ctrl*>(ws + lay.ctrl_off)->head[0];
+    p.head_next = &reinterpret_cast<Ctrl*>(ws + lay.ctrl_off)->head[1];
+    p.done_lines = reinterpret_cast<uint32_t*>(ws + lay.ctrl_off + sizeof(Ctrl));
     p.head_dim = r.d;
     p.coherent_out = 0;
     p.static_first = 1;
@@ -140,6 +142,7 @@ struct pkv_handle {
     hipEvent_t ev_after = nullptr;
     uint64_t* trace = nullptr;
     int32_t trace_cap = 0;
+    uint32_t parity = 0;                // pop counter of the next one-shot launch (Ctrl::head)
     // resident loop
     LoopCtrl* lctrl = nullptr;          // host view (fine-grained, mapped)
     LoopCtrl* lctrl_dev = nullptr;
@@ -173,6 +176,9 @@ DecodeParams make_params(const pkv_handle* h, const pkv_tensors* t) {
     DecodeParams p = decode_params(h->r, h->lay, h->ws, t, h->host_err_dev);
     p.trace = h->trace;
     p.trace_cap = h->trace_cap;
+    Ctrl* c = reinterpret_cast<Ctrl*>(h->ws + h->lay.ctrl_off);
+    p.head = &c->head[h->parity];
+    p.head_next = &c->head[h->parity ^ 1];
     return p;
 }
 
@@ -582,6 +588,7 @@ PKV_API pkv_status pkv_decode(pkv_handle* h, const pkv_tensors* t, void* stream)
     if (h->ev_before && (e = hipEventRecord(h->ev_before, st)) != hipSuccess) return hip_fail(h, e, "event record");
     int rc = launch_decode(p, h->r.d, h->r.g, h->r.kv_dtype, h->grid, st);
     if (rc != 0) return hip_fail(h, (hipError_t)rc, "decode launch");
+    h->parity ^= 1u;
     if (h->ev_after && (e = hipEventRecord(h->ev_after, st)) != hipSuccess) return hip_fail(h, e, "event record");
     const int merge_rows = h->built_on_device ? h->batch : h->qinfo.n_merge_rows;
     if (h->r.merge_mode == PKV_MERGE_SEPARATE && merge_rows > 0) {
@@ -671,17 +678,20 @@ PKV_API pkv_status pkv_query(pkv_handle* h, pkv_runtime_info* info) {
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(h, e, "device sync");
     Ctrl c;
+    uint32_t lines[kDoneLines * 32];
     QHdr q;
-    if ((e = hipMemcpy(&c, h->ws + h->lay.ctrl_off, sizeof(c), hipMemcpyDeviceToHost)) != hipSuccess)
+    if ((e = hipMemcpy(&c, h->ws + h->lay.ctrl_off, sizeof(c), hipMemcpyDeviceToHost)) != hipSuccess ||
+        (e = hipMemcpy(lines, h->ws + h->lay.ctrl_off + sizeof(Ctrl), sizeof(lines), hipMemcpyDeviceToHost)) !=
+            hipSuccess)
         return hip_fail(h, e, "ctrl read");
     if ((e = hipMemcpy(&q, h->ws + h->lay.queue_off, sizeof(q), hipMemcpyDeviceToHost)) != hipSuccess)
         return hip_fail(h, e, "queue header read");
     memset(info, 0, sizeof(*info));
     info->error_code = c.error_code;
     info->error_detail = c.error_detail;
-    info->queue_head = c.head;
+    info->queue_head = c.head[h->parity];
     info->n_items = (uint32_t)q.n_items;
-    info->items_done = c.items_done;
+    for (int i = 0; i < kDoneLines; ++i) info->items_done += lines[32 * i];
     info->decode_calls = c.decode_calls;
     info->grid = h->grid;
     info->num_cus = h->device_cus;

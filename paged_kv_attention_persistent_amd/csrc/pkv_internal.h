@@ -28,17 +28,25 @@ struct Item {
 };
 static_assert(sizeof(Item) == 16, "item is 16 bytes");
 
-// Control words at the start of the workspace (device memory).
+// Control words at the start of the workspace (device memory).  One-shot
+// launches alternate between two pop counters: launch k pops from
+// head[k & 1] and zeroes head[(k + 1) & 1], which the next launch uses (the
+// launches of a handle run one after another), so no launch has to count its
+// workgroups out to re-arm its counter.
 struct Ctrl {
-    uint32_t head;          // next item to pop; reset to 0 by the last workgroup out
-    uint32_t done;          // workgroups finished in the current launch
+    uint32_t head[2];       // pop counters of alternate one-shot launches
     uint32_t error_code;    // PKV_DEVERR_*
     uint32_t error_detail;
-    uint32_t items_done;
-    uint32_t decode_calls;
-    uint32_t pad[58];
+    uint32_t decode_calls;  // one-shot decode launches
+    uint32_t pad[59];
 };
 static_assert(sizeof(Ctrl) == 256, "ctrl is 256 bytes");
+// Items run by one-shot launches, counted as each starts in kDoneLines
+// counters one 128-byte line apart (workgroup g adds to counter
+// g mod kDoneLines), right after Ctrl, so that the adds of many workgroups
+// never queue on one address.  The host sums the counters.
+constexpr int kDoneLines = 64;
+constexpr uint64_t kCtrlBytes = sizeof(Ctrl) + (uint64_t)kDoneLines * 128;
 
 // Queue header, first bytes of the queue region.
 struct QHdr {
@@ -156,6 +164,8 @@ struct DecodeParams {
     uint32_t* arrive;           // [max_batch][Hkv] arrival counters (fused merge)
     uint64_t* trace;            // per-item trace records (nullable)
     uint32_t* head;             // pop counter of this queue
+    uint32_t* head_next;        // one-shot: the next launch's pop counter, zeroed at the start (nullable)
+    uint32_t* done_lines;       // one-shot: items-run counters (kDoneLines, 32 words apart; nullable)
     int32_t trace_cap;
     int32_t head_dim;
     int32_t coherent_out;       // 1: outputs stored system-coherently (resident loop)

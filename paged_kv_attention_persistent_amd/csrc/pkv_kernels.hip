@@ -838,7 +838,18 @@ __device__ void merge_row(const DecodeParams& P, int b, int hk, int nc, int base
 // Under the static schedule the next item is simply idx + grid.
 __device__ __forceinline__ uint32_t pop_next(const DecodeParams& P, uint32_t idx) {
     if (P.static_sched) return idx + gridDim.x;
+    if (P.static_first && (uint32_t)P.qhdr->n_items <= gridDim.x) return gridDim.x;
     return (P.static_first ? gridDim.x : 0u) + atomicAdd(P.head, 1u);
+}
+
+// Whether a workgroup finishing an item must claim another.  Not under the
+// static schedule, and not in a one-shot launch whose static first round
+// already covers the queue (no more items than workgroups): there every
+// claim would come back empty, and the claims of all workgroups would queue
+// on the one device-scope counter as their items end.
+__device__ __forceinline__ bool claims_needed(const DecodeParams& P) {
+    if (P.static_sched) return false;
+    return !P.static_first || (uint32_t)P.qhdr->n_items > gridDim.x;
 }
 
 // One queue item, decoded and checked (all fields wave-uniform).
@@ -996,7 +1007,7 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, const ItemRe
     // barrier below, so its round trip overlaps the reductions and the wait
     // for the other waves.
     uint32_t popped = 0;
-    if (tid == 0 && !P.static_sched) {
+    if (tid == 0 && claims_needed(P)) {
         // A lane-private copy of the address keeps the compiler from turning
         // this one-lane atomic into its wave-wide form, which reads the
         // result at once.
@@ -1107,6 +1118,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
     Ctrl* ctrl = P.ctrl;
     const uint32_t n_items = (uint32_t)P.qhdr->n_items;
     const uint64_t t_enter = P.trace ? wall_clock64() : 0;
+    if (blockIdx.x == 0 && tid == 0) {
+        // the next launch's pop counter: idle since the previous launch ended
+        if (P.head_next) __hip_atomic_store(P.head_next, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        atomicAdd(&ctrl->decode_calls, 1u);
+    }
     if (P.fused_merge) {                 // rows with no tokens take the neutral state
         const int n_rows = P.qhdr->n_merge_rows;
         for (int ri = blockIdx.x; ri < n_rows; ri += gridDim.x) {
@@ -1120,7 +1136,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
         }
     }
     uint32_t idx = blockIdx.x;                     // first round: static assignment
-    uint32_t done_here = 0;
     if (P.trace && tid == 0 && n_items + blockIdx.x < (uint32_t)P.trace_cap) {
         // workgroup record after the item records: entry time, start of work
         uint64_t* rec = P.trace + 4ull * (n_items + blockIdx.x);
@@ -1134,8 +1149,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
         uint32_t nxt = 0;
         uint64_t t_start = 0;
         if (P.trace) t_start = wall_clock64();
+        // counted as the item starts, so the add's round trip overlaps the
+        // item instead of lengthening the launch's end
+        if (tid == 0 && P.done_lines) atomicAdd(P.done_lines + 32 * (blockIdx.x % kDoneLines), 1u);
         process_item<D, G, KV, true>(P, sm, read_item(P, idx), nxt);
-        ++done_here;
         if (P.trace && tid == 0 && idx < (uint32_t)P.trace_cap) {
             const uint64_t t_end = wall_clock64();
             const uint32_t hw = __builtin_amdgcn_s_getreg((4 << 0) | (0 << 6) | (31 << 11));   // HW_ID
@@ -1150,17 +1167,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams P) {
         if (tid == 0) sm.next = nxt;
         __syncthreads();
         idx = __builtin_amdgcn_readfirstlane(sm.next);
-    }
-    if (tid == 0) {
-        // Thread 0's last pop has returned before this point, so when the
-        // done count completes no workgroup can pop again: re-arm the head.
-        if (done_here) atomicAdd(&ctrl->items_done, done_here);
-        const uint32_t prev = atomicAdd(&ctrl->done, 1u);
-        if (prev == gridDim.x - 1) {                        // last workgroup out re-arms
-            atomicExch(&ctrl->head, 0u);
-            atomicExch(&ctrl->done, 0u);
-            atomicAdd(&ctrl->decode_calls, 1u);
-        }
     }
 }
 
@@ -1783,8 +1789,9 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* __restrict
 }
 
 __global__ void init_ctrl_kernel(Ctrl* c, uint32_t* arrive, int n_arrive) {
-    uint32_t* w = reinterpret_cast<uint32_t*>(c);
-    if (blockIdx.x == 0 && threadIdx.x < sizeof(Ctrl) / 4) w[threadIdx.x] = 0u;
+    uint32_t* w = reinterpret_cast<uint32_t*>(c);          // Ctrl and the items-done counters
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < (int)(kCtrlBytes / 4); i += gridDim.x * blockDim.x)
+        w[i] = 0u;
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_arrive; i += gridDim.x * blockDim.x)
         arrive[i] = 0u;
 }

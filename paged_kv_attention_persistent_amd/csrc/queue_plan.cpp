@@ -167,7 +167,7 @@ void compute_layout(const Resolved& r, pkv_layout* lay) {
     memset(lay, 0, sizeof(*lay));
     uint64_t off = 0;
     lay->ctrl_off = off;
-    off = align256(off + sizeof(Ctrl));
+    off = align256(off + kCtrlBytes);
     lay->queue_off = off;
     off = align256(off + sizeof(QHdr));
     lay->n_chunks_off = off;
