@@ -1017,28 +1017,72 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, const ItemRe
         popped = __hip_atomic_fetch_add(head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    // Combine the 8 token groups of this wave (lanes r = 0..7 with equal p).
+    // Combine the 8 token groups of this wave (lanes r = 0..7 with equal p):
+    // each lane's state is rescaled to the group maximum, then summed over
+    // lane bits 3..5 and written to LDS.
+    constexpr int DPW = KV::kDimsPerWord;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         const float M = groups_max(st.m[g]);
         const float a = __builtin_amdgcn_exp2f(st.m[g] - M);
-        const float l = groups_sum(st.l[g] * a);
-#pragma unroll
-        for (int e = 0; e < D / 8; ++e) st.acc[g][e] = groups_sum(st.acc[g][e] * a);
+        st.l[g] = groups_sum(st.l[g] * a);
         st.m[g] = M;
-        st.l[g] = l;
+#pragma unroll
+        for (int e = 0; e < D / 8; ++e) st.acc[g][e] *= a;
     }
-    if (r == 0) {
-        constexpr int DPW = KV::kDimsPerWord;
+    if constexpr (KV::kBytes == 2) {
+        // bf16 cache: a reduce-scatter of the V = G * D / 8 accumulator
+        // values.  Each row-swap permute exchanges half of two registers, so
+        // one permute and one add fold two values over a lane bit; after bits
+        // 5, 4 and 3 lane r holds the sums of values r * V / 8 ..
+        // (r + 1) * V / 8 - 1, and every lane writes its share.  (About a
+        // third of the instructions of summing every value on every lane;
+        // under the fp32 cache's register pressure its extra live values
+        // cost more than it saves, so that cache keeps the all-reduce below.)
+        constexpr int V = G * (D / 8);
+        float v1[V / 2];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-#pragma unroll
-            for (int ww = 0; ww < Tile<D, KV>::NW; ++ww)
-#pragma unroll
-                for (int e = 0; e < DPW; ++e)
-                    sm.acc[w][g * D + word_dim<KV>(p, ww, e)] = st.acc[g][ww * DPW + e];
-            if (p == 0) { sm.m[w][g] = st.m[g]; sm.l[w][g] = st.l[g]; }
+        for (int i = 0; i < V / 2; ++i) {       // bit 5: lanes 0-31 keep the low half
+            const int g0 = i / (D / 8), e0 = i % (D / 8);
+            const int g1 = (V / 2 + i) / (D / 8), e1 = (V / 2 + i) % (D / 8);
+            const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.acc[g0][e0]),
+                                                            __float_as_uint(st.acc[g1][e1]), false, false);
+            v1[i] = __uint_as_float(t[0]) + __uint_as_float(t[1]);
         }
+        float v2[V / 4];
+#pragma unroll
+        for (int i = 0; i < V / 4; ++i) {       // bit 4: even 16-lane rows keep the low half
+            const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(v1[i]), __float_as_uint(v1[V / 4 + i]),
+                                                            false, false);
+            v2[i] = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+        }
+        const bool b3 = (lane >> 3) & 1;        // bit 3: the partner is 8 lanes away in the row
+#pragma unroll
+        for (int i = 0; i < V / 8; ++i) {
+            const float keep = b3 ? v2[V / 8 + i] : v2[i];
+            const float send = b3 ? v2[i] : v2[V / 8 + i];
+            const int j = r * (V / 8) + i;
+            const int g = j / (D / 8), e = j % (D / 8);
+            sm.acc[w][g * D + word_dim<KV>(p, e / DPW, e % DPW)] = keep + dpp_f<0x128>(send);
+        }
+    } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int e = 0; e < D / 8; ++e) st.acc[g][e] = groups_sum(st.acc[g][e]);
+        if (r == 0) {
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int ww = 0; ww < Tile<D, KV>::NW; ++ww)
+#pragma unroll
+                    for (int e = 0; e < DPW; ++e)
+                        sm.acc[w][g * D + word_dim<KV>(p, ww, e)] = st.acc[g][ww * DPW + e];
+        }
+    }
+    if (r == 0 && p == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) { sm.m[w][g] = st.m[g]; sm.l[w][g] = st.l[g]; }
     }
     __syncthreads();
     if (tid == 0) {
