@@ -187,11 +187,40 @@ def test_tiny_workload_and_repeat_calls():
     wl = workloads.tiny()
     run = Run(wl)
     ro, rl = oracle_full(wl)
-    for i in range(3):                                   # head counter re-arms each launch
+    for i in range(3):                                   # each launch finds its pop counter at zero
         o, l = run.decode()
         check(o, l, ro, rl, f"tiny call {i}")
     st = run.dec.query()
     assert st["decode_calls"] == 3 and st["queue_head"] == 0 and st["items_done"] == 3
+    run.close()
+
+
+@pytest.mark.parametrize("rows,sched", [(40, "atomic"), (4, "atomic"), (40, "static")])
+def test_claim_counters_alternate_between_launches(rows, sched):
+    """One-shot launches pop from two counters in turn, each launch zeroing
+    the other for the next one.  Every item is followed by one claim when the
+    queue has more items than workgroups (so a launch makes exactly n_items
+    claims, the last grid of them empty), none when the static first round
+    covers the queue or under the static schedule; results are unchanged."""
+    lens = [int(x) for x in np.random.default_rng(rows).integers(1, 3000, size=rows)]
+    wl = workloads.custom(f"claims{rows}", lens, 32, 8, 128)
+    run = Run(wl, schedule=pkv.PKV_SCHEDULE_STATIC if sched == "static" else pkv.PKV_SCHEDULE_ATOMIC)
+    ro, rl = oracle_full(wl)
+    lay = run.dec.layout
+    n_items, grid = None, None
+    for call in range(4):
+        o, l = run.decode()
+        check(o, l, ro, rl, f"claims {rows} {sched} call {call}")
+        st = run.dec.query()
+        n_items, grid = st["n_items"], st["grid"]
+        heads = run.dec.workspace[lay.ctrl_off:lay.ctrl_off + 8].cpu().view(torch.int32).numpy()
+        claims = n_items if (sched == "atomic" and n_items > grid) else 0
+        used = call % 2                                  # launch k pops from counter k mod 2
+        assert heads[used] == claims and heads[1 - used] == 0, (call, heads.tolist(), n_items, grid)
+        assert st["queue_head"] == 0 and st["decode_calls"] == call + 1
+        assert st["items_done"] == n_items * (call + 1)
+    say(f"claims rows {rows} {sched}: items {n_items}, grid {grid}")
+    assert (n_items > grid) == (rows == 40), (n_items, grid)     # both regimes are covered
     run.close()
 
 
