@@ -224,6 +224,51 @@ def test_claim_counters_alternate_between_launches(rows, sched):
     run.close()
 
 
+
+@pytest.mark.parametrize("sched", list(SCHEDULES))
+@pytest.mark.parametrize("device_queue", [False, True])
+def test_wide_block_table_and_batch_below_capacity(sched, device_queue):
+    """A block table whose rows are wider than max_pages_per_seq
+    (block_table_stride) with out-of-pool ids in every padding column, and a
+    batch of 5 on a configuration sized for 8: every output against the
+    oracle on two calls in a row, no page fault reported (the padding is
+    never read), under each schedule and both queue builders."""
+    lens = [37, 1000, 0, 20000, 300]
+    wl = workloads.custom("wide_bt", lens, 8, 2, 128, spare_pages=3)
+    dev = "cuda"
+    maxp = wl.max_pages_per_seq
+    stride = maxp + 13
+    bt = torch.full((wl.batch, stride), 1 << 30, dtype=torch.int32)
+    bt[:, maxp:] = torch.tensor([-5, wl.num_pages, 1 << 30] * 5, dtype=torch.int32)[:stride - maxp]
+    bt[:, :maxp] = torch.as_tensor(wl.block_table)
+    bt = bt.to(dev)
+    cfg = pkv.make_config(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_pages, 8, maxp, scale=wl.scale,
+                          kv_chunk_tokens=2048, schedule=SCHEDULES[sched],
+                          num_cus=torch.cuda.get_device_properties(0).multi_processor_count)
+    dec = pkv.PagedDecoder(cfg)
+    q, k, v = wl.q(dev), wl.pool("k", dev, True), wl.pool("v", dev, True)
+    lens_t = wl.ctx_lens_t(dev)
+    out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((wl.batch, wl.num_q_heads), dtype=torch.float32, device=dev)
+    t = pkv.make_tensors(q, k, v, bt, lens_t, out, lse)
+    assert t.block_table_stride == stride
+    ro, rl = oracle_full(wl)
+    try:
+        for call in range(2):
+            out.fill_(float("nan"))
+            lse.fill_(float("nan"))
+            if device_queue:
+                dec.build_queue_device(lens_t)
+            else:
+                dec.build_queue(wl.ctx_lens)
+            pkv.pkv_decode(dec.handle, t, dec.stream)
+            torch.cuda.synchronize()
+            assert dec.query()["error_code"] == 0
+            check(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ro, rl,
+                  f"wide block table {sched} device_queue={device_queue} call {call}")
+    finally:
+        dec.close()
+
 # ------------------------------------------------------ full-size cases ----
 
 _ORACLE_CACHE = {}
