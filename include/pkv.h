@@ -240,7 +240,8 @@ typedef struct pkv_layout {
                                    u16 chunk, u32 tok_begin, u32 tok_end */
     uint64_t partial_o_off;     /* fp32 [layers][max_items][G][D], normalised partial outputs */
     uint64_t partial_lse_off;   /* fp32 [layers][max_items][G], natural-log partial LSE */
-    uint64_t arrive_off;        /* uint32 [layers][max_batch][Hkv] arrival counters of the fused merge */
+    uint64_t arrive_off;        /* uint32 [layers][max_batch][Hkv] arrival counters of the fused merge,
+                                   then uint32 [max_items] counters of its two-level form */
     uint64_t cursor_off;        /* PKV_SCHEDULE_PAGES: uint32 page cursors, one 128-byte line per
                                    (row, KV head); PKV_SCHEDULE_STEAL: one per (row, KV head,
                                    wave), 8 waves; empty otherwise */

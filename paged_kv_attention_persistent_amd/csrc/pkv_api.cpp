@@ -49,6 +49,7 @@ DecodeParams decode_params(const Resolved& r, const pkv_layout& lay, unsigned ch
     p.steal = r.schedule == PKV_SCHEDULE_STEAL ? 1 : 0;
     p.partial_lse = reinterpret_cast<float*>(ws + lay.partial_lse_off);
     p.arrive = reinterpret_cast<uint32_t*>(ws + lay.arrive_off);
+    p.grp_arrive = p.arrive + (size_t)r.max_batch * r.hkv * r.num_layers;
     p.trace = nullptr;
     p.trace_cap = 0;
     p.head = &reinterpret_cast<Ctrl*>(ws + lay.ctrl_off)->head[0];
@@ -448,7 +449,7 @@ PKV_API pkv_status pkv_create(const pkv_config* cfg, void* workspace, size_t wor
     memset(h->host_err, 0, 64);
     int rc = launch_init_ctrl(reinterpret_cast<Ctrl*>(h->ws + h->lay.ctrl_off),
                               reinterpret_cast<uint32_t*>(h->ws + h->lay.arrive_off),
-                              h->r.max_batch * h->r.hkv * h->r.num_layers, h->stream);
+                              (int)arrive_words(h->r), h->stream);
     if (rc == 0 && h->r.persistent)
         rc = launch_zero(h->ws + h->lay.loop_off, sizeof(LoopGlobal) + 2 * loop_counter_bytes(h->r), h->stream);
     if (rc == 0 && (h->r.schedule == PKV_SCHEDULE_PAGES || h->r.schedule == PKV_SCHEDULE_STEAL))

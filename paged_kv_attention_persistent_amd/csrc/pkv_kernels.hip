@@ -772,13 +772,6 @@ __device__ __forceinline__ void store_lse(const DecodeParams& P, int b, size_t h
     else *dst = v;
 }
 
-// Exact merge of the partial states of one split (row, KV head) (PersistentKV
-// page, Methodology 1, "Sequence Splitting"): with M = max_c lse_c and
-// w_c = exp(lse_c - M), O = sum_c w_c o_c / sum_c w_c and
-// LSE = M + ln sum_c w_c.  A row with no ranges gets O = 0, LSE = -inf.
-// Ranges are read 32 at a time, all loads of a block issued together; blocks
-// after the first fold in by rescaling (the same identity, applied twice).
-// Each thread merges two adjacent dims of one head.
 // The page cursors of a (row, KV head): one for the page-claim schedule, one
 // per wave index for the steal schedule.
 __device__ __forceinline__ void rearm_cursors(const DecodeParams& P, int b, int hk) {
@@ -787,48 +780,97 @@ __device__ __forceinline__ void rearm_cursors(const DecodeParams& P, int b, int 
     for (int i = 0; i < n; ++i) atomicExch(c + (size_t)i * kCursorStride, 0u);
 }
 
-template <int D, int G, int NT, bool COHERENT>
-__device__ void merge_row(const DecodeParams& P, int b, int hk, int nc, int base, int tid) {
+// Exact merge of partial states (PersistentKV page, Methodology 1, "Sequence
+// Splitting"): with M = max_c lse_c and w_c = exp(lse_c - M),
+// O = sum_c w_c o_c / sum_c w_c and LSE = M + ln sum_c w_c; no states (or
+// only neutral ones) give O = 0, LSE = -inf.  fold_states merges, for head g
+// and dims d, d + 1 of KV head hk, the n states at range slots first,
+// first + step, ...; they are read 32 at a time, all loads of a block issued
+// together, and blocks after the first fold in by rescaling (the same
+// identity applied twice).  The result has the form of a range's partial
+// state, so merged states can be merged again.
+template <int D, int G, bool COHERENT>
+__device__ __forceinline__ void fold_states(const DecodeParams& P, int hk, int g, int d, int first, int step, int n,
+                                            float& out0, float& out1, float& out_lse) {
     constexpr int CB = 32;
+    float M = -INFINITY, L = 0.0f, O0 = 0.0f, O1 = 0.0f;
+    for (int c0 = 0; c0 < n; c0 += CB) {
+        float lv[CB], o0[CB], o1[CB];
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+            lv[j] = -INFINITY;
+            o0[j] = 0.0f;
+            o1[j] = 0.0f;
+            if (c0 + j < n) {
+                const size_t s = ((size_t)(first + (c0 + j) * step) * P.hkv + hk) * G + g;
+                lv[j] = ld_partial<COHERENT>(P.partial_lse + s);
+                o0[j] = ld_partial<COHERENT>(P.partial_o + s * D + d);
+                o1[j] = ld_partial<COHERENT>(P.partial_o + s * D + d + 1);
+            }
+        }
+        float Mb = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < CB; ++j) Mb = fmaxf(Mb, lv[j]);
+        if (Mb == -INFINITY) continue;
+        const float Mn = fmaxf(M, Mb);
+        const float a = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((M - Mn) * kLog2e);
+        L *= a;
+        O0 *= a;
+        O1 *= a;
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+            const float wgt = lv[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((lv[j] - Mn) * kLog2e);
+            L += wgt;
+            O0 = fmaf(wgt, o0[j], O0);
+            O1 = fmaf(wgt, o1[j], O1);
+        }
+        M = Mn;
+    }
+    const bool any = L > 0.0f;
+    out0 = any ? O0 / L : 0.0f;
+    out1 = any ? O1 / L : 0.0f;
+    out_lse = any ? M + logf(L) : -INFINITY;
+}
+
+// Rows with more ranges than this merge in two levels (one-shot launches):
+// each group of kMergeGroup consecutive ranges is folded by the last of its
+// workgroups to arrive, into the slot of the group's first range (whose
+// state it has just read), and the row's last group folds the group states.
+// One workgroup alone would read every range's state of the row through one
+// CU (512 KiB for 256 ranges at D = 128, G = 4); in two levels the groups
+// are read in parallel and the last step reads one state per group.
+constexpr int kMergeGroup = 32;
+
+// The final merge of a (row, KV head): the n states at slots first + k step
+// into the outputs.  Each thread merges two adjacent dims of one head.
+template <int D, int G, int NT, bool COHERENT>
+__device__ void merge_row(const DecodeParams& P, int b, int hk, int first, int step, int n, int tid) {
     for (int t = tid; t < G * D / 2; t += NT) {
         const int g = (2 * t) / D, d = (2 * t) % D;
         const size_t h = (size_t)hk * G + g;
-        float M = -INFINITY, L = 0.0f, O0 = 0.0f, O1 = 0.0f;
-        for (int c0 = 0; c0 < nc; c0 += CB) {
-            float lv[CB], o0[CB], o1[CB];
-#pragma unroll
-            for (int j = 0; j < CB; ++j) {
-                lv[j] = -INFINITY;
-                o0[j] = 0.0f;
-                o1[j] = 0.0f;
-                if (c0 + j < nc) {
-                    const size_t s = ((size_t)(base + c0 + j) * P.hkv + hk) * G + g;
-                    lv[j] = ld_partial<COHERENT>(P.partial_lse + s);
-                    o0[j] = ld_partial<COHERENT>(P.partial_o + s * D + d);
-                    o1[j] = ld_partial<COHERENT>(P.partial_o + s * D + d + 1);
-                }
-            }
-            float Mb = -INFINITY;
-#pragma unroll
-            for (int j = 0; j < CB; ++j) Mb = fmaxf(Mb, lv[j]);
-            if (Mb == -INFINITY) continue;
-            const float Mn = fmaxf(M, Mb);
-            const float a = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((M - Mn) * kLog2e);
-            L *= a;
-            O0 *= a;
-            O1 *= a;
-#pragma unroll
-            for (int j = 0; j < CB; ++j) {
-                const float wgt = lv[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((lv[j] - Mn) * kLog2e);
-                L += wgt;
-                O0 = fmaf(wgt, o0[j], O0);
-                O1 = fmaf(wgt, o1[j], O1);
-            }
-            M = Mn;
-        }
-        const bool any = L > 0.0f;
-        store_out_pair(P, b, h, d, any ? O0 / L : 0.0f, any ? O1 / L : 0.0f);
-        if (d == 0) store_lse(P, b, h, any ? M + logf(L) : -INFINITY);
+        float o0, o1, lse;
+        fold_states<D, G, COHERENT>(P, hk, g, d, first, step, n, o0, o1, lse);
+        store_out_pair(P, b, h, d, o0, o1);
+        if (d == 0) store_lse(P, b, h, lse);
+    }
+}
+
+// First level of a two-level merge: fold the n ranges from slot first into
+// slot first.  Every state is read before any is overwritten (the barrier),
+// and the merged state is stored coherently like a range's.
+template <int D, int G, int NT, bool COHERENT>
+__device__ void merge_group(const DecodeParams& P, int hk, int first, int n, int tid) {
+    static_assert(G * D / 2 <= NT, "one (head, dim pair) per thread");
+    const bool has = tid < G * D / 2;
+    const int g = (2 * tid) / D, d = (2 * tid) % D;
+    float o0 = 0.0f, o1 = 0.0f, lse = -INFINITY;
+    if (has) fold_states<D, G, COHERENT>(P, hk, g, d, first, 1, n, o0, o1, lse);
+    __syncthreads();
+    if (has) {
+        const size_t s = ((size_t)first * P.hkv + hk) * G + g;
+        st_partial<true>(P.partial_o + s * D + d, o0);
+        st_partial<true>(P.partial_o + s * D + d + 1, o1);
+        if (d == 0) st_partial<true>(P.partial_lse + s, lse);
     }
 }
 
@@ -887,7 +929,7 @@ __device__ __forceinline__ ItemRef read_item(const DecodeParams& P, uint32_t idx
         if (it.nch > 1) {
             it.base = base_u;
             const int slot = (it.base + it.chunk) * P.hkv + it.hk;
-            it.ok = it.chunk < it.nch && slot >= 0 && (it.base + it.nch) * P.hkv <= P.max_items &&
+            it.ok = it.chunk < it.nch && it.base >= 0 && slot >= 0 && (it.base + it.nch) * P.hkv <= P.max_items &&
                     it.len >= it.te && it.len <= (uint32_t)P.max_tokens;
         } else {
             it.ok = it.nch == 1;
@@ -1135,21 +1177,49 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, const ItemRe
         // thread waits until its coherent partial stores have completed
         // (s_waitcnt vmcnt(0)), the workgroup then counts itself in with one
         // atomic, and the workgroup that completes the count reads every
-        // partial with coherent loads issued after it saw the count.
+        // partial with coherent loads issued after it saw the count.  Rows
+        // with more than kMergeGroup ranges (one-shot launches) first count
+        // in per group of ranges, and the group's last arriver folds the
+        // group and then counts the group in for the row, by the same steps.
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
-        if (tid == 0) {
-            const uint32_t old = atomicAdd(&P.arrive[(size_t)b * P.hkv + hk], 1u);
-            sm.last = (old + 1 == (uint32_t)it.nch) ? 1u : 0u;
-        }
-        __syncthreads();
-        if (sm.last) {
-            merge_row<D, G, kThreads, true>(P, b, hk, it.nch, it.base, tid);
+        const int ngroups = (it.nch + kMergeGroup - 1) / kMergeGroup;
+        const bool two_level = ONE_SHOT && ngroups > 1;
+        bool row_step = true;                         // uniform over the workgroup
+        if (two_level) {
+            const int gfirst = (it.chunk / kMergeGroup) * kMergeGroup;
+            const int gn = it.nch - gfirst < kMergeGroup ? it.nch - gfirst : kMergeGroup;
+            uint32_t* gcount = P.grp_arrive + (size_t)(it.base + gfirst) * P.hkv + hk;
             if (tid == 0) {
-                atomicExch(&P.arrive[(size_t)b * P.hkv + hk], 0u);
-                // every item of the row has arrived, so no wave claims from
-                // its cursors any more: the next launch starts them at zero
-                if (P.cursors) rearm_cursors(P, b, hk);
+                const uint32_t old = atomicAdd(gcount, 1u);
+                sm.last = (old + 1 == (uint32_t)gn) ? 1u : 0u;
+            }
+            __syncthreads();
+            row_step = sm.last != 0;
+            if (row_step) {
+                if (tid == 0) atomicExch(gcount, 0u);    // every range of the group has arrived
+                merge_group<D, G, kThreads, true>(P, hk, it.base + gfirst, gn, tid);
+                __builtin_amdgcn_s_waitcnt(0x0F70);
+                __syncthreads();
+            }
+        }
+        if (row_step) {
+            if (tid == 0) {
+                const uint32_t old = atomicAdd(&P.arrive[(size_t)b * P.hkv + hk], 1u);
+                sm.last = (old + 1 == (uint32_t)(two_level ? ngroups : it.nch)) ? 1u : 0u;
+            }
+            __syncthreads();
+            if (sm.last) {
+                if (two_level)
+                    merge_row<D, G, kThreads, true>(P, b, hk, it.base, kMergeGroup, ngroups, tid);
+                else
+                    merge_row<D, G, kThreads, true>(P, b, hk, it.base, 1, it.nch, tid);
+                if (tid == 0) {
+                    atomicExch(&P.arrive[(size_t)b * P.hkv + hk], 0u);
+                    // every item of the row has arrived, so no wave claims from
+                    // its cursors any more: the next launch starts them at zero
+                    if (P.cursors) rearm_cursors(P, b, hk);
+                }
             }
         }
     }
@@ -1281,7 +1351,7 @@ __device__ __forceinline__ ItemRef read_item_mirror(const DecodeParams& P, uint3
         if (it.nch > 1) {
             it.base = base_u;
             const int slot = (it.base + it.chunk) * P.hkv + it.hk;
-            it.ok = it.chunk < it.nch && slot >= 0 && (it.base + it.nch) * P.hkv <= P.max_items;
+            it.ok = it.chunk < it.nch && it.base >= 0 && slot >= 0 && (it.base + it.nch) * P.hkv <= P.max_items;
         } else {
             it.ok = it.nch == 1;
         }
@@ -1582,6 +1652,9 @@ __global__ __launch_bounds__(kThreads) void resident_kernel(LoopParams L) {
 }
 
 // The separate merge kernel: one workgroup per (merge row, KV head).
+// Merge kernel of the separate-merge mode: one workgroup per (row, KV head),
+// with the fused merge's two levels for rows of more than kMergeGroup ranges
+// (the groups one after another), so that both modes give the same bits.
 template <int D, int G>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
     const int n_rows = P.qhdr->n_merge_rows;
@@ -1591,8 +1664,20 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams P) {
     const int b = P.merge_rows[ri];
     if (b < 0 || b >= P.batch) return;
     const int nc = P.n_chunks[b];
-    if (nc == 1 || (P.part_off[b] + nc) * P.hkv > P.max_items) return;
-    merge_row<D, G, 256, false>(P, b, hk, nc, P.part_off[b], threadIdx.x);
+    const int base = P.part_off[b];
+    if (nc == 1 || nc < 0 || base < 0 || (base + nc) * P.hkv > P.max_items) return;
+    if (nc > kMergeGroup) {
+        for (int gfirst = 0; gfirst < nc; gfirst += kMergeGroup)
+            merge_group<D, G, 256, false>(P, hk, base + gfirst, nc - gfirst < kMergeGroup ? nc - gfirst : kMergeGroup,
+                                          threadIdx.x);
+        // the group states were stored by this workgroup: wait for them, and
+        // read them with coherent loads (not through this CU's L1)
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        merge_row<D, G, 256, true>(P, b, hk, base, kMergeGroup, (nc + kMergeGroup - 1) / kMergeGroup, threadIdx.x);
+    } else {
+        merge_row<D, G, 256, false>(P, b, hk, base, 1, nc, threadIdx.x);
+    }
     // the decode kernel has finished: its page cursor starts the next launch at zero
     if (P.cursors && threadIdx.x == 0) rearm_cursors(P, b, hk);
 }

@@ -73,7 +73,7 @@ extern "C" PKV_API pkv_status pkv_decode_noalloc(const pkv_config* cfg, const in
     // node: the clears are small fill kernels.
     const DecodeParams p = decode_params(r, lay, ws, t, error_word);
     const BuildParams bp = build_params(r, lay, ws, ctx_lens_device, batch, error_word);
-    int rc = launch_init_ctrl(p.ctrl, p.arrive, r.max_batch * r.hkv * r.num_layers, stream);
+    int rc = launch_init_ctrl(p.ctrl, p.arrive, (int)arrive_words(r), stream);
     if (rc == 0 && (r.schedule == PKV_SCHEDULE_PAGES || r.schedule == PKV_SCHEDULE_STEAL))
         rc = launch_zero(ws + lay.cursor_off, lay.loop_off - lay.cursor_off, stream);
     if (rc == 0) rc = launch_build_queue(bp, stream);

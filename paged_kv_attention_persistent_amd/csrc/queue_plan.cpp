@@ -159,6 +159,10 @@ uint64_t loop_slot_bytes(const Resolved& r, const pkv_layout& lay) {
                     16ull * r.max_items);
 }
 
+uint64_t arrive_words(const Resolved& r) {
+    return (uint64_t)r.max_batch * r.hkv * r.num_layers + (uint64_t)r.max_items;
+}
+
 uint64_t loop_counter_bytes(const Resolved& r) {
     return align256(sizeof(LoopSlotCtr) + 4ull * r.max_batch);
 }
@@ -186,7 +190,7 @@ void compute_layout(const Resolved& r, pkv_layout* lay) {
     lay->partial_lse_off = off;
     off = align256(off + 4ull * r.max_items * r.g * layers);
     lay->arrive_off = off;
-    off = align256(off + 4ull * r.max_batch * r.hkv * layers);
+    off = align256(off + 4ull * arrive_words(r));
     lay->cursor_off = off;
     // one cursor per (row, KV head), or per (row, KV head, wave) for the steal schedule
     if (r.schedule == PKV_SCHEDULE_PAGES) off = align256(off + 4ull * kCursorStride * r.max_batch * r.hkv);

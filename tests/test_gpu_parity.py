@@ -269,6 +269,38 @@ def test_wide_block_table_and_batch_below_capacity(sched, device_queue):
     finally:
         dec.close()
 
+
+TWO_LEVEL_LENS = [70 * 1024 - 100, 3000, 0, 40 * 1024 - 1024 + 17]     # 70, 3, 0 and 40 ranges of 1024
+
+
+@pytest.mark.parametrize("kv", KVS)
+@pytest.mark.parametrize("sched", list(SCHEDULES))
+def test_two_level_merge_against_oracle_and_separate_merge(sched, kv):
+    """Rows of more than 32 ranges merge in two levels in one-shot launches
+    (groups of 32 ranges folded by their last workgroups, then the group
+    states): every output against the oracle on three calls in a row (the
+    group and row counters re-arm), a 3-range row and an empty row beside
+    them, and the separate merge kernel, which runs the same two levels,
+    bit for bit equal to the fused one."""
+    wl = workloads.custom("two_level", TWO_LEVEL_LENS, 8, 2, 128, spare_pages=5, kv_dtype=kv)
+    ro, rl = oracle_full(wl)
+    res = {}
+    for merge in ("fused", "separate"):
+        run = Run(wl, kv_chunk_tokens=1024, schedule=SCHEDULES[sched],
+                  merge_mode=pkv.PKV_MERGE_FUSED if merge == "fused" else pkv.PKV_MERGE_SEPARATE)
+        run.dec.build_queue(wl.ctx_lens)
+        nch = run.queue_bytes()["n_chunks"].tolist()
+        assert nch == [70, 3, 0, 40], nch
+        for call in range(3):
+            o, l = run.decode()
+            check(o, l, ro, rl, f"two-level {sched} {kv} {merge} call {call}",
+                  lse_tol=LSE_F32 if kv == "f32" else MAX_ABS)
+        res[merge] = (run.out.clone(), run.lse.clone())
+        run.close()
+    if sched == "atomic":          # the page-claim and steal schedules split pages at run time
+        assert torch.equal(res["fused"][0].view(torch.int16), res["separate"][0].view(torch.int16))
+        assert torch.equal(res["fused"][1].view(torch.int32), res["separate"][1].view(torch.int32))
+
 # ------------------------------------------------------ full-size cases ----
 
 _ORACLE_CACHE = {}
