@@ -78,7 +78,8 @@ enum {
  * page count for which sum_b ceil(ceil(L_b / P) / T) <= max(1, num_cus / Hkv):
  * the shortest ranges that still give at most one item per workgroup (the
  * longest row's page count if the rows alone exceed that bound), and never
- * shorter than 64 pages. */
+ * shorter than 16 pages (64 pages for the resident loop, persistent = 1).
+ * The default max_items is sized by that floor. */
 enum { PKV_POLICY_AUTO = 0, PKV_POLICY_NO_SPLIT = 1, PKV_POLICY_SPLIT = 2 };
 
 /* Queue order: CANONICAL = (seq, kv_head, chunk) ascending; LPT = stable sort

@@ -29,9 +29,11 @@ Readings taken where the page is silent:
   page's own count for one sequence (as many ranges as it takes to fill the
   GPU) to a batch, keeping the longest range as short as one round allows.
   If no T reaches the bound (more non-empty rows than K), T is the longest
-  row's page count.  T is never below 64 pages (1024 tokens, eight pages
-  per wave of a workgroup): shorter ranges cost more in per-range start and
-  merge than they gain in balance.
+  row's page count.  T is never below a floor: 16 pages (256 tokens) for
+  one-shot calls, 64 pages (1024 tokens) for the resident loop, whose
+  workspace sizes its per-layer partial states by this floor.  The floor is
+  a measured tuning, not the page's: the shortest ranges that keep one
+  range per workgroup are the fastest down to 16 pages.
 * Ranges are fixed chunks from token 0: chunk c covers
   [c * C, min(L_b, (c + 1) * C)).
 * Item encoding, 16 bytes little-endian:
@@ -64,7 +66,8 @@ ITEM_DTYPE = np.dtype([("seq", "<u4"), ("kv_head", "<u2"), ("chunk", "<u2"),
 assert ITEM_DTYPE.itemsize == 16
 
 
-FIT_MIN_PAGES = 64
+FIT_MIN_PAGES = 16           # one-shot calls
+FIT_MIN_PAGES_LOOP = 64      # the resident loop
 
 
 def fit_chunk(ctx_lens, num_kv_heads: int, num_cus: int, page_size: int = 16,
@@ -99,10 +102,13 @@ def decide_split(ctx_lens, num_kv_heads: int, num_cus: int, chunk_tokens: int,
 
 
 def build_queue(ctx_lens, num_kv_heads: int, num_cus: int, chunk_tokens: int,
-                policy: int = POLICY_AUTO, order: int = ORDER_CANONICAL):
+                policy: int = POLICY_AUTO, order: int = ORDER_CANONICAL,
+                fit_min_pages: int = FIT_MIN_PAGES):
     """Compact work queue for one decode call.
 
-    ``chunk_tokens = 0`` selects chunk mode "fit" (see ``fit_chunk``).
+    ``chunk_tokens = 0`` selects chunk mode "fit" (see ``fit_chunk``), with
+    ranges of at least ``fit_min_pages`` pages (``FIT_MIN_PAGES_LOOP`` for
+    the resident loop's steps).
 
     Returns a dict with
       split      bool, the policy decision
@@ -120,7 +126,7 @@ def build_queue(ctx_lens, num_kv_heads: int, num_cus: int, chunk_tokens: int,
         if L < 0:
             raise ValueError("negative context length")
     if chunk_tokens == 0:                                 # chunk mode "fit"
-        chunk_tokens = fit_chunk(lens, num_kv_heads, num_cus)
+        chunk_tokens = fit_chunk(lens, num_kv_heads, num_cus, min_pages=fit_min_pages)
     split = decide_split(lens, num_kv_heads, num_cus, chunk_tokens, policy)
     bsz = len(lens)
 

@@ -93,6 +93,7 @@ BuildParams build_params(const Resolved& r, const pkv_layout& lay, unsigned char
     p.policy = r.policy;
     p.max_items = r.max_items;
     p.max_tokens = r.max_pages_per_seq * r.page;
+    p.fit_min_pages = r.fit_min_pages;
     return p;
 }
 

@@ -13,7 +13,13 @@ namespace pkv {
 constexpr int kPageSize = 16;          // tokens per page (the only size built)
 constexpr int kThreads = 512;          // 8 waves of 64 lanes per workgroup
 constexpr int kWaves = kThreads / 64;
-constexpr int kFitMinPages = 64;       // chunk mode "fit": ranges of at least 64 pages
+// Chunk mode "fit": shortest range in pages.  One-shot launches take ranges
+// down to 16 pages (measured: the shortest ranges that still give one item
+// per workgroup are the fastest); the resident loop keeps 64, since the
+// workspace holds its partial states for every layer and sizes them by this
+// floor.
+constexpr int kFitMinPages = 16;
+constexpr int kFitMinPagesLoop = 64;
 constexpr int kCursorStride = 32;      // u32 words between page cursors (one 128-byte line each)
 constexpr int kSinkBytes = 4096;       // >= the largest tile (16 rows x 128 bf16, 8 rows x 128 fp32)
 
@@ -130,6 +136,7 @@ struct Resolved {
     float scale;
     int policy, order, chunk, num_cus, max_items, wg_per_cu, merge_mode;
     int persistent, num_layers, timeout_ms, schedule, append, kv_dtype;
+    int fit_min_pages;          // kFitMinPages, or kFitMinPagesLoop for the resident loop
 };
 
 pkv_status resolve_config(const pkv_config* cfg, int device_cus, Resolved* r, const char** why);
@@ -232,6 +239,7 @@ struct BuildParams {
     int32_t policy;
     int32_t max_items;
     int32_t max_tokens;
+    int32_t fit_min_pages;
 };
 
 // Kernel parameters over a workspace laid out by compute_layout (pkv_api.cpp).

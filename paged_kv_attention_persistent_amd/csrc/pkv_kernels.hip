@@ -1727,7 +1727,7 @@ __global__ __launch_bounds__(kBuildThreads) void build_queue_kernel(BuildParams 
     // sum_b ceil(pages_b / T) <= K = max(1, CUs / Hkv), by bisection over T
     // with a block-wide sum per step (clamped at K + 1, which is all the
     // comparison needs); the longest row's pages when no T reaches K; never
-    // below kFitMinPages.
+    // below the floor P.fit_min_pages.
     int chunk = P.chunk;
     if (chunk == 0) {
         __shared__ unsigned long long s_cnt;
@@ -1757,7 +1757,7 @@ __global__ __launch_bounds__(kBuildThreads) void build_queue_kernel(BuildParams 
             }
             T = lo;
         }
-        chunk = (T > kFitMinPages ? T : kFitMinPages) * kPageSize;
+        chunk = (T > P.fit_min_pages ? T : P.fit_min_pages) * kPageSize;
     }
     bool split;
     if (P.policy == PKV_POLICY_NO_SPLIT) split = false;

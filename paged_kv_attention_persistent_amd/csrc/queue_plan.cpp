@@ -108,10 +108,11 @@ pkv_status resolve_config(const pkv_config* user_cfg, int device_cus, Resolved* 
     if (r->num_cus <= 0) { *why = "num_cus unknown (set it in the config)"; return PKV_ERR_INVALID_ARG; }
     const int64_t max_tokens = (int64_t)r->max_pages_per_seq * kPageSize;
     // ranges per row: ceil(max_tokens / C) for fixed chunks; for "fit" the
-    // range floor bounds it by ceil(max_pages_per_seq / kFitMinPages), which,
-    // like the whole layout, does not depend on the CU count
+    // range floor bounds it by ceil(max_pages_per_seq / floor), which, like
+    // the whole layout, does not depend on the CU count
+    r->fit_min_pages = cfg->persistent ? kFitMinPagesLoop : kFitMinPages;
     const int64_t max_chunks = r->chunk ? (max_tokens + r->chunk - 1) / r->chunk
-                                        : ((int64_t)r->max_pages_per_seq + kFitMinPages - 1) / kFitMinPages;
+                                        : ((int64_t)r->max_pages_per_seq + r->fit_min_pages - 1) / r->fit_min_pages;
     if (max_chunks > 65535) { *why = "more than 65535 ranges per row"; return PKV_ERR_CAPACITY; }
     if (cfg->max_items < 0) { *why = "max_items must be >= 0"; return PKV_ERR_INVALID_ARG; }
     if (cfg->max_items > 0) {
@@ -208,7 +209,7 @@ void compute_layout(const Resolved& r, pkv_layout* lay) {
 // Chunk mode "fit": the smallest T pages with sum_b ceil(pages_b / T) <= K,
 // K = max(1, CUs / Hkv), so that the split queue still has at most one range
 // per workgroup; the longest row's page count when no T reaches K; and never
-// below kFitMinPages.  The count falls as T grows, so a bisection finds the
+// below r.fit_min_pages.  The count falls as T grows, so a bisection finds the
 // smallest T.
 int fit_chunk(const Resolved& r, const int32_t* ctx_lens, int batch, int64_t max_len) {
     const int64_t budget = std::max(1, r.num_cus / r.hkv);
@@ -230,7 +231,7 @@ int fit_chunk(const Resolved& r, const int32_t* ctx_lens, int batch, int64_t max
         }
         T = lo;
     }
-    return (int)(std::max<int64_t>(T, kFitMinPages) * r.page);
+    return (int)(std::max<int64_t>(T, r.fit_min_pages) * r.page);
 }
 
 pkv_status plan_queue(const Resolved& r, const int32_t* ctx_lens, int32_t batch, QHdr* qh,

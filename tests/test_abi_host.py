@@ -219,7 +219,7 @@ def test_layout_regions_are_ordered_and_aligned():
     offs = [lay.ctrl_off, lay.queue_off, lay.n_chunks_off, lay.part_off_off, lay.merge_rows_off,
             lay.items_off, lay.partial_o_off, lay.partial_lse_off, lay.arrive_off, lay.total_bytes]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
-    assert lay.max_items == 8 * (8192 // 64)      # ranges of at least 64 pages
+    assert lay.max_items == 8 * (8192 // 16)      # one-shot ranges of at least 16 pages
     assert lay.partial_lse_off - lay.partial_o_off >= lay.max_items * 4 * 128 * 4
 
 

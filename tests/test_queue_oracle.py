@@ -130,7 +130,8 @@ def test_fit_chunk_one_row_is_the_ceiling_of_pages_over_the_budget():
         K = max(1, cus // hkv)
         assert wq.fit_chunk([16 * n], hkv, cus, min_pages=1) == 16 * (-(-n // K))
         assert wq.fit_chunk([16 * n - 5], hkv, cus, min_pages=1) == 16 * (-(-n // K))
-        assert wq.fit_chunk([16 * n], hkv, cus) == 16 * max(64, -(-n // K))
+        assert wq.fit_chunk([16 * n], hkv, cus) == 16 * max(wq.FIT_MIN_PAGES, -(-n // K))
+        assert wq.fit_chunk([16 * n], hkv, cus, min_pages=wq.FIT_MIN_PAGES_LOOP) == 16 * max(64, -(-n // K))
 
 
 def test_fit_chunk_equal_rows():
@@ -138,13 +139,13 @@ def test_fit_chunk_equal_rows():
     for B, n in [(2, 1000), (3, 64), (5, 17), (16, 4096)]:
         K = 256 // 8
         assert wq.fit_chunk([16 * n] * B, 8, 256, min_pages=1) == 16 * (-(-n // (K // B)))
-        assert wq.fit_chunk([16 * n] * B, 8, 256) == 16 * max(64, -(-n // (K // B)))
+        assert wq.fit_chunk([16 * n] * B, 8, 256) == 16 * max(wq.FIT_MIN_PAGES, -(-n // (K // B)))
 
 
 def test_fit_chunk_fallback_and_edges():
     assert wq.fit_chunk([], 8, 256, min_pages=1) == 16
     assert wq.fit_chunk([0, 0], 8, 256, min_pages=1) == 16
-    assert wq.fit_chunk([], 8, 256) == 16 * 64
+    assert wq.fit_chunk([], 8, 256) == 16 * wq.FIT_MIN_PAGES
     # more non-empty rows than the budget: no T fits, T = longest row
     assert wq.fit_chunk([16 * 5] * 40, 8, 256, min_pages=1) == 16 * 5
     assert wq.fit_chunk([16 * 500] * 40, 8, 256) == 16 * 500
@@ -154,7 +155,7 @@ def test_fit_mode_on_the_workloads():
     cus = 256
     t = workloads.tiny()
     q = wq.build_queue(t.ctx_lens, 1, cus, 0)
-    assert not q["split"] and len(q["items"]) == 1 and q["chunk_tokens"] == 1024
+    assert not q["split"] and len(q["items"]) == 1 and q["chunk_tokens"] == 16 * wq.FIT_MIN_PAGES
     lc = workloads.long_context()
     q = wq.build_queue(lc.ctx_lens, 8, cus, 0)
     assert q["chunk_tokens"] == 4096 and len(q["items"]) == 256       # same as the fixed 4096
