@@ -804,8 +804,11 @@ __device__ __forceinline__ void fold_states(const DecodeParams& P, int hk, int g
             if (c0 + j < n) {
                 const size_t s = ((size_t)(first + (c0 + j) * step) * P.hkv + hk) * G + g;
                 lv[j] = ld_partial<COHERENT>(P.partial_lse + s);
-                o0[j] = ld_partial<COHERENT>(P.partial_o + s * D + d);
-                o1[j] = ld_partial<COHERENT>(P.partial_o + s * D + d + 1);
+                // the two dims are adjacent: one 8-byte load
+                const uint64_t* po = reinterpret_cast<const uint64_t*>(P.partial_o + s * D + d);
+                const uint64_t x = COHERENT ? __hip_atomic_load(po, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *po;
+                o0[j] = __uint_as_float((uint32_t)x);
+                o1[j] = __uint_as_float((uint32_t)(x >> 32));
             }
         }
         float Mb = -INFINITY;
