@@ -38,7 +38,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="long", choices=["long", "mixed", "short", "tiny"])
     ap.add_argument("--others", default="mixed,short",
-                    help="extra workloads measured in the same run ('' for none)")
+                    help="extra workloads measured in the same run ('' for none; also long_tp8, the "
+                         "long context's per-GPU share under 8-way head sharding)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bounded oracle sample for cpu_baseline (0 disables)")
     ap.add_argument("--order", default="canonical", choices=["canonical", "lpt"])

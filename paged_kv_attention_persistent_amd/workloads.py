@@ -318,6 +318,15 @@ def long_context(seed: int = MEASURE_SEED, ctx: int = 131072) -> Workload:
     return Workload("long", 32, 8, 128, 16, lens, _tables(rng, lens, 16, npg), npg, seed)
 
 
+def long_tp8(seed: int = MEASURE_SEED, ctx: int = 131072) -> Workload:
+    """One GPU's share of the long context when its 32/8 heads are split over
+    8 GPUs by head: batch 1, 4 query heads / 1 KV head, head_dim 128."""
+    rng = np.random.default_rng([seed, 5])
+    lens = np.array([ctx], dtype=np.int32)
+    npg = -(-ctx // 16)
+    return Workload("long_tp8", 4, 1, 128, 16, lens, _tables(rng, lens, 16, npg), npg, seed)
+
+
 def mixed(seed: int = MEASURE_SEED, batch: int = 8, lo: int = 1024, hi: int = 65536) -> Workload:
     """8 sequences, lengths log-uniform in [1024, 65536] (rounded), 32/8 heads."""
     rng = np.random.default_rng([seed, 3])
@@ -348,7 +357,7 @@ def custom(name: str, lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
                     _tables(rng, lens, page_size, npg, max_pages), npg, seed, kv_dtype=kv_dtype)
 
 
-CONFIGS = {"tiny": tiny, "long": long_context, "mixed": mixed, "short": many_short}
+CONFIGS = {"tiny": tiny, "long": long_context, "mixed": mixed, "short": many_short, "long_tp8": long_tp8}
 
 
 @dataclass
