@@ -407,7 +407,9 @@ PKV_API pkv_status pkv_query(pkv_handle* h, pkv_runtime_info* info);
 /* Clear the device error word after a reported fault (synchronises the
  * device), so that the handle may be used again (GPUOS page, section 5: a
  * kill switch returns an error code to the host, which decides what next).
- * PKV_ERR_STATE while a resident loop runs. */
+ * Also starts the merge's arrival counters and the page cursors at zero
+ * again, since a refused item never counted in.  PKV_ERR_STATE while a
+ * resident loop runs. */
 PKV_API pkv_status pkv_clear_error(pkv_handle* h);
 
 /* Destroy the handle, the shutdown call of the GPUOS page's host API

@@ -709,6 +709,12 @@ PKV_API pkv_status pkv_clear_error(pkv_handle* h) {
     const uint32_t z[2] = {0u, 0u};
     e = hipMemcpy(h->ws + h->lay.ctrl_off + offsetof(Ctrl, error_code), z, sizeof(z), hipMemcpyHostToDevice);
     if (e != hipSuccess) return hip_fail(h, e, "clear error");
+    // An item the kernel refused never counted in for its row's merge, so the
+    // arrival counters (and the page cursors of its row) may be left part-way:
+    // start them at zero again.
+    int rc = launch_zero(h->ws + h->lay.arrive_off, h->lay.loop_off - h->lay.arrive_off, h->stream);
+    if (rc == 0 && (e = hipStreamSynchronize(h->stream)) != hipSuccess) return hip_fail(h, e, "clear counters");
+    if (rc != 0) return hip_fail(h, (hipError_t)rc, "clear counters");
     __atomic_store_n(h->host_err, 0u, __ATOMIC_RELEASE);
     return PKV_OK;
 }

@@ -710,6 +710,34 @@ def test_bad_block_table_entry_is_reported_not_read():
     run.close()
 
 
+@pytest.mark.parametrize("sched", list(SCHEDULES))
+def test_clear_error_restarts_the_merge_counters(sched):
+    """An item the kernel refuses never counts in for its row's merge; after
+    pkv_clear_error the row and group arrival counters and the page cursors
+    start from zero again.  Garbage planted in that region (as a refused item
+    would leave it) must not change a following decode of split rows, with
+    one- and two-level merges."""
+    wl = workloads.custom("clear_counters", TWO_LEVEL_LENS, 8, 2, 128, spare_pages=5)
+    run = Run(wl, kv_chunk_tokens=1024, schedule=SCHEDULES[sched])
+    ro, rl = oracle_full(wl)
+    o, l = run.decode()
+    check(o, l, ro, rl, f"clear counters {sched} before")
+    lay = run.dec.layout
+    region = run.dec.workspace[lay.arrive_off:lay.loop_off].view(torch.int32)
+    n_counters = wl.batch * wl.num_kv_heads + lay.max_items       # row counters, then group counters
+    cursors = run.dec.workspace[lay.cursor_off:lay.loop_off].view(torch.int32)
+    # every counter and cursor is back at zero after a launch (the region's
+    # alignment padding is never written)
+    assert int(region[:n_counters].abs().sum()) == 0 and int(cursors.abs().sum()) == 0
+    region.copy_(torch.randint(1, 7, region.shape, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    pkv.pkv_clear_error(run.dec.handle)
+    assert int(region.abs().sum()) == 0
+    for call in range(2):
+        o, l = run.decode()
+        check(o, l, ro, rl, f"clear counters {sched} after, call {call}")
+    run.close()
+
 def test_device_builder_reports_bad_lengths_in_the_error_word():
     """The device queue builder checks every length before it writes a queue:
     a length beyond max_pages_per_seq pages sets PKV_DEVERR_BAD_ITEM with the
