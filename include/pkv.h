@@ -242,7 +242,7 @@ typedef struct pkv_layout {
     uint64_t partial_o_off;     /* fp32 [layers][max_items][G][D], normalised partial outputs */
     uint64_t partial_lse_off;   /* fp32 [layers][max_items][G], natural-log partial LSE */
     uint64_t arrive_off;        /* uint32 [layers][max_batch][Hkv] arrival counters of the fused merge,
-                                   then uint32 [max_items] counters of its two-level form */
+                                   then uint32 [layers][max_items] counters of its two-level form */
     uint64_t cursor_off;        /* PKV_SCHEDULE_PAGES: uint32 page cursors, one 128-byte line per
                                    (row, KV head); PKV_SCHEDULE_STEAL: one per (row, KV head,
                                    wave), 8 waves; empty otherwise */

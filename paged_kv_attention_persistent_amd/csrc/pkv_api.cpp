@@ -226,6 +226,7 @@ pkv_status start_loop(pkv_handle* h) {
     lp.partial_o_layer = (uint64_t)h->r.max_items * h->r.g * h->r.d;
     lp.partial_lse_layer = (uint64_t)h->r.max_items * h->r.g;
     lp.arrive_layer = (uint64_t)h->r.max_batch * h->r.hkv;
+    lp.grp_layer = (uint64_t)h->r.max_items;
     int clock_khz = 0;
     if ((e = hipDeviceGetAttribute(&clock_khz, hipDeviceAttributeWallClockRate, h->device)) != hipSuccess ||
         clock_khz <= 0)

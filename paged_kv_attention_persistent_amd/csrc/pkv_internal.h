@@ -143,7 +143,7 @@ pkv_status resolve_config(const pkv_config* cfg, int device_cus, Resolved* r, co
 void compute_layout(const Resolved& r, pkv_layout* lay);
 uint64_t loop_counter_bytes(const Resolved& r);
 // Words of the arrival region: [layers][max_batch][Hkv] row counters, then
-// [max_items] group counters of the one-shot two-level merge.
+// [layers][max_items] group counters of the two-level merge.
 uint64_t arrive_words(const Resolved& r);
 uint64_t loop_slot_bytes(const Resolved& r, const pkv_layout& lay);
 uint64_t loop_grant_bytes(const Resolved& r);      // append page grants in a slot, after LoopDesc
@@ -172,7 +172,7 @@ struct DecodeParams {
     float* partial_o;
     float* partial_lse;
     uint32_t* arrive;           // [max_batch][Hkv] arrival counters (fused merge)
-    uint32_t* grp_arrive;       // one-shot two-level merge: [max_items] group counters, at the slot of the group's first range
+    uint32_t* grp_arrive;       // two-level merge: [max_items] group counters, at the slot of the group's first range
     uint64_t* trace;            // per-item trace records (nullable)
     uint32_t* head;             // pop counter of this queue
     uint32_t* head_next;        // one-shot: the next launch's pop counter, zeroed at the start (nullable)
@@ -218,6 +218,7 @@ struct LoopParams {
     uint64_t partial_o_layer;   // elements per layer of partial_o
     uint64_t partial_lse_layer;
     uint64_t arrive_layer;
+    uint64_t grp_layer;         // group counters per layer (max_items)
     uint64_t timeout_ticks;     // 100 MHz wall-clock ticks
     int32_t max_batch;
 };

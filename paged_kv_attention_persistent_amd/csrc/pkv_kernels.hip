@@ -835,8 +835,8 @@ __device__ __forceinline__ void fold_states(const DecodeParams& P, int hk, int g
     out_lse = any ? M + logf(L) : -INFINITY;
 }
 
-// Rows with more ranges than this merge in two levels (one-shot launches):
-// each group of kMergeGroup consecutive ranges is folded by the last of its
+// Rows with more ranges than this merge in two levels: each group of
+// kMergeGroup consecutive ranges is folded by the last of its
 // workgroups to arrive, into the slot of the group's first range (whose
 // state it has just read), and the row's last group folds the group states.
 // One workgroup alone would read every range's state of the row through one
@@ -1181,13 +1181,13 @@ __device__ void process_item(const DecodeParams& P, Smem<D, G>& sm, const ItemRe
         // (s_waitcnt vmcnt(0)), the workgroup then counts itself in with one
         // atomic, and the workgroup that completes the count reads every
         // partial with coherent loads issued after it saw the count.  Rows
-        // with more than kMergeGroup ranges (one-shot launches) first count
-        // in per group of ranges, and the group's last arriver folds the
-        // group and then counts the group in for the row, by the same steps.
+        // with more than kMergeGroup ranges first count in per group of
+        // ranges, and the group's last arriver folds the group and then
+        // counts the group in for the row, by the same steps.
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
         const int ngroups = (it.nch + kMergeGroup - 1) / kMergeGroup;
-        const bool two_level = ONE_SHOT && ngroups > 1;
+        const bool two_level = ngroups > 1;
         bool row_step = true;                         // uniform over the workgroup
         if (two_level) {
             const int gfirst = (it.chunk / kMergeGroup) * kMergeGroup;
@@ -1554,6 +1554,7 @@ __global__ __launch_bounds__(kThreads) void resident_kernel(LoopParams L) {
                 Q.partial_o = P.partial_o + (uint64_t)layer * L.partial_o_layer;
                 Q.partial_lse = P.partial_lse + (uint64_t)layer * L.partial_lse_layer;
                 Q.arrive = P.arrive + (uint64_t)layer * L.arrive_layer;
+                Q.grp_arrive = P.grp_arrive + (uint64_t)layer * L.grp_layer;
                 // one thread reads the item over PCIe; the workgroup shares it
                 __shared__ ItemRef s_it;
                 if (tid == 0) s_it = read_item_mirror(Q, i);

@@ -161,7 +161,7 @@ uint64_t loop_slot_bytes(const Resolved& r, const pkv_layout& lay) {
 }
 
 uint64_t arrive_words(const Resolved& r) {
-    return (uint64_t)r.max_batch * r.hkv * r.num_layers + (uint64_t)r.max_items;
+    return ((uint64_t)r.max_batch * r.hkv + (uint64_t)r.max_items) * r.num_layers;
 }
 
 uint64_t loop_counter_bytes(const Resolved& r) {

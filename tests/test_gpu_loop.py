@@ -124,8 +124,9 @@ def check_all(lp, units=None):
     assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS and lerr.max() <= MAX_ABS
 
 
-@pytest.mark.parametrize("variant", ["nosplit_d128", "split_d128", "nosplit_d64_g8", "many_steps",
-                                     "nosplit_d128_f32", "split_d128_f32", "nosplit_d64_g8_f32"])
+@pytest.mark.parametrize("variant", ["nosplit_d128", "split_d128", "nosplit_d64_g8", "many_steps", "two_level",
+                                     "nosplit_d128_f32", "split_d128_f32", "nosplit_d64_g8_f32",
+                                     "two_level_f32"])
 def test_small_loop_every_output(variant):
     say("variant", variant)
     kv = "f32" if variant.endswith("_f32") else "bf16"
@@ -143,6 +144,14 @@ def test_small_loop_every_output(variant):
         sl = workloads.session_loop(seed=13, sessions=6, layers=2, steps=3, lo=1, hi=90,
                                     num_q_heads=16, num_kv_heads=2, head_dim=64, name="loop_d64")
         kw = dict(policy=pkv.PKV_POLICY_NO_SPLIT)
+    elif variant == "two_level":
+        # rows of up to 76 ranges of 32 tokens: their merges run in two levels
+        # (groups of 32 ranges, then the group states), in every layer; one
+        # short row beside them merges in one level
+        sl = workloads.session_loop(seed=18, sessions=3, layers=3, steps=3, lo=1200, hi=2400,
+                                    num_q_heads=8, num_kv_heads=2, name="loop_two_level")
+        sl.l0[1] = 40
+        kw = dict(policy=pkv.PKV_POLICY_SPLIT, kv_chunk_tokens=32)
     else:
         # many short steps: each counter slot is reused 24 times, so a
         # workgroup that lags a step behind meets a slot in every state
@@ -154,6 +163,9 @@ def test_small_loop_every_output(variant):
         for t in range(sl.steps):
             dt, info = lp.step(t)
             say(f"step {t}: {dt * 1e3:.2f} ms, items/layer {info.n_items}, split {info.split}")
+            if variant == "two_level":
+                longest = -(-int(max(sl.ctx_lens(t))) // 32)
+                assert longest > 64, longest          # three groups of ranges
         st = lp.dec.query()
         assert st["loop_out_epoch"] == sl.steps and st["loop_alive"] == 1
     finally:
