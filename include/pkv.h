@@ -123,10 +123,14 @@ enum { PKV_SCHEDULE_ATOMIC = 0, PKV_SCHEDULE_STATIC = 1, PKV_SCHEDULE_PAGES = 2,
  * resident loop (with or without append) take either. */
 enum { PKV_KV_BF16 = 0, PKV_KV_F32 = 1 };
 
-/* How split rows are merged.  FUSED: inside the decode kernel, the last
- * workgroup to finish a split (row, KV head) merges its partial states (one
- * launch per step).  SEPARATE: a second kernel merges every split row (the
- * two-kernel split + merge scheme).  Both compute the same exact merge. */
+/* How split rows are merged (the exact log-sum-exp merge of PersistentKV
+ * page, Methodology 1, "Sequence Splitting").  FUSED: inside the decode
+ * kernel, the last workgroup to finish a split (row, KV head) merges its
+ * partial states (one launch per step); a row of more than 32 ranges merges
+ * in two levels, each group of 32 consecutive ranges folded by its last
+ * workgroup and the group states by the row's last group.  SEPARATE: a
+ * second kernel merges every split row (the two-kernel split + merge
+ * scheme), in the same two levels.  Both give the same bits. */
 enum { PKV_MERGE_FUSED = 0, PKV_MERGE_SEPARATE = 1 };
 
 /* Device error words (pkv_runtime_info.error_code). */
