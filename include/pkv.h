@@ -89,7 +89,10 @@ enum { PKV_ORDER_CANONICAL = 0, PKV_ORDER_LPT = 1 };
 /* Item-to-workgroup assignment in one-shot launches.  ATOMIC (default): the
  * PersistentKV page's work queue -- workgroup g runs item g first, then claims
  * further items with an atomic counter as it finishes (no claims at all when
- * the queue has no more items than workgroups: the first round covers it).
+ * the queue has no more items than workgroups: the first round covers it;
+ * and a host-built queue of items of one length in whole rounds of the grid
+ * runs round-robin as under STATIC, since claims could not change how much
+ * each workgroup runs).
  * Consecutive launches of a handle use two such counters in turn, each
  * launch clearing the other's for the next.  STATIC: the WPK note's
  * compiled schedule -- workgroup g runs items g, g + grid, g + 2 grid, ...

@@ -138,6 +138,7 @@ struct pkv_handle {
     uint32_t* host_err_dev = nullptr;
     bool built = false;
     bool built_on_device = false;
+    bool queue_uniform = false;         // host-built queue whose items all have one length
     int batch = 0;
     pkv_queue_info qinfo{};
     hipEvent_t ev_before = nullptr;
@@ -534,6 +535,7 @@ PKV_API pkv_status pkv_build_queue(pkv_handle* h, const int32_t* ctx_lens_host, 
     h->staging_next = 1 - i;
     h->built = true;
     h->built_on_device = false;
+    h->queue_uniform = qh->uniform != 0;
     h->batch = batch;
     h->qinfo = qi;
     if (info) *info = qi;
@@ -587,7 +589,14 @@ PKV_API pkv_status pkv_decode(pkv_handle* h, const pkv_tensors* t, void* stream)
     // words and partial states are shared by every launch of the handle)
     if ((e = after_upload(h, st)) != hipSuccess || (e = after_readers(h, st)) != hipSuccess)
         return hip_fail(h, e, "stream wait");
-    const DecodeParams p = make_params(h, t);
+    DecodeParams p = make_params(h, t);
+    // A host-built queue of items of one length in whole rounds of the grid:
+    // claims could not change how much each workgroup runs and would only
+    // queue on the one pop counter as the rounds end, so the launch assigns
+    // round-robin (the static schedule: the same item computations, the same
+    // outputs).
+    if (!h->built_on_device && h->queue_uniform && h->qinfo.n_items > h->grid && h->qinfo.n_items % h->grid == 0)
+        p.static_sched = 1;
     if (h->ev_before && (e = hipEventRecord(h->ev_before, st)) != hipSuccess) return hip_fail(h, e, "event record");
     int rc = launch_decode(p, h->r.d, h->r.g, h->r.kv_dtype, h->grid, st);
     if (rc != 0) return hip_fail(h, (hipError_t)rc, "decode launch");

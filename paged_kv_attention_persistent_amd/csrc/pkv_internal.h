@@ -61,7 +61,8 @@ struct QHdr {
     int32_t split;
     int32_t chunk_tokens;
     int32_t batch;
-    int32_t pad[59];
+    int32_t uniform;        // 1: every item has the same number of tokens
+    int32_t pad[58];
 };
 static_assert(sizeof(QHdr) == 256, "queue header is 256 bytes");
 

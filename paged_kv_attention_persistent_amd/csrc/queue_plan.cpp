@@ -298,6 +298,9 @@ pkv_status plan_queue(const Resolved& r, const int32_t* ctx_lens, int32_t batch,
     qh->split = split ? 1 : 0;
     qh->chunk_tokens = chunk;
     qh->batch = batch;
+    qh->uniform = n_items > 0 ? 1 : 0;
+    for (int64_t i = 1; i < n_items && qh->uniform; ++i)
+        if (items[i].tok_end - items[i].tok_begin != items[0].tok_end - items[0].tok_begin) qh->uniform = 0;
     if (info) {
         memset(info, 0, sizeof(*info));
         info->n_items = (int32_t)n_items;

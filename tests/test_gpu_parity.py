@@ -195,15 +195,21 @@ def test_tiny_workload_and_repeat_calls():
     run.close()
 
 
-@pytest.mark.parametrize("rows,sched", [(40, "atomic"), (4, "atomic"), (40, "static")])
-def test_claim_counters_alternate_between_launches(rows, sched):
+@pytest.mark.parametrize("rows,sched,uniform", [(40, "atomic", False), (4, "atomic", False), (40, "static", False),
+                                               (64, "atomic", True), (40, "atomic", True)])
+def test_claim_counters_alternate_between_launches(rows, sched, uniform):
     """One-shot launches pop from two counters in turn, each launch zeroing
     the other for the next one.  Every item is followed by one claim when the
     queue has more items than workgroups (so a launch makes exactly n_items
     claims, the last grid of them empty), none when the static first round
-    covers the queue or under the static schedule; results are unchanged."""
-    lens = [int(x) for x in np.random.default_rng(rows).integers(1, 3000, size=rows)]
-    wl = workloads.custom(f"claims{rows}", lens, 32, 8, 128)
+    covers the queue, under the static schedule, or for items of one length
+    in whole rounds (64 rows x 8 KV heads = 512 items: round-robin); 40 equal
+    rows (320 items, not whole rounds) still claim.  Results are unchanged."""
+    if uniform:
+        lens = [2000] * rows
+    else:
+        lens = [int(x) for x in np.random.default_rng(rows).integers(1, 3000, size=rows)]
+    wl = workloads.custom(f"claims{rows}{'u' if uniform else ''}", lens, 32, 8, 128)
     run = Run(wl, schedule=pkv.PKV_SCHEDULE_STATIC if sched == "static" else pkv.PKV_SCHEDULE_ATOMIC)
     ro, rl = oracle_full(wl)
     lay = run.dec.layout
@@ -214,13 +220,16 @@ def test_claim_counters_alternate_between_launches(rows, sched):
         st = run.dec.query()
         n_items, grid = st["n_items"], st["grid"]
         heads = run.dec.workspace[lay.ctrl_off:lay.ctrl_off + 8].cpu().view(torch.int32).numpy()
-        claims = n_items if (sched == "atomic" and n_items > grid) else 0
+        whole_rounds = uniform and n_items % grid == 0
+        claims = n_items if (sched == "atomic" and n_items > grid and not whole_rounds) else 0
         used = call % 2                                  # launch k pops from counter k mod 2
         assert heads[used] == claims and heads[1 - used] == 0, (call, heads.tolist(), n_items, grid)
         assert st["queue_head"] == 0 and st["decode_calls"] == call + 1
         assert st["items_done"] == n_items * (call + 1)
     say(f"claims rows {rows} {sched}: items {n_items}, grid {grid}")
-    assert (n_items > grid) == (rows == 40), (n_items, grid)     # both regimes are covered
+    assert (n_items > grid) == (rows != 4), (n_items, grid)      # both regimes are covered
+    if uniform and rows == 64:
+        assert n_items % grid == 0, (n_items, grid)
     run.close()
 
 
