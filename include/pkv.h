@@ -79,7 +79,9 @@ enum {
  * the shortest ranges that still give at most one item per workgroup (the
  * longest row's page count if the rows alone exceed that bound), and never
  * shorter than 16 pages (64 pages for the resident loop, persistent = 1).
- * The default max_items is sized by that floor. */
+ * Such a queue holds at most max(Hkv * max_batch, num_cus) items, and the
+ * default max_items in this mode is max(Hkv * max_batch, num_cus, 1024), so
+ * that the layout is the same for every num_cus up to 1024. */
 enum { PKV_POLICY_AUTO = 0, PKV_POLICY_NO_SPLIT = 1, PKV_POLICY_SPLIT = 2 };
 
 /* Queue order: CANONICAL = (seq, kv_head, chunk) ascending; LPT = stable sort

@@ -15,11 +15,14 @@ constexpr int kThreads = 512;          // 8 waves of 64 lanes per workgroup
 constexpr int kWaves = kThreads / 64;
 // Chunk mode "fit": shortest range in pages.  One-shot launches take ranges
 // down to 16 pages (measured: the shortest ranges that still give one item
-// per workgroup are the fastest); the resident loop keeps 64, since the
-// workspace holds its partial states for every layer and sizes them by this
-// floor.
+// per workgroup are the fastest); the resident loop keeps 64 (measured: its
+// layers wait on each other's merges, and 32- or 48-page ranges stepped no
+// faster).
 constexpr int kFitMinPages = 16;
 constexpr int kFitMinPagesLoop = 64;
+// CUs that the default queue capacity of chunk mode "fit" covers on any
+// device (more when the config names more)
+constexpr int kFitCuSlots = 1024;
 constexpr int kCursorStride = 32;      // u32 words between page cursors (one 128-byte line each)
 constexpr int kSinkBytes = 4096;       // >= the largest tile (16 rows x 128 bf16, 8 rows x 128 fp32)
 

@@ -107,18 +107,23 @@ pkv_status resolve_config(const pkv_config* user_cfg, int device_cus, Resolved* 
     r->num_cus = cfg->num_cus > 0 ? cfg->num_cus : device_cus;
     if (r->num_cus <= 0) { *why = "num_cus unknown (set it in the config)"; return PKV_ERR_INVALID_ARG; }
     const int64_t max_tokens = (int64_t)r->max_pages_per_seq * kPageSize;
-    // ranges per row: ceil(max_tokens / C) for fixed chunks; for "fit" the
-    // range floor bounds it by ceil(max_pages_per_seq / floor), which, like
-    // the whole layout, does not depend on the CU count
     r->fit_min_pages = cfg->persistent ? kFitMinPagesLoop : kFitMinPages;
-    const int64_t max_chunks = r->chunk ? (max_tokens + r->chunk - 1) / r->chunk
-                                        : ((int64_t)r->max_pages_per_seq + r->fit_min_pages - 1) / r->fit_min_pages;
+    // Default capacity.  Fixed C-token chunks: Hkv * max_batch * ceil(max_tokens / C).
+    // Chunk mode "fit": a queue that does not split holds one item per
+    // (row, KV head); a split queue holds at most max(1, CUs / Hkv) ranges per
+    // KV head when some range length T reaches that budget (the floor only
+    // lengthens ranges), else one range per row.  Hence at most
+    // max(Hkv * max_batch, CUs) items, with the CU term taken as
+    // max(kFitCuSlots, CUs) so that the layout is the same on every device of
+    // up to kFitCuSlots CUs.
+    const int64_t max_chunks = r->chunk ? (max_tokens + r->chunk - 1) / r->chunk : 1;
     if (max_chunks > 65535) { *why = "more than 65535 ranges per row"; return PKV_ERR_CAPACITY; }
     if (cfg->max_items < 0) { *why = "max_items must be >= 0"; return PKV_ERR_INVALID_ARG; }
     if (cfg->max_items > 0) {
         r->max_items = cfg->max_items;
     } else {
-        const int64_t bound = (int64_t)r->hkv * r->max_batch * max_chunks;
+        int64_t bound = (int64_t)r->hkv * r->max_batch * max_chunks;
+        if (!r->chunk) bound = std::max<int64_t>(bound, std::max(kFitCuSlots, r->num_cus));
         if (bound > (int64_t)1 << 28) { *why = "derived max_items too large; set max_items"; return PKV_ERR_CAPACITY; }
         r->max_items = (int)bound;
     }

@@ -132,7 +132,7 @@ static int fuzz(unsigned seed, int trials) {
         c.policy = uni(0, 2);
         c.order = uni(0, 1);
         c.kv_chunk_tokens = pick({0, 0, 16, 512, 4096, 17});
-        c.num_cus = pick({8, 64, 256, 304});
+        c.num_cus = pick({8, 64, 256, 304, 2048});
         c.max_items = rng() % 3 ? 0 : uni(1, 4000);
         c.merge_mode = uni(0, 1);
         c.persistent = rng() % 4 == 0;
@@ -176,6 +176,7 @@ static int fuzz(unsigned seed, int trials) {
             }
         } else {
             CHECK(p.st == PKV_ERR_CAPACITY, "planner error %d", p.st);
+            CHECK(c.max_items > 0, "the default capacity refused a valid batch");
         }
         // out-of-range inputs are refused
         if (B > 0) {

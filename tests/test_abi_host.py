@@ -219,8 +219,41 @@ def test_layout_regions_are_ordered_and_aligned():
     offs = [lay.ctrl_off, lay.queue_off, lay.n_chunks_off, lay.part_off_off, lay.merge_rows_off,
             lay.items_off, lay.partial_o_off, lay.partial_lse_off, lay.arrive_off, lay.total_bytes]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
-    assert lay.max_items == 8 * (8192 // 16)      # one-shot ranges of at least 16 pages
+    assert lay.max_items == 1024                  # chunk mode "fit": max(Hkv * max_batch, 1024)
     assert lay.partial_lse_off - lay.partial_o_off >= lay.max_items * 4 * 128 * 4
+
+
+def test_default_capacity_in_fit_mode_holds_every_queue():
+    # a split queue in chunk mode "fit" holds at most max(1, CUs / Hkv) ranges
+    # per KV head, or one range per row when no range length reaches that, so
+    # max(Hkv * max_batch, CUs) items bound it whatever the rows' lengths
+    big = pkv.pkv_workspace_layout(pkv.make_config(32, 8, 128, 100000, 512, 8192, num_cus=256))
+    assert big.max_items == 8 * 512
+    assert pkv.pkv_workspace_layout(pkv.make_config(32, 8, 128, 100000, 1, 8192, num_cus=2048)).max_items == 2048
+    fixed = pkv.pkv_workspace_layout(pkv.make_config(32, 8, 128, 100000, 4, 8192, num_cus=256,
+                                                     kv_chunk_tokens=4096))
+    assert fixed.max_items == 8 * 4 * (8192 * 16 // 4096)
+    rng = np.random.default_rng(11)
+    for hkv in (1, 2, 8):
+        for cus in (8, 80, 256, 304, 1024, 2048):
+            for mb in (1, 3, 40, 300):
+                maxp = 40000
+                for policy in (pkv.PKV_POLICY_AUTO, pkv.PKV_POLICY_SPLIT):
+                    cfg = pkv.make_config(hkv * 4, hkv, 128, 1000, mb, maxp, num_cus=cus, policy=policy)
+                    cap = pkv.pkv_workspace_layout(cfg).max_items
+                    assert cap == max(hkv * mb, cus, 1024)
+                    batches = [[16 * maxp] * mb, [16 * maxp] + [1] * (mb - 1),
+                               rng.integers(0, 16 * maxp + 1, size=mb).tolist(),
+                               rng.integers(1, 200, size=mb).tolist()]
+                    most = 0
+                    for lens in batches:
+                        items = pkv.pkv_plan_queue(cfg, lens)[0]
+                        most = max(most, len(items))
+                        assert len(items) <= max(hkv * mb, hkv * max(1, cus // hkv))
+                    assert most <= cap
+    # the bound is reached: one long row, one KV head, 1024 CUs
+    cfg = pkv.make_config(4, 1, 128, 1000, 1, 32768, num_cus=1024)
+    assert len(pkv.pkv_plan_queue(cfg, [16 * 32768])[0]) == 1024 == pkv.pkv_workspace_layout(cfg).max_items
 
 
 def test_f32_stream_rounds_to_bf16_stream():
