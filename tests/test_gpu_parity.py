@@ -947,6 +947,37 @@ def test_million_token_context(kv):
         torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("kv", KVS)
+def test_queue_filling_the_default_capacity(kv):
+    """Chunk mode "fit" with 1024 CUs as the policy input (the device runs the
+    queue with its own workgroups, in claimed rounds): one KV head and a row
+    of 32,768 pages, the last one partial, give exactly 1024 ranges of 512
+    tokens, the default capacity max(Hkv * max_batch, CUs, 1024) filled to
+    its last item.  The row merges in two levels (32 groups of 32 ranges);
+    fused and separate merges, host- and device-built queues, every output
+    against the oracle."""
+    L = 32768 * 16 - 5
+    wl = workloads.custom("capacity_1024", [L], 4, 1, 128, kv_dtype=kv)
+    ro = rl = None
+    for merge in (pkv.PKV_MERGE_FUSED, pkv.PKV_MERGE_SEPARATE):
+        run = Run(wl, num_cus=1024, merge_mode=merge)
+        assert run.dec.layout.max_items == 1024
+        if ro is None:
+            ro, rl = oracle_unit(wl, workloads.bits_u16(run.q), 0, 0)
+        for device_queue in (False, True):
+            o, l = run.decode(device_queue=device_queue)
+            if not device_queue:
+                assert run.info.split and run.info.n_items == 1024 and run.info.chunk_tokens == 512
+            else:
+                hdr = run.queue_bytes()["hdr"]
+                assert list(hdr) == [1024, 1, 1, 512, 1], hdr
+            check(o, l, ro[None], rl[None], f"capacity {kv} merge {merge} device queue {device_queue}",
+                  lse_tol(wl))
+        run.close()
+        del run
+        torch.cuda.empty_cache()
+
+
 # ------------------------------------------------ seeded random sweep ----
 
 def _random_case(rng, i):
